@@ -1,0 +1,449 @@
+"""CPU oracle for the Mamba-2 SSD forward and the SSDi8 persistent-INT8 path.
+
+TEST INFRASTRUCTURE. Only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module. It shares no code with the HIP
+library and imports nothing from it.
+
+Sources (the pages are cited by title and section):
+  [SSDi8]  "SSDi8: Accurate and Efficient 8-bit Quantization for State Space
+           Duality" (paper notes page, ICLR 2026): "Overall framework" (the five
+           chunk modules, B/C quantized once along G, dAcs kept in floating
+           point), "Key design 1" (Eq. 4 and the reconstruction
+           State_INT32 = Q(X_scaled) x Q(B)), "Key design 2" (in-register
+           INT32->INT8 requantisation, per-(H,P) state scale, Eq. 6 shift update
+           with S = 2^7, B/C reuse by ChunkBMM/ChunkScan, CB's dequant folded
+           into the ChunkScan2 LUT), "Key design 3" (quantisation axes: G for
+           B/C, (H,P) for X_scaled and the state, never N), "Training
+           strategy" (static symmetric scales).
+  [SSM]    The selective state-space recurrence the SSD block computes,
+           h_t = exp(dt_t*A) h_{t-1} + dt_t x_t (x) B_t,  y_t = C_t . h_t + D x_t,
+           which the SSDi8 "Overall framework" splits into chunks L = c*l. The
+           pages never print it; it is the plain definition everything here
+           is checked against.
+
+Everything is float64 unless a step of the method fixes another precision.
+Readings where the pages are silent or garbled (each one is implemented the
+same way on the GPU side):
+  R1  scales are step sizes s = amax/q_max (so Key design 2's requant factor
+      s_x*s_b*q_max/s_s, with s_s the state *range*, equals s_X*s_B/s_S here);
+  R2  "Round" is round-half-away-from-zero, saturating to +-q_max;
+  R3  the Eq. 6 division by S = 2^7 is a rounding shift
+      sign(v)*((|v| + 2^6) >> 7);
+  R4  Q(Decay) = RHAZ(Decay * S) lies in [0, S] (128 needs a uint8);
+  R5  the in-chunk cumulative sum of dt*A is accumulated in float64 in
+      sequence order; dAcs is kept as float32, LUT_state is formed in float64
+      and rounded once to float32; Q(Decay) is decided in float64;
+  R6  the quantiser products are single float32 roundings (no fused
+      multiply-add): Q(v) = sat(RHAZ(fl32(fl32(v) * inv))),
+      Q(Xs) = sat(RHAZ(fl32(fl32(LUT32 * x) * inv_X))),
+      S8 = sat(RHAZ(fl32(fl32(S32) * M_req)));
+  R7  CB stays the exact int32 product of the reused Q(C), Q(B); ChunkScan2
+      multiplies it by s_C*s_B inside its LUT;
+  R8  head h uses group h // (H/G); the initial state is zero; a partial last
+      chunk is zero padded (dt = 0 steps leave the state unchanged);
+  R9  calibration: amax of |B|, |C| per g; of |LUT*x| per (h,p) with the
+      float64 LUT; of the float64 chunk states max(|S_k|, |H_k|) per (h,p)
+      over (b, k, n), over two calibration sequences.
+
+Where exactness is claimed, float64 matmuls are used on integer-valued
+operands whose partial sums stay below 2^53, so they are exact in any order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Plain definition: the recurrence, its quadratic dual and the chunked algebra
+# ---------------------------------------------------------------------------
+
+
+def head_group(H: int, G: int) -> np.ndarray:
+    """Group of each head: contiguous blocks of H/G heads (R8)."""
+    assert H % G == 0
+    return np.arange(H) // (H // G)
+
+
+def recurrence(x, dt, A, B, C, D, h0=None):
+    """[SSM] sequential recurrence in float64.
+
+    x [b,L,H,P], dt [b,L,H], A [H], B/C [b,L,G,N], D [H].
+    Returns (y [b,L,H,P], final state [b,H,P,N]).
+    """
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    D = np.asarray(D, np.float64)
+    b, L, H, P = x.shape
+    N = B.shape[-1]
+    g = head_group(H, B.shape[2])
+    h = np.zeros((b, H, P, N)) if h0 is None else np.array(h0, np.float64)
+    y = np.empty((b, L, H, P))
+    for t in range(L):
+        decay = np.exp(dt[:, t, :] * A[None, :])                     # [b,H]
+        u = dt[:, t, :, None] * x[:, t]                               # [b,H,P]
+        Bt = B[:, t][:, g]                                            # [b,H,N]
+        Ct = C[:, t][:, g]
+        h = decay[:, :, None, None] * h + u[:, :, :, None] * Bt[:, :, None, :]
+        y[:, t] = (h * Ct[:, :, None, :]).sum(-1) + D[None, :, None] * x[:, t]
+    return y, h
+
+
+def quadratic(x, dt, A, B, C, D):
+    """[SSM] dual ("attention") form, brute force for tiny L:
+
+    y_t = sum_{j<=t} (C_t . B_j) exp(sum_{u=j+1..t} dt_u A) dt_j x_j + D x_t,
+    with each segment sum formed directly (not as a difference of cumsums).
+    """
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    b, L, H, P = x.shape
+    g = head_group(H, B.shape[2])
+    idx = np.arange(L)
+    # inside[t, j, u] = 1 when j < u <= t
+    inside = ((idx[None, None, :] > idx[None, :, None])
+              & (idx[None, None, :] <= idx[:, None, None])).astype(np.float64)
+    causal = idx[None, :] <= idx[:, None]
+    y = np.empty((b, L, H, P))
+    for bi in range(b):
+        for hi in range(H):
+            dA = dt[bi, :, hi] * np.float64(A[hi])                      # [L]
+            seg = inside @ dA                                           # [t, j]
+            cb = C[bi, :, g[hi]] @ B[bi, :, g[hi]].T                    # [t, j]
+            M = np.where(causal, cb * np.exp(np.where(causal, seg, 0.0)), 0.0)
+            M = M * dt[bi, None, :, hi]
+            y[bi, :, hi] = M @ x[bi, :, hi] + np.float64(D[hi]) * x[bi, :, hi]
+    return y
+
+
+def _pad_chunks(arr, L_pad, axis=1):
+    L = arr.shape[axis]
+    if L == L_pad:
+        return arr
+    pad = [(0, 0)] * arr.ndim
+    pad[axis] = (0, L_pad - L)
+    return np.pad(arr, pad)
+
+
+def chunked(x, dt, A, B, C, D, chunk, h0=None):
+    """[SSM] + [SSDi8 "Overall framework"]: the chunked decomposition in float64.
+
+    Within chunk k with a_s = sum_{s'<=s} dt_s' A:
+      ChunkState   S_k   = sum_s dt_s exp(a_{l-1} - a_s) x_s (x) B_s
+      StatePassing H_k   = exp(a_{l-1}) H_{k-1} + S_k
+      ChunkBMM     CB[s,s'] = C_s . B_s'
+      ChunkScan1   Y_off = exp(a_s) C_s . H_{k-1}
+      ChunkScan2   Y_diag= sum_{s'<=s} CB[s,s'] exp(a_s - a_s') dt_s' x_s'
+    Returns (y, final state, chunk states S [b,c,H,P,N], passed states H [b,c,H,P,N]).
+    With ``with_y=False`` (see ``chunk_states``) the scan is skipped.
+    """
+    return _chunked(x, dt, A, B, C, D, chunk, h0, True)
+
+
+def chunk_states(x, dt, A, B, chunk, h0=None):
+    """Float64 chunk states S_k and passed states H_k only (no output)."""
+    _, hl, S, Hs = _chunked(x, dt, A, B, None, None, chunk, h0, False)
+    return hl, S, Hs
+
+
+def _chunked(x, dt, A, B, C, D, chunk, h0, with_y):
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    b, L, H, P = x.shape
+    N = B.shape[-1]
+    g = head_group(H, B.shape[2])
+    l = chunk
+    c = -(-L // l)
+    Lp = c * l
+    xp = _pad_chunks(x, Lp).reshape(b, c, l, H, P)
+    dtp = _pad_chunks(dt, Lp).reshape(b, c, l, H)
+    Bp = _pad_chunks(B, Lp).reshape(b, c, l, -1, N)
+    if with_y:
+        C = np.asarray(C, np.float64)
+        D = np.asarray(D, np.float64)
+        Cp = _pad_chunks(C, Lp).reshape(b, c, l, -1, N)
+        y = np.empty((b, c, l, H, P))
+    Hprev = np.zeros((b, H, P, N)) if h0 is None else np.array(h0, np.float64)
+    S_all = np.empty((b, c, H, P, N))
+    H_all = np.empty((b, c, H, P, N))
+    tri = np.tril(np.ones((l, l), dtype=bool))
+    for k in range(c):
+        a = np.cumsum(dtp[:, k] * A[None, None, :], axis=1).transpose(0, 2, 1)   # [b,H,l]
+        xs = xp[:, k].transpose(0, 2, 1, 3)                                       # [b,H,l,P]
+        dts = dtp[:, k].transpose(0, 2, 1)                                        # [b,H,l]
+        Bs = Bp[:, k][:, :, g].transpose(0, 2, 1, 3)                              # [b,H,l,N]
+        lut = dts * np.exp(a[:, :, -1:] - a)                                      # [b,H,l]
+        S = np.matmul((lut[..., None] * xs).transpose(0, 1, 3, 2), Bs)            # [b,H,P,N]
+        Hk = np.exp(a[:, :, -1])[:, :, None, None] * Hprev + S
+        if with_y:
+            Cs = Cp[:, k][:, :, g].transpose(0, 2, 1, 3)                          # [b,H,l,N]
+            y_off = np.exp(a)[..., None] * np.matmul(Cs, Hprev.transpose(0, 1, 3, 2))
+            cb = np.matmul(Cs, Bs.transpose(0, 1, 3, 2))                          # [b,H,s,s']
+            seg = a[:, :, :, None] - a[:, :, None, :]
+            Lmat = np.where(tri, np.exp(np.where(tri, seg, 0.0)), 0.0)
+            y_diag = np.matmul(cb * Lmat * dts[:, :, None, :], xs)
+            yk = y_off + y_diag + D[None, :, None, None] * xs                     # [b,H,l,P]
+            y[:, k] = yk.transpose(0, 2, 1, 3)
+        S_all[:, k], H_all[:, k] = S, Hk
+        Hprev = Hk
+    if not with_y:
+        return None, Hprev, S_all, H_all
+    return y.reshape(b, Lp, H, P)[:, :L], Hprev, S_all, H_all
+
+
+# ---------------------------------------------------------------------------
+# The SSDi8 integer method
+# ---------------------------------------------------------------------------
+
+
+def qmax_of(bits: int) -> int:
+    """q_max = 2^(b-1) - 1 ([SSDi8] Key design 2)."""
+    return (1 << (bits - 1)) - 1
+
+
+def fl32(v):
+    """Round float64 values to the nearest float32 (ties to even), back in float64."""
+    return np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+
+
+def rhaz(v):
+    """Round half away from zero (R2), in float64: sign(v) * floor(|v| + 1/2)."""
+    v = np.asarray(v, np.float64)
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+def saturate(q, qmax: int):
+    return np.clip(q, -qmax, qmax)
+
+
+def quantize(v, inv, bits: int = 8):
+    """Q(v) = sat(RHAZ(fl32(fl32(v) * inv))) as int64 (R2, R6)."""
+    return saturate(rhaz(fl32(fl32(v) * np.asarray(inv, np.float64))), qmax_of(bits)).astype(np.int64)
+
+
+def rounding_shift(v, shift: int):
+    """Division by 2^shift rounded half away from zero, integers only (R3)."""
+    v = np.asarray(v, np.int64)
+    half = np.int64(1) << np.int64(shift - 1)
+    return np.sign(v) * ((np.abs(v) + half) >> np.int64(shift))
+
+
+def scale_pack(amax_B, amax_C, amax_Xs, amax_S, nheads: int, bits: int = 8) -> dict:
+    """Static scale pack from calibration maxima (R1).
+
+    s = fp32(amax / q_max) (s = 1 when amax is 0); inv = fp32(1 / s);
+    M_req[h,p] = fp32(s_X[h,p] * s_B[g(h)] / s_S[h,p]). Returns float32 arrays.
+    """
+    qm = float(qmax_of(bits))
+
+    def step(a):
+        a = np.asarray(a, np.float64)
+        return np.where(a > 0, a / qm, 1.0).astype(np.float32)
+
+    s_B, s_C, s_X, s_S = step(amax_B), step(amax_C), step(amax_Xs), step(amax_S)
+    G = s_B.shape[0]
+    H = nheads
+    g = head_group(H, G)
+    sB_h = s_B.astype(np.float64)[g][:, None]
+    M_req = (s_X.astype(np.float64) * sB_h / s_S.astype(np.float64)).astype(np.float32)
+    inv = lambda s: (1.0 / s.astype(np.float64)).astype(np.float32)  # noqa: E731
+    return {
+        "s_B": s_B, "s_C": s_C, "inv_B": inv(s_B), "inv_C": inv(s_C),
+        "s_X": s_X, "inv_X": inv(s_X), "s_S": s_S, "M_req": M_req, "bits": bits,
+    }
+
+
+def calibrate(seqs, A, ngroups: int, chunk: int) -> dict:
+    """Calibration maxima over sequences (R9). Each seq: float64 x, dt, B, C."""
+    amax_B = np.zeros(ngroups)
+    amax_C = np.zeros(ngroups)
+    amax_X = None
+    amax_S = None
+    A = np.asarray(A, np.float64)
+    for sq in seqs:
+        x, dt, B, C = (np.asarray(sq[k], np.float64) for k in ("x", "dt", "B", "C"))
+        b, L, H, P = x.shape
+        amax_B = np.maximum(amax_B, np.abs(B).max(axis=(0, 1, 3)))
+        amax_C = np.maximum(amax_C, np.abs(C).max(axis=(0, 1, 3)))
+        l = chunk
+        c = -(-L // l)
+        dtp = _pad_chunks(dt, c * l).reshape(b, c, l, H)
+        xp = _pad_chunks(x, c * l).reshape(b, c, l, H, P)
+        a = np.cumsum(dtp * A, axis=2)
+        lut = dtp * np.exp(a[:, :, -1:, :] - a)                        # [b,c,l,H]
+        ax = np.abs(lut[..., None] * xp).max(axis=(0, 1, 2))            # [H,P]
+        amax_X = ax if amax_X is None else np.maximum(amax_X, ax)
+        _, S, Hs = chunk_states(x, dt, A, B, chunk)
+        sm = np.maximum(np.abs(S), np.abs(Hs)).max(axis=(0, 1, 4))      # [H,P]
+        amax_S = sm if amax_S is None else np.maximum(amax_S, sm)
+    return {"B": amax_B, "C": amax_C, "Xs": amax_X, "S": amax_S}
+
+
+def chunk_cumsum(dt, A, chunk: int, bits: int = 8) -> dict:
+    """ChunkCumsum ([SSDi8] "Overall framework"; R4, R5).
+
+    dt [b,L,H] float64 (exact widening of the stored values), A [H] float32.
+    Returns per (b, h, k, s), zero padded past L:
+      a      float64 in-chunk cumulative sum of dt*A, in sequence order
+      dAcs   float32 rounding of a
+      lut    float32 rounding of dt_s * exp(a_{l-1} - a_s) (LUT_state of Eq. 4)
+      decay  float64 exp(a_{l-1}) per (b, h, k)
+      qdecay int64   RHAZ(decay * 2^(bits-1)) in [0, 2^(bits-1)]
+    """
+    dt = np.asarray(dt, np.float64)
+    b, L, H = dt.shape
+    l = chunk
+    c = -(-L // l)
+    dtp = _pad_chunks(dt, c * l).reshape(b, c, l, H).transpose(0, 3, 1, 2)   # [b,H,c,l]
+    prod = dtp * np.asarray(A, np.float64)[None, :, None, None]            # exact
+    a = np.cumsum(prod, axis=3)               # sequential accumulation (R5)
+    lut64 = dtp * np.exp(a[..., -1:] - a)
+    decay = np.exp(a[..., -1])
+    S = float(1 << (bits - 1))
+    qdecay = np.minimum(rhaz(decay * S), S).astype(np.int64)
+    return {"a": a, "dAcs": fl32(a), "lut": fl32(lut64), "decay": decay, "qdecay": qdecay}
+
+
+def quantize_xs(x, lut32, inv_X, chunk: int, bits: int = 8):
+    """Q(X_scaled) with X_scaled = LUT_state (.) X ([SSDi8] Key design 1, R6).
+
+    x [b,L,H,P] float64, lut32 [b,H,c,l] float32 values, inv_X [H,P].
+    Returns int64 [b,L,H,P].
+    """
+    b, L, H, P = x.shape
+    lut_t = lut32.transpose(0, 2, 3, 1).reshape(b, -1, H)[:, :L]            # [b,L,H]
+    xs = fl32(lut_t[..., None] * x)
+    return saturate(rhaz(fl32(xs * np.asarray(inv_X, np.float64)[None, None])),
+                    qmax_of(bits)).astype(np.int64)
+
+
+def chunk_state_int(qxs, qB, chunk: int):
+    """State_INT32 = Q(X_scaled)^T x Q(B) per chunk ([SSDi8] Key design 1).
+
+    qxs [b,L,H,P], qB [b,L,G,N] integers. Returns int64 [b,c,H,P,N].
+    """
+    b, L, H, P = qxs.shape
+    G, N = qB.shape[2], qB.shape[3]
+    g = head_group(H, G)
+    l = chunk
+    c = -(-L // l)
+    qx = _pad_chunks(qxs.astype(np.float64), c * l).reshape(b, c, l, H, P)
+    qb = _pad_chunks(qB.astype(np.float64), c * l).reshape(b, c, l, G, N)[:, :, :, g]   # [b,c,l,H,N]
+    # integer-valued float64 matmul, exact (|sum| <= l * q_max^2 < 2^53)
+    s32 = np.matmul(qx.transpose(0, 1, 3, 4, 2), qb.transpose(0, 1, 3, 2, 4))  # [b,c,H,P,N]
+    return s32.astype(np.int64)
+
+
+def requantize_state(s32, M_req, bits: int = 8):
+    """State_INT8 = sat(RHAZ(fl32(fl32(S32) * M_req[h,p]))) ([SSDi8] Key design 2, R1, R6)."""
+    m = np.asarray(M_req, np.float64)[None, None, :, :, None]
+    return saturate(rhaz(fl32(fl32(s32.astype(np.float64)) * m)), qmax_of(bits)).astype(np.int64)
+
+
+def state_passing_int(s8, qdecay, bits: int = 8):
+    """Eq. 6 of [SSDi8] Key design 2 with S = 2^(bits-1) (R3):
+
+    H_0 = S8_0;  H_k = sat(S8_k + RSH(Q(Decay_k) * H_{k-1})).
+    s8 [b,c,H,P,N], qdecay [b,H,c]. Returns passed states [b,c,H,P,N].
+    """
+    qm = qmax_of(bits)
+    out = np.empty_like(s8)
+    c = s8.shape[1]
+    hk = s8[:, 0].astype(np.int64)
+    out[:, 0] = hk
+    for k in range(1, c):
+        qd = qdecay[:, :, k].astype(np.int64)[:, :, None, None]
+        hk = saturate(s8[:, k] + rounding_shift(qd * hk, bits - 1), qm)
+        out[:, k] = hk
+    return out
+
+
+def chunk_bmm_int(qC, qB, chunk: int):
+    """CB_k = Q(C) Q(B)^T per chunk and group ([SSDi8] Key design 2: reuse, R7).
+
+    Returns int64 [b,c,G,l,l] (full square; the scan reads its lower triangle).
+    """
+    b, L, G, N = qC.shape
+    l = chunk
+    c = -(-L // l)
+    qc = _pad_chunks(qC.astype(np.float64), c * l).reshape(b, c, l, G, N).transpose(0, 1, 3, 2, 4)
+    qb = _pad_chunks(qB.astype(np.float64), c * l).reshape(b, c, l, G, N).transpose(0, 1, 3, 4, 2)
+    return np.matmul(qc, qb).astype(np.int64)
+
+
+def chunk_scan_int8(x, dt, a, qC, cb, passed, D, scales: dict, chunk: int):
+    """ChunkScan1 + ChunkScan2 + D skip of the INT8 path ([SSDi8] Key design 2).
+
+    Scan1: Y_off[s,p] = exp(a_s) s_C s_S[h,p] sum_n Q(C)[s,n] H_{k-1}[p,n] (k >= 1).
+    Scan2: Y_diag[s,p] = sum_{s'<=s} CB[s,s'] s_C s_B exp(a_s - a_s') dt_s' x[s',p].
+    Evaluated in float64. a [b,H,c,l] float64. Returns y [b,L,H,P].
+    """
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    b, L, H, P = x.shape
+    G = qC.shape[2]
+    g = head_group(H, G)
+    l = chunk
+    c = -(-L // l)
+    xp = _pad_chunks(x, c * l).reshape(b, c, l, H, P)
+    dtp = _pad_chunks(dt, c * l).reshape(b, c, l, H)
+    qc = _pad_chunks(qC.astype(np.float64), c * l).reshape(b, c, l, G, -1)
+    s_C = np.asarray(scales["s_C"], np.float64)[g]                       # [H]
+    s_B = np.asarray(scales["s_B"], np.float64)[g]
+    s_S = np.asarray(scales["s_S"], np.float64)                          # [H,P]
+    D = np.asarray(D, np.float64)
+    tri = np.tril(np.ones((l, l), dtype=bool))
+    y = np.empty((b, c, l, H, P))
+    for k in range(c):
+        ak = a[:, :, k, :]                                                # [b,H,l]
+        xs = xp[:, k].transpose(0, 2, 1, 3)                               # [b,H,l,P]
+        if k > 0:
+            prev = passed[:, k - 1].astype(np.float64)                    # [b,H,P,N]
+            qcs = qc[:, k][:, :, g].transpose(0, 2, 1, 3)                 # [b,H,l,N]
+            acc1 = np.matmul(qcs, prev.transpose(0, 1, 3, 2))             # [b,H,l,P] exact
+            y_off = acc1 * (np.exp(ak)[..., None] * (s_C[:, None] * s_S)[None, :, None, :])
+        else:
+            y_off = 0.0
+        cbk = cb[:, k][:, g].astype(np.float64)                          # [b,H,l,l]
+        seg = ak[:, :, :, None] - ak[:, :, None, :]
+        Lmat = np.where(tri, np.exp(np.where(tri, seg, 0.0)), 0.0)
+        M = cbk * (s_C * s_B)[None, :, None, None] * Lmat * dtp[:, k].transpose(0, 2, 1)[:, :, None, :]
+        yk = y_off + np.matmul(M, xs) + D[None, :, None, None] * xs
+        y[:, k] = yk.transpose(0, 2, 1, 3)
+    return y.reshape(b, c * l, H, P)[:, :L]
+
+
+def forward_int8(x, dt, A, B, C, D, scales: dict, chunk: int) -> dict:
+    """The whole persistent-INT8 SSD forward, step by step ([SSDi8] Overall framework).
+
+    Inputs are float64 widenings of the stored tensors; A, D float32 values.
+    Returns every intermediate: qB, qC, cumsum dict, qxs, s32, s8 (local chunk
+    states), passed (states after StatePassing), cb, y.
+    """
+    bits = int(scales.get("bits", 8))
+    H = x.shape[2]
+    G = B.shape[2]
+    qB = quantize(B, np.asarray(scales["inv_B"], np.float64)[None, None, :, None], bits)
+    qC = quantize(C, np.asarray(scales["inv_C"], np.float64)[None, None, :, None], bits)
+    cs = chunk_cumsum(dt, A, chunk, bits)
+    qxs = quantize_xs(x, cs["lut"], scales["inv_X"], chunk, bits)
+    s32 = chunk_state_int(qxs, qB, chunk)
+    s8 = requantize_state(s32, scales["M_req"], bits)
+    passed = state_passing_int(s8, cs["qdecay"], bits)
+    cb = chunk_bmm_int(qC, qB, chunk)
+    y = chunk_scan_int8(x, dt, cs["a"], qC, cb, passed, D, scales, chunk)
+    assert H % G == 0
+    return {"qB": qB, "qC": qC, "cumsum": cs, "qxs": qxs, "s32": s32, "s8": s8,
+            "passed": passed, "cb": cb, "y": y}
+
+
+def rel_max_err(y, ref) -> float:
+    """max |y - ref| / RMS(ref): the accuracy metric for the floating outputs."""
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(np.asarray(y, np.float64) - ref)) / rms)
