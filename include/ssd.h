@@ -1,0 +1,210 @@
+/*
+ * ssd.h - C ABI of the MI355X (gfx950) Mamba-2 SSD chunked forward.
+ *
+ * Two paths compute the SSD block's forward pass as a chunked selective scan:
+ *   SSD_PATH_FLOAT  floating-point chunk algebra (fp16/bf16 MFMA, fp32 accumulate)
+ *   SSD_PATH_INT8   the persistent-INT8 path of "SSDi8: Accurate and Efficient
+ *                   8-bit Quantization for State Space Duality" (paper notes page,
+ *                   ICLR 2026), sections "Overall framework" and "Key designs 1-3".
+ *
+ * The operation (the selective state-space recurrence the SSDi8 "Overall
+ * framework" splits into chunks L = c*l; zero initial state):
+ *   h_t[h,p,n] = exp(dt_t[h] A[h]) h_{t-1}[h,p,n] + dt_t[h] x_t[h,p] B_t[g(h),n]
+ *   y_t[h,p]   = sum_n C_t[g(h),n] h_t[h,p,n] + D[h] x_t[h,p]
+ * with head h in group g(h) = h / (H/G).
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *   X, Y   [B, L, H, P]     dt [B, L, H]     B, C [B, L, G, N]     A, D [H] fp32
+ *   qB, qC [B, L, G, N] int8
+ *   dAcs, lut [B, H, c, l] fp32            qdecay [B, H, c] uint8
+ *   states [B, c, H, P, N]  int8 (INT8 path) or fp32 (float path)
+ *   CB     [B, c, G, l, l]  int32 (INT8 path) or fp32 (float path)
+ *   final_state [B, H, P, N] int8 or fp32
+ * where c = ceil(L / l). A partial last chunk behaves as if zero padded
+ * (dt = 0 steps leave the state unchanged); padded positions of dAcs hold the
+ * last valid cumulative value and of lut hold 0.
+ *
+ * Ownership: every buffer is allocated by the caller in device memory (except
+ * the shape, scale and tap descriptors, which are host structs holding device
+ * pointers) and must be 16-byte aligned. The library never allocates, frees or
+ * keeps a pointer after a call returns; it holds no mutable global state and
+ * may be called from several threads on different streams.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the null stream). Calls only
+ * enqueue work; results are valid once the stream has been synchronised.
+ *
+ * Errors: every call validates all arguments before enqueueing anything; a
+ * call that returns an error has written nothing. No C++ exception crosses
+ * this interface. Preconditions that are NOT checked: finite inputs, dt > 0,
+ * A < 0 (so every decay is <= 1), finite positive scales, and that output
+ * buffers do not overlap inputs (except where a call says "in place").
+ */
+#ifndef MAMBA_SSD_CHUNKED_AMD_SSD_H
+#define MAMBA_SSD_CHUNKED_AMD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-valued call. */
+enum {
+  SSD_OK = 0,
+  SSD_E_NULL = 1,        /* a required pointer is NULL */
+  SSD_E_SHAPE = 2,       /* negative or zero sizes, H % G != 0, size overflow */
+  SSD_E_UNSUPPORTED = 3, /* chunk not in {64,128,256}, P not in {16,32,64},
+                            N not in {16,32,64,128}, unknown dtype or path */
+  SSD_E_ALIGN = 4,       /* a buffer is not 16-byte aligned */
+  SSD_E_WORKSPACE = 5,   /* workspace smaller than ssd_workspace_bytes() */
+  SSD_E_HIP = 6,         /* the HIP runtime reported a launch error */
+  SSD_E_INTERNAL = 7
+};
+
+/* Element type of X, dt, B, C and Y. */
+enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_F16 = 1, SSD_DTYPE_BF16 = 2 };
+
+/* Which path a call computes. */
+enum { SSD_PATH_FLOAT = 0, SSD_PATH_INT8 = 1 };
+
+/* Problem shape. batch == 0 or seqlen == 0 is a valid empty problem (calls
+ * return SSD_OK and enqueue nothing); every other size must be > 0. */
+typedef struct ssd_shape {
+  int64_t batch;    /* B */
+  int64_t seqlen;   /* L */
+  int64_t nheads;   /* H */
+  int64_t headdim;  /* P */
+  int64_t dstate;   /* N */
+  int64_t ngroups;  /* G, divides H */
+  int64_t chunk;    /* l */
+  int32_t dtype;    /* SSD_DTYPE_* */
+  int32_t reserved; /* must be 0 */
+} ssd_shape;
+
+/* Static scale pack of the INT8 path (device fp32 arrays). Step sizes
+ * s = amax / 127 ("Key design 2" and "Training strategy": static symmetric
+ * scales; B/C per group G, X_scaled and the state per (H,P)).
+ *   s_B, s_C, inv_B, inv_C   [G]       inv = fp32(1 / s)
+ *   inv_X, s_S, M_req        [H * P]   M_req = fp32(s_X * s_B[g(h)] / s_S)
+ */
+typedef struct ssd_scales {
+  const float* s_B;
+  const float* s_C;
+  const float* inv_B;
+  const float* inv_C;
+  const float* inv_X;
+  const float* s_S;
+  const float* M_req;
+} ssd_scales;
+
+/* Optional debug outputs of the INT8 path (any member may be NULL). */
+typedef struct ssd_taps {
+  int8_t* q_xs;      /* Q(X_scaled)            [B, L, H, P] */
+  int32_t* s32;      /* State_INT32 per chunk  [B, c, H, P, N] */
+  int8_t* s8_local;  /* State_INT8 per chunk before StatePassing [B, c, H, P, N] */
+  int8_t* passed;    /* states after StatePassing [B, c, H, P, N] (ssd_forward only) */
+} ssd_taps;
+
+/* ChunkBMM/ChunkScan B/C input quantisation, once per group ("Overall
+ * framework": B and C are quantised along G once at SSD entry and reused;
+ * "Key design 3").  qB = sat127(RHAZ(fl32(fl32(B) * inv_B[g]))), same for C,
+ * with round-half-away-from-zero and single float32 roundings.
+ * B, C: [B,L,G,N] in shape->dtype. scales: inv_B, inv_C used. */
+int ssd_quantize_bc(const ssd_shape* shape, const void* B, const void* C,
+                    const ssd_scales* scales, int8_t* qB, int8_t* qC, void* stream);
+
+/* ChunkCumsum ("Overall framework": kept in floating point).
+ * Per (b, h, chunk k): a_s = sum_{s'<=s} dt_s' * A[h], accumulated in float64
+ * in sequence order. Writes dAcs = fp32(a_s); lut = fp32(dt_s * exp(a_{l-1} - a_s))
+ * evaluated in float64 (LUT_state of "Key design 1", Eq. 4); and, if qdecay is
+ * not NULL, qdecay = min(128, RHAZ(128 * exp(a_{l-1}))) decided in float64
+ * (the fixed-point Decay of "Key design 2", Eq. 6, S = 2^7).
+ * lut and qdecay may be NULL. */
+int ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* dAcs,
+                     float* lut, uint8_t* qdecay, void* stream);
+
+/* ChunkState ("Key design 1": State = X x (B . LUT_state), Eq. 4, computed as
+ * the reconstruction Q(X_scaled) x Q(B)).
+ * INT8: Q(Xs)[t,h,p] = sat127(RHAZ(fl32(fl32(lut * x) * inv_X[h,p]))),
+ *       S32 = sum_s Q(Xs)[s,h,p] Q(B)[s,g,n] (int8 MFMA, int32 accumulate),
+ *       states = sat127(RHAZ(fl32(fl32(S32) * M_req[h,p]))) (requantised in
+ *       registers, "Key design 2"). Bq = qB (int8); states int8; taps optional.
+ * FLOAT: states[k,h,p,n] = sum_s lut_s x[s,h,p] B[s,g,n] in fp32 (MFMA on
+ *       operands in the input dtype); Bq = B in shape->dtype; states fp32;
+ *       scales and taps are ignored and may be NULL. */
+int ssd_chunk_state(const ssd_shape* shape, int path, const void* X, const float* lut,
+                    const void* Bq, const ssd_scales* scales, void* states,
+                    const ssd_taps* taps, void* stream);
+
+/* StatePassing (Eq. 6 of "Key design 2"), in place over `states`, sequential
+ * over chunks. INT8: H_0 = S_0, H_k = sat127(S_k + RSH7(qdecay_k * H_{k-1}))
+ * with RSH7(v) = sign(v) * ((|v| + 64) >> 7); qdecay required, dAcs unused.
+ * FLOAT: H_k = exp(dAcs[k, l-1]) * H_{k-1} + S_k in fp32; qdecay unused.
+ * On return slot k holds H_k (the state after chunk k). final_state (may be
+ * NULL) receives H_{c-1}. */
+int ssd_state_passing(const ssd_shape* shape, int path, void* states, const float* dAcs,
+                      const uint8_t* qdecay, void* final_state, void* stream);
+
+/* ChunkBMM ("Key design 2": reuses the INT8 B and C):
+ * CB[b,k,g,i,j] = sum_n Cq[k*l+i, g, n] * Bq[k*l+j, g, n] for j <= i, 0 above
+ * the diagonal. INT8: Cq, Bq int8, CB int32 (exact). FLOAT: input dtype,
+ * CB fp32. Positions past L contribute 0. */
+int ssd_chunk_bmm(const ssd_shape* shape, int path, const void* Cq, const void* Bq,
+                  void* CB, void* stream);
+
+/* ChunkScan1 + ChunkScan2 + the D skip ("Key design 2").
+ *   Scan1 (k >= 1): Y_off[s,p] = exp(dAcs_s) * sum_n C[s,n] H_{k-1}[p,n]; on the
+ *     INT8 path C = Q(C), H = int8 states and the sum is dequantised with
+ *     s_C[g] * s_S[h,p].
+ *   Scan2: Y_diag[s,p] = sum_{s'<=s} CB[s,s'] exp(dAcs_s - dAcs_s') dt_s' x[s',p]
+ *     (INT8: CB int32 with its dequant s_C * s_B folded into the LUT).
+ *   Y = Y_off + Y_diag + D[h] x, stored in shape->dtype.
+ * states are the passed states (slot k-1 feeds chunk k). */
+int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* dt,
+                   const float* dAcs, const void* Cq, const void* CB, const void* states,
+                   const float* D, const ssd_scales* scales, void* Y, void* stream);
+
+/* The whole SSD forward in one call ("Overall framework": all modules).
+ * B, C, X, dt in shape->dtype; Y in shape->dtype. INT8 needs scales.
+ * final_state (may be NULL): int8 (INT8) or fp32 (FLOAT) [B,H,P,N].
+ * workspace: device memory of at least ssd_workspace_bytes(shape, path) bytes
+ * (may be NULL when that is 0). taps: INT8 only, may be NULL. The integer
+ * intermediates are bit-identical to those of the module calls above. */
+int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
+                const float* A, const void* B, const void* C, const float* D,
+                const ssd_scales* scales, void* Y, void* final_state, void* workspace,
+                size_t workspace_bytes, const ssd_taps* taps, void* stream);
+
+/* Workspace bytes ssd_forward needs (0 for an invalid shape). Host only. */
+size_t ssd_workspace_bytes(const ssd_shape* shape, int path);
+
+/* Calibration maxima for the static scales ("Training strategy": static
+ * scales from calibration data). Over one sequence batch, raises (running
+ * max) amax = [amax_B[G], amax_C[G], amax_Xs[H*P], amax_S[H*P]] (device fp32,
+ * caller zero-fills before the first call) with |B|, |C| per group, |LUT * x|
+ * per (h,p) and the float chunk states max(|S_k|, |H_k|) per (h,p) over
+ * (b, k, n), computed on the float path in fp32. workspace: at least
+ * ssd_calibrate_workspace_bytes(shape) bytes. */
+int ssd_calibrate_amax(const ssd_shape* shape, const void* X, const void* dt,
+                       const float* A, const void* B, const void* C, float* amax,
+                       void* workspace, size_t workspace_bytes, void* stream);
+size_t ssd_calibrate_workspace_bytes(const ssd_shape* shape);
+
+/* Host-only: static scale pack from calibration maxima (host arrays).
+ * amax = [amax_B[G], amax_C[G], amax_Xs[H*P], amax_S[H*P]];
+ * pack (host, 4*G + 4*H*P floats) = [s_B, s_C, inv_B, inv_C (G each),
+ * s_X, inv_X, s_S, M_req (H*P each)], with s = fp32(amax / 127) (1 when
+ * amax is 0 or not finite), inv = fp32(1 / s), M_req = fp32(s_X s_B / s_S)
+ * evaluated in float64. */
+int ssd_scales_from_amax(int64_t ngroups, int64_t nheads, int64_t headdim,
+                         const float* amax, float* pack);
+
+/* Static string for a status code. */
+const char* ssd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSD_CHUNKED_AMD_SSD_H */

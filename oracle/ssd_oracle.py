@@ -212,9 +212,15 @@ def fl32(v):
 
 
 def rhaz(v):
-    """Round half away from zero (R2), in float64: sign(v) * floor(|v| + 1/2)."""
+    """Round half away from zero (R2), exact for every float64 value.
+
+    The fraction |v| - floor(|v|) is exact, so comparing it with 1/2 decides
+    the tie rule without the rounding that |v| + 1/2 could introduce.
+    """
     v = np.asarray(v, np.float64)
-    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+    m = np.abs(v)
+    f = np.floor(m)
+    return np.sign(v) * (f + (m - f >= 0.5))
 
 
 def saturate(q, qmax: int):

@@ -146,6 +146,9 @@ def test_rhaz_ties_and_saturation():
     below = np.nextafter(np.float32(0.5), np.float32(0)).astype(np.float64)
     assert O.rhaz(below) == 0.0
     assert O.rhaz(-below) == 0.0
+    # and the float64 neighbour of 0.5 from below (the Q(Decay) decision is in float64)
+    below64 = np.nextafter(0.5, 0.0)
+    assert O.rhaz(below64) == 0.0 and O.rhaz(np.nextafter(2.5, 0.0)) == 2.0 and O.rhaz(-2.5) == -3.0
 
 
 def test_quantize_is_single_float32_rounding():
