@@ -26,7 +26,7 @@
  *
  * Ownership: every buffer is allocated by the caller in device memory (except
  * the shape, scale and tap descriptors, which are host structs holding device
- * pointers) and must be 16-byte aligned. The library never allocates, frees or
+ * pointers) and must be 16-byte aligned (the scale arrays: 4-byte aligned). The library never allocates, frees or
  * keeps a pointer after a call returns; it holds no mutable global state and
  * may be called from several threads on different streams.
  *

@@ -1,0 +1,418 @@
+// C ABI of the SSD chunked forward: argument validation (host only, before
+// any launch), workspace carving and dispatch to the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.hpp"
+
+using ssd::Dims;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Validates the shape; fills d. *empty is set for batch == 0 or seqlen == 0.
+int check_shape(const ssd_shape* s, Dims* d, bool* empty) {
+  if (!s) return SSD_E_NULL;
+  if (s->reserved != 0) return SSD_E_SHAPE;
+  if (s->batch < 0 || s->seqlen < 0) return SSD_E_SHAPE;
+  if (s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 || s->ngroups <= 0 || s->chunk <= 0)
+    return SSD_E_SHAPE;
+  if (s->nheads % s->ngroups != 0) return SSD_E_SHAPE;
+  if (s->dtype < SSD_DTYPE_F32 || s->dtype > SSD_DTYPE_BF16) return SSD_E_UNSUPPORTED;
+  if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return SSD_E_UNSUPPORTED;
+  if (s->headdim != 16 && s->headdim != 32 && s->headdim != 64) return SSD_E_UNSUPPORTED;
+  if (s->dstate != 16 && s->dstate != 32 && s->dstate != 64 && s->dstate != 128)
+    return SSD_E_UNSUPPORTED;
+  // grid limits: H in x, chunks in y, batch in z
+  const int64_t c = (s->seqlen + s->chunk - 1) / s->chunk;
+  if (s->nheads > 65535 || s->batch > 65535 || c > 65535) return SSD_E_SHAPE;
+  // every element count must fit an int64 byte offset
+  int64_t t;
+  if (!mul_ok(s->batch, s->seqlen, &t) || !mul_ok(t, s->nheads, &t) ||
+      !mul_ok(t, s->headdim, &t) || !mul_ok(t, 16, &t))
+    return SSD_E_SHAPE;
+  int64_t u;
+  if (!mul_ok(s->batch, c, &u) || !mul_ok(u, s->nheads, &u) || !mul_ok(u, s->headdim, &u) ||
+      !mul_ok(u, s->dstate, &u) || !mul_ok(u, 16, &u))
+    return SSD_E_SHAPE;
+  int64_t v;
+  if (!mul_ok(s->batch, c, &v) || !mul_ok(v, s->ngroups, &v) || !mul_ok(v, s->chunk, &v) ||
+      !mul_ok(v, s->chunk, &v) || !mul_ok(v, 16, &v))
+    return SSD_E_SHAPE;
+  d->B = s->batch;
+  d->L = s->seqlen;
+  d->H = (int)s->nheads;
+  d->P = (int)s->headdim;
+  d->N = (int)s->dstate;
+  d->G = (int)s->ngroups;
+  d->l = (int)s->chunk;
+  d->c = (int)c;
+  d->hpg = d->H / d->G;
+  *empty = (s->batch == 0 || s->seqlen == 0);
+  return SSD_OK;
+}
+
+int check_path(int path) {
+  return (path == SSD_PATH_FLOAT || path == SSD_PATH_INT8) ? SSD_OK : SSD_E_UNSUPPORTED;
+}
+
+// Each required pointer must be non-NULL and 16-byte aligned.
+int check_ptrs(std::initializer_list<const void*> req) {
+  for (const void* p : req)
+    if (!p) return SSD_E_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return SSD_E_ALIGN;
+  return SSD_OK;
+}
+
+int check_opt(std::initializer_list<const void*> opt) {
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return SSD_E_ALIGN;
+  return SSD_OK;
+}
+
+// Scale arrays are read element-wise: non-NULL and 4-byte aligned.
+int check_scales(const ssd_scales* sc) {
+  if (!sc) return SSD_E_NULL;
+  const void* req[] = {sc->s_B, sc->s_C, sc->inv_B, sc->inv_C, sc->inv_X, sc->s_S, sc->M_req};
+  for (const void* p : req)
+    if (!p) return SSD_E_NULL;
+  for (const void* p : req)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return SSD_E_ALIGN;
+  return SSD_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_E_HIP; }
+
+ssd::ScalePtrs scale_ptrs(const ssd_scales* sc) {
+  ssd::ScalePtrs p{};
+  if (sc) {
+    p.s_B = sc->s_B;
+    p.s_C = sc->s_C;
+    p.inv_B = sc->inv_B;
+    p.inv_C = sc->inv_C;
+    p.inv_X = sc->inv_X;
+    p.s_S = sc->s_S;
+    p.M_req = sc->M_req;
+  }
+  return p;
+}
+
+// Byte sizes of the intermediates.
+struct Sizes {
+  size_t qbc, cs, qd, st_i8, st_f32, cb;
+};
+Sizes sizes_of(const Dims& d) {
+  Sizes z;
+  z.qbc = (size_t)d.B * d.L * d.G * d.N;
+  z.cs = (size_t)d.B * d.H * d.c * d.l * sizeof(float);
+  z.qd = (size_t)d.B * d.H * d.c;
+  z.st_i8 = (size_t)d.B * d.c * d.H * d.P * d.N;
+  z.st_f32 = z.st_i8 * sizeof(float);
+  z.cb = (size_t)d.B * d.c * d.G * d.l * d.l * sizeof(int32_t);
+  return z;
+}
+
+// Workspace of the module-by-module composition of ssd_forward.
+size_t modular_ws_bytes(const Dims& d, bool int8) {
+  const Sizes z = sizes_of(d);
+  size_t n = 2 * align_up(z.cs) + align_up(z.cb);
+  if (int8)
+    n += 2 * align_up(z.qbc) + align_up(z.qd) + align_up(z.st_i8);
+  else
+    n += align_up(z.st_f32);
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_E_NULL: return "a required pointer is NULL";
+    case SSD_E_SHAPE: return "invalid shape (sizes, H % G, or size overflow)";
+    case SSD_E_UNSUPPORTED: return "unsupported chunk, headdim, dstate, dtype or path";
+    case SSD_E_ALIGN: return "a buffer is not 16-byte aligned";
+    case SSD_E_WORKSPACE: return "workspace too small";
+    case SSD_E_HIP: return "HIP runtime error";
+    case SSD_E_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+int ssd_quantize_bc(const ssd_shape* shape, const void* B, const void* C,
+                    const ssd_scales* scales, int8_t* qB, int8_t* qC, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_scales(scales))) return rc;
+  if ((rc = check_ptrs({B, C, qB, qC}))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_quantize_bc(d, shape->dtype, B, C, scales->inv_B, scales->inv_C,
+                                            qB, qC, (hipStream_t)stream));
+}
+
+int ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* dAcs,
+                     float* lut, uint8_t* qdecay, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_ptrs({dt, A, dAcs}))) return rc;
+  if ((rc = check_opt({lut, qdecay}))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_chunk_cumsum(d, shape->dtype, dt, A, dAcs, lut, qdecay,
+                                             (hipStream_t)stream));
+}
+
+int ssd_chunk_state(const ssd_shape* shape, int path, const void* X, const float* lut,
+                    const void* Bq, const ssd_scales* scales, void* states,
+                    const ssd_taps* taps, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_path(path))) return rc;
+  const bool i8 = path == SSD_PATH_INT8;
+  if ((rc = check_ptrs({X, lut, Bq, states}))) return rc;
+  if (i8 && (rc = check_scales(scales))) return rc;
+  int8_t* tq = (i8 && taps) ? taps->q_xs : nullptr;
+  int32_t* ts = (i8 && taps) ? taps->s32 : nullptr;
+  if ((rc = check_opt({tq, ts}))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_chunk_state(d, shape->dtype, i8, X, lut, Bq,
+                                            i8 ? scales->inv_X : nullptr,
+                                            i8 ? scales->M_req : nullptr, states, tq, ts,
+                                            (hipStream_t)stream));
+}
+
+int ssd_state_passing(const ssd_shape* shape, int path, void* states, const float* dAcs,
+                      const uint8_t* qdecay, void* final_state, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_path(path))) return rc;
+  const bool i8 = path == SSD_PATH_INT8;
+  if ((rc = check_ptrs({states, i8 ? (const void*)qdecay : (const void*)dAcs}))) return rc;
+  if ((rc = check_opt({final_state}))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_state_passing(d, i8, states, dAcs, qdecay, final_state,
+                                              (hipStream_t)stream));
+}
+
+int ssd_chunk_bmm(const ssd_shape* shape, int path, const void* Cq, const void* Bq, void* CB,
+                  void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_path(path))) return rc;
+  if ((rc = check_ptrs({Cq, Bq, CB}))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_chunk_bmm(d, shape->dtype, path == SSD_PATH_INT8, Cq, Bq, CB,
+                                          (hipStream_t)stream));
+}
+
+int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* dt,
+                   const float* dAcs, const void* Cq, const void* CB, const void* states,
+                   const float* D, const ssd_scales* scales, void* Y, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_path(path))) return rc;
+  const bool i8 = path == SSD_PATH_INT8;
+  if ((rc = check_ptrs({X, dt, dAcs, Cq, CB, states, D, Y}))) return rc;
+  if (i8 && (rc = check_scales(scales))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_chunk_scan(d, shape->dtype, i8, X, dt, dAcs, Cq, CB, states, D,
+                                           i8 ? scales->s_C : nullptr,
+                                           i8 ? scales->s_B : nullptr,
+                                           i8 ? scales->s_S : nullptr, Y, (hipStream_t)stream));
+}
+
+size_t ssd_workspace_bytes(const ssd_shape* shape, int path) {
+  Dims d;
+  bool empty;
+  if (check_shape(shape, &d, &empty) != SSD_OK || check_path(path) != SSD_OK) return 0;
+  const bool i8 = path == SSD_PATH_INT8;
+  if (empty) return 0;
+  if (ssd::fused_supported(d, shape->dtype, i8)) return ssd::fused_workspace_bytes(d, i8);
+  return modular_ws_bytes(d, i8);
+}
+
+int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt, const float* A,
+                const void* B, const void* C, const float* D, const ssd_scales* scales, void* Y,
+                void* final_state, void* workspace, size_t workspace_bytes,
+                const ssd_taps* taps, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_path(path))) return rc;
+  const bool i8 = path == SSD_PATH_INT8;
+  if ((rc = check_ptrs({X, dt, A, B, C, D, Y}))) return rc;
+  if (i8 && (rc = check_scales(scales))) return rc;
+  int8_t* tq = (i8 && taps) ? taps->q_xs : nullptr;
+  int32_t* ts = (i8 && taps) ? taps->s32 : nullptr;
+  int8_t* t8 = (i8 && taps) ? taps->s8_local : nullptr;
+  int8_t* tp = (i8 && taps) ? taps->passed : nullptr;
+  if ((rc = check_opt({final_state, workspace, tq, ts, t8, tp}))) return rc;
+  if (empty) return SSD_OK;
+  const size_t need = ssd_workspace_bytes(shape, path);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int dtype = shape->dtype;
+  const ssd::ScalePtrs sp = scale_ptrs(scales);
+
+  if (ssd::fused_supported(d, dtype, i8)) {
+    hipError_t e = ssd::launch_forward_fused(d, dtype, i8, X, dt, A, B, C, D, sp, Y, final_state,
+                                             workspace, tq, ts, t8, tp, st);
+    return hip_status(e);
+  }
+
+  // module-by-module composition
+  const Sizes z = sizes_of(d);
+  char* w = (char*)workspace;
+  float* dAcs = (float*)w;
+  w += align_up(z.cs);
+  float* lut = (float*)w;
+  w += align_up(z.cs);
+  void* CB = w;
+  w += align_up(z.cb);
+  hipError_t e;
+  if (i8) {
+    int8_t* qB = (int8_t*)w;
+    w += align_up(z.qbc);
+    int8_t* qC = (int8_t*)w;
+    w += align_up(z.qbc);
+    uint8_t* qd = (uint8_t*)w;
+    w += align_up(z.qd);
+    int8_t* states = (int8_t*)w;
+    if ((e = ssd::launch_quantize_bc(d, dtype, B, C, sp.inv_B, sp.inv_C, qB, qC, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, qd, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_state(d, dtype, true, X, lut, qB, sp.inv_X, sp.M_req, states, tq, ts, st)))
+      return SSD_E_HIP;
+    if (t8 && (e = hipMemcpyAsync(t8, states, z.st_i8, hipMemcpyDeviceToDevice, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_state_passing(d, true, states, dAcs, qd, final_state, st))) return SSD_E_HIP;
+    if (tp && (e = hipMemcpyAsync(tp, states, z.st_i8, hipMemcpyDeviceToDevice, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_bmm(d, dtype, true, qC, qB, CB, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_scan(d, dtype, true, X, dt, dAcs, qC, CB, states, D, sp.s_C, sp.s_B,
+                                    sp.s_S, Y, st)))
+      return SSD_E_HIP;
+  } else {
+    float* states = (float*)w;
+    if ((e = ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_state(d, dtype, false, X, lut, B, nullptr, nullptr, states, nullptr,
+                                     nullptr, st)))
+      return SSD_E_HIP;
+    if ((e = ssd::launch_state_passing(d, false, states, dAcs, nullptr, final_state, st)))
+      return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_bmm(d, dtype, false, C, B, CB, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_chunk_scan(d, dtype, false, X, dt, dAcs, C, CB, states, D, nullptr,
+                                    nullptr, nullptr, Y, st)))
+      return SSD_E_HIP;
+  }
+  return SSD_OK;
+}
+
+size_t ssd_calibrate_workspace_bytes(const ssd_shape* shape) {
+  Dims d;
+  bool empty;
+  if (check_shape(shape, &d, &empty) != SSD_OK || empty) return 0;
+  const Sizes z = sizes_of(d);
+  return 2 * align_up(z.cs) + align_up(z.st_f32);
+}
+
+int ssd_calibrate_amax(const ssd_shape* shape, const void* X, const void* dt, const float* A,
+                       const void* B, const void* C, float* amax, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_ptrs({X, dt, A, B, C, amax}))) return rc;
+  if ((rc = check_opt({workspace}))) return rc;
+  if (empty) return SSD_OK;
+  const size_t need = ssd_calibrate_workspace_bytes(shape);
+  if (!workspace || workspace_bytes < need) return SSD_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const Sizes z = sizes_of(d);
+  char* w = (char*)workspace;
+  float* dAcs = (float*)w;
+  w += align_up(z.cs);
+  float* lut = (float*)w;
+  w += align_up(z.cs);
+  float* states = (float*)w;
+  float* amB = amax;
+  float* amC = amax + d.G;
+  float* amX = amax + 2 * d.G;
+  float* amS = amX + (size_t)d.H * d.P;
+  const int dtype = shape->dtype;
+  if (ssd::launch_amax_bc(d, dtype, B, C, amB, amC, st)) return SSD_E_HIP;
+  if (ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st)) return SSD_E_HIP;
+  if (ssd::launch_amax_xs(d, dtype, X, lut, amX, st)) return SSD_E_HIP;
+  if (ssd::launch_chunk_state(d, dtype, false, X, lut, B, nullptr, nullptr, states, nullptr,
+                              nullptr, st))
+    return SSD_E_HIP;
+  if (ssd::launch_amax_states(d, states, amS, st)) return SSD_E_HIP;
+  if (ssd::launch_state_passing(d, false, states, dAcs, nullptr, nullptr, st)) return SSD_E_HIP;
+  if (ssd::launch_amax_states(d, states, amS, st)) return SSD_E_HIP;
+  return SSD_OK;
+}
+
+int ssd_scales_from_amax(int64_t ngroups, int64_t nheads, int64_t headdim, const float* amax,
+                         float* pack) {
+  if (!amax || !pack) return SSD_E_NULL;
+  if (ngroups <= 0 || nheads <= 0 || headdim <= 0 || nheads % ngroups) return SSD_E_SHAPE;
+  const int64_t G = ngroups, HP = nheads * headdim, hpg = nheads / ngroups;
+  auto step = [](float a) -> float {
+    const double v = (double)a;
+    if (!(v > 0.0) || !std::isfinite(v)) return 1.0f;
+    return (float)(v / 127.0);
+  };
+  float* s_B = pack;
+  float* s_C = pack + G;
+  float* inv_B = pack + 2 * G;
+  float* inv_C = pack + 3 * G;
+  float* s_X = pack + 4 * G;
+  float* inv_X = s_X + HP;
+  float* s_S = inv_X + HP;
+  float* M_req = s_S + HP;
+  for (int64_t g = 0; g < G; ++g) {
+    s_B[g] = step(amax[g]);
+    s_C[g] = step(amax[G + g]);
+    inv_B[g] = (float)(1.0 / (double)s_B[g]);
+    inv_C[g] = (float)(1.0 / (double)s_C[g]);
+  }
+  for (int64_t i = 0; i < HP; ++i) {
+    s_X[i] = step(amax[2 * G + i]);
+    s_S[i] = step(amax[2 * G + HP + i]);
+    inv_X[i] = (float)(1.0 / (double)s_X[i]);
+    const int64_t g = (i / headdim) / hpg;
+    M_req[i] = (float)((double)s_X[i] * (double)s_B[g] / (double)s_S[i]);
+  }
+  return SSD_OK;
+}
+
+}  // extern "C"

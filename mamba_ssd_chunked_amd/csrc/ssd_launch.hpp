@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI (ssd_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Validated problem dimensions. c = ceil(L / l); hpg = H / G.
+struct Dims {
+  int64_t B, L;
+  int H, P, N, G, l, c, hpg;
+};
+
+struct ScalePtrs {
+  const float* s_B;
+  const float* s_C;
+  const float* inv_B;
+  const float* inv_C;
+  const float* inv_X;
+  const float* s_S;
+  const float* M_req;
+};
+
+hipError_t launch_quantize_bc(const Dims& d, int dtype, const void* B, const void* C,
+                              const float* inv_B, const float* inv_C, int8_t* qB, int8_t* qC,
+                              hipStream_t st);
+hipError_t launch_chunk_cumsum(const Dims& d, int dtype, const void* dt, const float* A,
+                               float* dAcs, float* lut, uint8_t* qdecay, hipStream_t st);
+hipError_t launch_chunk_state(const Dims& d, int dtype, bool int8, const void* X,
+                              const float* lut, const void* Bq, const float* inv_X,
+                              const float* M_req, void* states, int8_t* tap_qxs,
+                              int32_t* tap_s32, hipStream_t st);
+hipError_t launch_state_passing(const Dims& d, bool int8, void* states, const float* dAcs,
+                                const uint8_t* qdecay, void* final_state, hipStream_t st);
+hipError_t launch_chunk_bmm(const Dims& d, int dtype, bool int8, const void* Cq,
+                            const void* Bq, void* CB, hipStream_t st);
+hipError_t launch_chunk_scan(const Dims& d, int dtype, bool int8, const void* X, const void* dt,
+                             const float* dAcs, const void* Cq, const void* CB,
+                             const void* states, const float* D, const float* s_C,
+                             const float* s_B, const float* s_S, void* Y, hipStream_t st);
+
+// Fused forward (defined in k_fused.hip). Returns hipErrorNotSupported when the
+// fused kernels do not cover the shape; the caller then composes the modules.
+hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void* X,
+                                const void* dt, const float* A, const void* B, const void* C,
+                                const float* D, const ScalePtrs& sc, void* Y, void* final_state,
+                                void* ws, int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
+                                int8_t* tap_passed, hipStream_t st);
+size_t fused_workspace_bytes(const Dims& d, bool int8);
+bool fused_supported(const Dims& d, int dtype, bool int8);
+
+// Calibration helpers (k_calib.hip).
+hipError_t launch_amax_bc(const Dims& d, int dtype, const void* B, const void* C, float* amax_B,
+                          float* amax_C, hipStream_t st);
+hipError_t launch_amax_xs(const Dims& d, int dtype, const void* X, const float* lut,
+                          float* amax_X, hipStream_t st);
+hipError_t launch_amax_states(const Dims& d, const float* states, float* amax_S, hipStream_t st);
+
+}  // namespace ssd

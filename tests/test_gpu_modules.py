@@ -1,0 +1,247 @@
+"""GPU parity of every C-ABI call against the CPU oracle.
+
+Module tests feed each GPU module the oracle's upstream values, so every stage
+is checked on its own: integer outputs bit for bit, floating outputs within
+the stated tolerance. Pipeline tests then run the GPU path from the raw inputs.
+
+Tolerances (floating outputs): max over output channels (h, p) of
+max|y - y_ref| / RMS(y_ref on that channel) <= 2e-2 (float path, against the
+float64 definition) and <= 5e-2 (INT8 path, against the INT8 method).
+"""
+import functools
+
+import numpy as np
+import pytest
+
+from oracle import ssd_oracle as O
+from tests import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+CASE_NAMES = list(H.CASES)
+
+
+@functools.lru_cache(maxsize=None)
+def case_data(name):
+    c = H.make_case(H.CASES[name])
+    e = c.ev64
+    r8 = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales,
+                        c.w.chunk)
+    yf, hf, S, Hs = O.chunked(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"],
+                              c.w.chunk)
+    return c, r8, (yf, hf, S, Hs)
+
+
+def _setup(L, name):
+    import torch
+    c, r8, fl = case_data(name)
+    d = H.dev_inputs(c)
+    sh = H.shape_of(L, c.w)
+    sc = L.ScalePack(c.scales)
+    return torch, c, r8, fl, d, sh, sc
+
+
+def _i8(t, a):
+    return t.from_numpy(np.ascontiguousarray(a.astype(np.int8))).cuda()
+
+
+def _dev(a, dtype):
+    """numpy -> dense device tensor (oracle arrays are often transposed views)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_quantize_bc(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, _, d, sh, sc = _setup(L, name)
+    qB = torch.empty(d["B"].shape, dtype=torch.int8, device="cuda")
+    qC = torch.empty_like(qB)
+    L.ssd_quantize_bc(sh, d["B"], d["C"], sc, qB, qC)
+    torch.cuda.synchronize()
+    assert np.array_equal(qB.cpu().numpy(), r8["qB"])
+    assert np.array_equal(qC.cpu().numpy(), r8["qC"])
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_chunk_cumsum(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, _, d, sh, sc = _setup(L, name)
+    w = c.w
+    n = (w.batch, w.nheads, w.nchunks, w.chunk)
+    dAcs = torch.empty(n, dtype=torch.float32, device="cuda")
+    lut = torch.empty(n, dtype=torch.float32, device="cuda")
+    qd = torch.empty(n[:3], dtype=torch.uint8, device="cuda")
+    L.ssd_chunk_cumsum(sh, d["dt"], d["A"], dAcs, lut, qd)
+    torch.cuda.synchronize()
+    cs = r8["cumsum"]
+    # same float64 additions in the same order: bit-exact
+    assert np.array_equal(dAcs.cpu().numpy(), cs["dAcs"].astype(np.float32))
+    assert np.array_equal(qd.cpu().numpy(), cs["qdecay"])
+    # LUT goes through exp(): at most one float32 ulp apart, almost always equal
+    ud = H.ulp_diff_f32(lut.cpu().numpy(), cs["lut"].astype(np.float32))
+    assert ud.max() <= 1 and (ud > 0).mean() < 1e-4
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_chunk_state_int8(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, _, d, sh, sc = _setup(L, name)
+    w = c.w
+    lut = _dev(r8["cumsum"]["lut"], np.float32)
+    qB = _i8(torch, r8["qB"])
+    st = torch.empty((w.batch, w.nchunks, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
+    qxs = torch.empty(d["x"].shape, dtype=torch.int8, device="cuda")
+    s32 = torch.empty(st.shape, dtype=torch.int32, device="cuda")
+    L.ssd_chunk_state(sh, L.SSD_PATH_INT8, d["x"], lut, qB, sc, st, taps={"q_xs": qxs, "s32": s32})
+    torch.cuda.synchronize()
+    assert np.array_equal(qxs.cpu().numpy(), r8["qxs"])
+    assert np.array_equal(s32.cpu().numpy(), r8["s32"])
+    assert np.array_equal(st.cpu().numpy(), r8["s8"])
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_state_passing_int8(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, _, d, sh, sc = _setup(L, name)
+    st = _i8(torch, r8["s8"])
+    qd = _dev(r8["cumsum"]["qdecay"], np.uint8)
+    fin = torch.empty(st[:, 0].shape, dtype=torch.int8, device="cuda")
+    L.ssd_state_passing(sh, L.SSD_PATH_INT8, st, None, qd, fin)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.cpu().numpy(), r8["passed"])
+    assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_chunk_bmm_int8(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, _, d, sh, sc = _setup(L, name)
+    w = c.w
+    cb = torch.empty((w.batch, w.nchunks, w.ngroups, w.chunk, w.chunk), dtype=torch.int32, device="cuda")
+    L.ssd_chunk_bmm(sh, L.SSD_PATH_INT8, _i8(torch, r8["qC"]), _i8(torch, r8["qB"]), cb)
+    torch.cuda.synchronize()
+    ref = np.tril(r8["cb"])
+    assert np.array_equal(cb.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_chunk_scan_int8(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, _, d, sh, sc = _setup(L, name)
+    cs = r8["cumsum"]
+    dAcs = _dev(cs["dAcs"], np.float32)
+    cb = _dev(np.tril(r8["cb"]), np.int32)
+    y = torch.empty_like(d["x"])
+    L.ssd_chunk_scan(sh, L.SSD_PATH_INT8, d["x"], d["dt"], dAcs, _i8(torch, r8["qC"]), cb,
+                     _i8(torch, r8["passed"]), d["D"], sc, y)
+    torch.cuda.synchronize()
+    assert H.chan_err(H.f64(y), r8["y"]) <= 5e-2
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_float_modules(gpu_lib, name):
+    """Float path modules: ChunkState, StatePassing, ChunkBMM, ChunkScan."""
+    L = gpu_lib
+    torch, c, r8, (yf, hf, S, Hs), d, sh, sc = _setup(L, name)
+    w = c.w
+    cs = r8["cumsum"]
+    lut = _dev(cs["lut"], np.float32)
+    dAcs = _dev(cs["dAcs"], np.float32)
+    st = torch.empty((w.batch, w.nchunks, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device="cuda")
+    L.ssd_chunk_state(sh, L.SSD_PATH_FLOAT, d["x"], lut, d["B"], None, st)
+    torch.cuda.synchronize()
+    Sg = st.cpu().numpy().astype(np.float64)
+    tol = {"fp32": 1e-5, "fp16": 2e-3, "bf16": 1.5e-2}[w.dtype]
+    assert np.abs(Sg - S).max() <= tol * np.abs(S).max()
+    # passing on the oracle's float64 local states (cast to fp32)
+    st2 = _dev(S, np.float32)
+    fin = torch.empty(st2[:, 0].shape, dtype=torch.float32, device="cuda")
+    L.ssd_state_passing(sh, L.SSD_PATH_FLOAT, st2, dAcs, None, fin)
+    torch.cuda.synchronize()
+    Hg = st2.cpu().numpy().astype(np.float64)
+    assert np.abs(Hg - Hs).max() <= 1e-4 * np.abs(Hs).max()
+    assert np.array_equal(fin.cpu().numpy(), st2[:, -1].cpu().numpy())
+    # ChunkBMM against C B^T of the stored inputs
+    cb = torch.empty((w.batch, w.nchunks, w.ngroups, w.chunk, w.chunk), dtype=torch.float32, device="cuda")
+    L.ssd_chunk_bmm(sh, L.SSD_PATH_FLOAT, d["C"], d["B"], cb)
+    torch.cuda.synchronize()
+    e = c.ev64
+    Lp = w.nchunks * w.chunk
+    pad = lambda a: np.concatenate([a, np.zeros((a.shape[0], Lp - a.shape[1]) + a.shape[2:])], 1)  # noqa: E731
+    Cp = pad(e["C"]).reshape(w.batch, w.nchunks, w.chunk, w.ngroups, w.dstate)
+    Bp = pad(e["B"]).reshape(w.batch, w.nchunks, w.chunk, w.ngroups, w.dstate)
+    ref = np.tril(np.einsum("bkign,bkjgn->bkgij", Cp, Bp))
+    cbg = cb.cpu().numpy().astype(np.float64)
+    assert np.abs(cbg - ref).max() <= {"fp32": 1e-5, "fp16": 1e-3, "bf16": 1e-3}[w.dtype] * np.abs(ref).max()
+    # ChunkScan with the oracle's passed states
+    y = torch.empty_like(d["x"])
+    L.ssd_chunk_scan(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], dAcs, d["C"], cb,
+                     _dev(Hs, np.float32), d["D"], None, y)
+    torch.cuda.synchronize()
+    assert H.chan_err(H.f64(y), yf) <= 2e-2
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_forward_int8(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, (yf, _, _, _), d, sh, sc = _setup(L, name)
+    w = c.w
+    y = torch.empty_like(d["x"])
+    stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
+    taps = {"q_xs": torch.empty(d["x"].shape, dtype=torch.int8, device="cuda"),
+            "s8_local": torch.empty(stshape, dtype=torch.int8, device="cuda"),
+            "passed": torch.empty(stshape, dtype=torch.int8, device="cuda")}
+    L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], sc, y,
+                  final_state=fin, taps=taps)
+    torch.cuda.synchronize()
+    assert np.array_equal(taps["q_xs"].cpu().numpy(), r8["qxs"])
+    assert np.array_equal(taps["s8_local"].cpu().numpy(), r8["s8"])
+    assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
+    assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
+    assert H.chan_err(H.f64(y), r8["y"]) <= 5e-2
+    # determinism: a second run is bitwise identical
+    y2 = torch.empty_like(y)
+    L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], sc, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_forward_float(gpu_lib, name):
+    L = gpu_lib
+    torch, c, r8, (yf, hf, _, _), d, sh, sc = _setup(L, name)
+    w = c.w
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device="cuda")
+    L.ssd_forward(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None, y,
+                  final_state=fin)
+    torch.cuda.synchronize()
+    assert H.chan_err(H.f64(y), yf) <= 2e-2
+    fg = fin.cpu().numpy().astype(np.float64)
+    assert np.abs(fg - hf).max() <= 2e-2 * np.sqrt(np.mean(hf * hf)) * 10
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_calibrate_amax(gpu_lib, name):
+    import torch
+    L = gpu_lib
+    c, _, _ = case_data(name)
+    w = c.w
+    cal = H.synth.calibration_sequences(w, c.consts)
+    A = torch.from_numpy(c.consts["A"]).cuda()
+    G, HP = w.ngroups, w.nheads * w.headdim
+    amax = torch.zeros(2 * G + 2 * HP, dtype=torch.float32, device="cuda")
+    for s in cal:
+        ds = {k: H.to_dev(v, w.dtype) for k, v in s.items()}
+        L.ssd_calibrate_amax(H.shape_of(L, w, batch=1), ds["x"], ds["dt"], A, ds["B"], ds["C"], amax)
+    torch.cuda.synchronize()
+    a = amax.cpu().numpy().astype(np.float64)
+    ref = O.calibrate([H.synth.as_f64(s, w.dtype) for s in cal], c.consts["A"], G, w.chunk)
+    assert np.array_equal(a[:G], ref["B"]) and np.array_equal(a[G:2 * G], ref["C"])
+    ax = a[2 * G:2 * G + HP].reshape(ref["Xs"].shape)
+    assert np.abs(ax - ref["Xs"]).max() <= 1e-6 * ref["Xs"].max()
+    asx = a[2 * G + HP:].reshape(ref["S"].shape)
+    tol = {"fp32": 1e-4, "fp16": 2e-2, "bf16": 5e-2}[w.dtype]
+    assert np.all(np.abs(asx - ref["S"]) <= tol * ref["S"] + 1e-6)
