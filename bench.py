@@ -1,0 +1,213 @@
+"""Benchmark of the SSD-layer forward on one MI355X.
+
+A step is one ssd_forward call (the whole hot path: B/C quantisation,
+ChunkCumsum, ChunkState, StatePassing, ChunkBMM, ChunkScan) over one batch of
+synthetic Mamba-2 2.7B-shaped input (batch 8, L 2048, H 80, P 64, N 128, G 1,
+chunk 256, fp16), already resident in HBM. The INT8 path is the headline line;
+the float path is measured beside it.
+
+Prints one JSON line. --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
+WORKLOAD_ID = 2           # Mamba-2 2.7B-shaped layer
+
+
+def algorithmic_bytes_per_token(w, int8: bool) -> int:
+    """X, dt, B, C read once, Y written once, plus one chunk-state exchange
+    (each chunk-boundary state written once and read once) at the path's state
+    width: int8, or the input dtype for the float path."""
+    esz = {"fp32": 4, "fp16": 2, "bf16": 2}[w.dtype]
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    io = esz * (2 * H * P + H + 2 * G * N)
+    state = (1 if int8 else esz) * 2 * H * P * N / w.chunk
+    return int(round(io + state))
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, path: str):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    f = os.path.join(ROOT, "profiles", f"traffic_{workload}_{path}.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(w, consts, ev) -> dict:
+    """The float64 recurrence oracle timed on host cores, on one sequence of the
+    batch (all heads, full length), split by heads over a process pool."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    from mamba_ssd_chunked_amd import synth
+
+    x = synth.to_f64(ev["x"][:1], w.dtype)
+    dt = synth.to_f64(ev["dt"][:1], w.dtype)
+    B = synth.to_f64(ev["B"][:1], w.dtype)
+    C = synth.to_f64(ev["C"][:1], w.dtype)
+    ncpu = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, ncpu, w.nheads))
+    per = -(-w.nheads // workers)
+    hpg = w.nheads // w.ngroups
+    jobs = []
+    for h0 in range(0, w.nheads, per):
+        h1 = min(w.nheads, h0 + per)
+        g0, g1 = h0 // hpg, (h1 - 1) // hpg + 1
+        # a head block inside whole groups keeps the head -> group map
+        jobs.append((x[:, :, h0:h1], dt[:, :, h0:h1], consts["A"][h0:h1], B[:, :, g0:g1],
+                     C[:, :, g0:g1], consts["D"][h0:h1], h0, hpg, g0))
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_recurrence_job, jobs))
+    t1 = time.perf_counter()
+    tokens_per_s = w.seqlen / (t1 - t0)          # one sequence of L tokens, all heads
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 recurrence on 1 of {w.batch} sequences (all {w.nheads} heads, "
+                      f"L={w.seqlen}); {t1 - t0:.1f} s wall on {workers} processes",
+            "seconds": t1 - t0}
+
+
+def _recurrence_job(job):
+    import numpy as np
+
+    from oracle import ssd_oracle as O
+    x, dt, A, B, C, D, h0, hpg, g0 = job
+    H = x.shape[2]
+    # remap the block's heads onto its local groups
+    g_local = (np.arange(h0, h0 + H) // hpg) - g0
+    Bh = B[:, :, g_local]
+    Ch = C[:, :, g_local]
+    y, _ = O.recurrence(x, dt, A, Bh, Ch, D)
+    return float(y[0, -1, 0, 0])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paths", default="int8,float")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the SSD layer runs on a single MI355X here "
+              "(no multi-GPU path is built); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mamba_ssd_chunked_amd import _lib as L
+    from mamba_ssd_chunked_amd import synth
+
+    w = synth.WORKLOADS[WORKLOAD_ID]
+    consts = synth.layer_constants(w)
+    ev = synth.evaluation_batch(w, consts)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in ev.items()}
+    A = torch.from_numpy(consts["A"]).cuda()
+    D = torch.from_numpy(consts["D"]).cuda()
+    sh = L.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+
+    # static scales from the two calibration sequences, on the GPU
+    cal = synth.calibration_sequences(w, consts)
+    cal_dev = [{k: torch.from_numpy(v).cuda() for k, v in s.items()} for s in cal]
+    scales = L.calibrate(lambda s: L.make_shape(1, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                                w.ngroups, w.chunk, w.dtype), cal_dev, A)
+    y = torch.empty_like(dev["x"])
+    tokens = w.batch * w.seqlen
+    results = {}
+    for path_name in args.paths.split(","):
+        path = L.SSD_PATH_INT8 if path_name == "int8" else L.SSD_PATH_FLOAT
+        ws = torch.empty(max(1, L.ssd_workspace_bytes(sh, path)), dtype=torch.uint8, device="cuda")
+        sc = scales if path == L.SSD_PATH_INT8 else None
+
+        def step():
+            L.ssd_forward(sh, path, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, sc, y,
+                          workspace=ws)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev_s[i].record()
+            step()
+            ev_e[i].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per_call_ms = np.array([s.elapsed_time(e) for s, e in zip(ev_s, ev_e)])
+        ms_per_step = (t1 - t0) * 1e3 / args.steps
+        bpt = algorithmic_bytes_per_token(w, path == L.SSD_PATH_INT8)
+        bytes_per_call = bpt * tokens
+        avg_call_s = float(per_call_ms.mean()) * 1e-3
+        achieved = bytes_per_call / avg_call_s / 1e9
+        traffic = measured_traffic(w.name, path_name)
+        results[path_name] = {
+            "value": tokens / (ms_per_step * 1e-3),
+            "ms_per_step": ms_per_step,
+            "call_ms": {"mean": float(per_call_ms.mean()), "median": float(np.median(per_call_ms)),
+                        "p10": float(np.percentile(per_call_ms, 10)),
+                        "p90": float(np.percentile(per_call_ms, 90))},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                         "kernel": "ssd_forward (all kernels of one call)",
+                         "algorithmic_bytes_per_call": bytes_per_call,
+                         "algorithmic_bytes_per_token": bpt},
+        }
+    head = results.get("int8") or next(iter(results.values()))
+    out = {
+        "metric": "SSD-layer tokens/s (INT8 & fp16) at 1 MI355X; % of HBM/int8-MFMA roofline",
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if "int8" in results else w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk, "input_dtype": w.dtype, "path": "int8"},
+        "roofline": head["roofline"],
+        "paths": results,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, consts, ev)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,6 +16,8 @@ CASES = {
     "bf16_l128": synth.Workload(12, 1, 300, 4, 32, 64, 1, 128, "bf16", True),
     "f16_g_eq_h": synth.Workload(13, 1, 200, 4, 16, 32, 4, 64, "fp16", False),
     "f32_l256": synth.Workload(14, 1, 512, 2, 64, 128, 1, 256, "fp32", True),
+    "bf16_n64_l128": synth.Workload(15, 2, 700, 6, 64, 64, 2, 128, "bf16", True),
+    "f16_l128": synth.Workload(16, 1, 384, 3, 64, 128, 1, 128, "fp16", True),
 }
 
 

@@ -182,6 +182,28 @@ def test_float_modules(gpu_lib, name):
     assert H.chan_err(H.f64(y), yf) <= 2e-2
 
 
+def _modular_int8(L, torch, c, d, sh, sc):
+    """The INT8 path through the six module calls (GPU outputs feed GPU modules)."""
+    w = c.w
+    qB = torch.empty(d["B"].shape, dtype=torch.int8, device="cuda")
+    qC = torch.empty_like(qB)
+    L.ssd_quantize_bc(sh, d["B"], d["C"], sc, qB, qC)
+    n = (w.batch, w.nheads, w.nchunks, w.chunk)
+    dAcs = torch.empty(n, dtype=torch.float32, device="cuda")
+    lut = torch.empty_like(dAcs)
+    qd = torch.empty(n[:3], dtype=torch.uint8, device="cuda")
+    L.ssd_chunk_cumsum(sh, d["dt"], d["A"], dAcs, lut, qd)
+    st = torch.empty((w.batch, w.nchunks, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
+    L.ssd_chunk_state(sh, L.SSD_PATH_INT8, d["x"], lut, qB, sc, st)
+    L.ssd_state_passing(sh, L.SSD_PATH_INT8, st, None, qd)
+    cb = torch.empty((w.batch, w.nchunks, w.ngroups, w.chunk, w.chunk), dtype=torch.int32, device="cuda")
+    L.ssd_chunk_bmm(sh, L.SSD_PATH_INT8, qC, qB, cb)
+    y = torch.empty_like(d["x"])
+    L.ssd_chunk_scan(sh, L.SSD_PATH_INT8, d["x"], d["dt"], dAcs, qC, cb, st, d["D"], sc, y)
+    torch.cuda.synchronize()
+    return {"passed": st.cpu().numpy(), "y": H.f64(y)}
+
+
 @pytest.mark.parametrize("name", CASE_NAMES)
 def test_forward_int8(gpu_lib, name):
     L = gpu_lib
@@ -191,21 +213,29 @@ def test_forward_int8(gpu_lib, name):
     stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
     taps = {"q_xs": torch.empty(d["x"].shape, dtype=torch.int8, device="cuda"),
+            "s32": torch.empty(stshape, dtype=torch.int32, device="cuda"),
             "s8_local": torch.empty(stshape, dtype=torch.int8, device="cuda"),
             "passed": torch.empty(stshape, dtype=torch.int8, device="cuda")}
     L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], sc, y,
                   final_state=fin, taps=taps)
     torch.cuda.synchronize()
     assert np.array_equal(taps["q_xs"].cpu().numpy(), r8["qxs"])
+    assert np.array_equal(taps["s32"].cpu().numpy(), r8["s32"])
     assert np.array_equal(taps["s8_local"].cpu().numpy(), r8["s8"])
     assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
     assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
     assert H.chan_err(H.f64(y), r8["y"]) <= 5e-2
-    # determinism: a second run is bitwise identical
+    # determinism: a second run (without taps) is bitwise identical, final state too
     y2 = torch.empty_like(y)
-    L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], sc, y2)
+    fin2 = torch.empty_like(fin)
+    L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], sc, y2,
+                  final_state=fin2)
     torch.cuda.synchronize()
-    assert torch.equal(y, y2)
+    assert torch.equal(y, y2) and torch.equal(fin, fin2)
+    # and the module-by-module composition gives the same integers and Y within tolerance
+    ym = _modular_int8(L, torch, c, d, sh, sc)
+    assert np.array_equal(ym["passed"], r8["passed"])
+    assert H.chan_err(ym["y"], H.f64(y)) <= 5e-2
 
 
 @pytest.mark.parametrize("name", CASE_NAMES)
