@@ -45,43 +45,54 @@ __global__ __launch_bounds__(256) void k_quantize_bc(const void* __restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// ChunkCumsum: one thread per (b, k, h) chain, float64 accumulation in
-// sequence order. The second pass repeats the identical additions, so its
-// partial sums equal the first pass's bit for bit.
+// ChunkCumsum. One block per (chunk k, batch b, 16-head group). dt is staged in
+// LDS; one thread per head then forms the float64 prefix sums in sequence order
+// (the only serial part), and all threads evaluate the float64 exponentials and
+// write dAcs / LUT_state with coalesced stores. Padded positions past L carry
+// dt = 0, which leaves the running sum unchanged.
 // ---------------------------------------------------------------------------
+constexpr int kCsHeads = 16;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_chunk_cumsum(const void* __restrict__ dt,
                                                       const float* __restrict__ A,
                                                       float* __restrict__ dAcs,
                                                       float* __restrict__ lut,
                                                       uint8_t* __restrict__ qdecay, Dims d) {
-  const int64_t chain = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t nchain = d.B * (int64_t)d.c * d.H;
-  if (chain >= nchain) return;
-  const int h = (int)(chain % d.H);
-  const int k = (int)((chain / d.H) % d.c);
-  const int64_t b = chain / ((int64_t)d.H * d.c);
-  const double Ah = (double)A[h];
-  const int64_t t0 = (int64_t)k * d.l;
-  const int nvalid = (int)min((int64_t)d.l, d.L - t0);
-  const int64_t in0 = (b * d.L + t0) * d.H + h;
-  double a = 0.0;
-  for (int s = 0; s < nvalid; ++s) a += (double)ld_f<DT>(dt, in0 + (int64_t)s * d.H) * Ah;
-  const double alast = a;
-  const int64_t out0 = ((b * d.H + h) * d.c + k) * (int64_t)d.l;
-  a = 0.0;
-  for (int s = 0; s < d.l; ++s) {
-    double dv = 0.0;
-    if (s < nvalid) {
-      dv = (double)ld_f<DT>(dt, in0 + (int64_t)s * d.H);
-      a += dv * Ah;
-    }
-    dAcs[out0 + s] = (float)a;
-    if (lut) lut[out0 + s] = (float)(dv * exp(alast - a));
+  __shared__ float sdt[kCsHeads][256 + 1];
+  __shared__ double sa[kCsHeads][256 + 1];
+  const int k = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int h0 = blockIdx.z * kCsHeads;
+  const int nh = min(kCsHeads, d.H - h0);
+  const int l = d.l;
+  const int64_t t0 = (int64_t)k * l;
+  const int nvalid = (int)min((int64_t)l, d.L - t0);
+  for (int idx = threadIdx.x; idx < kCsHeads * l; idx += 256) {
+    const int j = idx % kCsHeads, s = idx / kCsHeads;
+    float v = 0.f;
+    if (j < nh && s < nvalid) v = ld_f<DT>(dt, (b * d.L + t0 + s) * d.H + h0 + j);
+    sdt[j][s] = v;
   }
-  if (qdecay) {
-    const double q = fmin(round(exp(alast) * 128.0), 128.0);
-    qdecay[(b * d.H + h) * d.c + k] = (uint8_t)q;
+  __syncthreads();
+  if ((int)threadIdx.x < nh) {
+    const int j = threadIdx.x;
+    const double Ah = (double)A[h0 + j];
+    double a = 0.0;
+    for (int s = 0; s < l; ++s) {
+      a += (double)sdt[j][s] * Ah;  // the product is exact in float64
+      sa[j][s] = a;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * l; idx += 256) {
+    const int j = idx / l, s = idx % l;
+    const double a = sa[j][s], alast = sa[j][l - 1];
+    const int64_t o = ((b * d.H + h0 + j) * d.c + k) * (int64_t)l + s;
+    dAcs[o] = (float)a;
+    if (lut) lut[o] = (float)((double)sdt[j][s] * exp(alast - a));
+    if (qdecay && s == 0)
+      qdecay[(b * d.H + h0 + j) * d.c + k] = (uint8_t)fmin(round(exp(alast) * 128.0), 128.0);
   }
 }
 
@@ -552,9 +563,8 @@ hipError_t launch_quantize_bc(const Dims& d, int dtype, const void* B, const voi
 
 hipError_t launch_chunk_cumsum(const Dims& d, int dtype, const void* dt, const float* A,
                                float* dAcs, float* lut, uint8_t* qdecay, hipStream_t st) {
-  const int64_t n = d.B * (int64_t)d.c * d.H;
-  const unsigned grid = (unsigned)((n + 255) / 256);
-#define L_(DT_) hipLaunchKernelGGL(k_chunk_cumsum<DT_>, dim3(grid), dim3(256), 0, st, dt, A, dAcs, lut, qdecay, d)
+  const dim3 grid(d.c, (unsigned)d.B, (d.H + kCsHeads - 1) / kCsHeads);
+#define L_(DT_) hipLaunchKernelGGL(k_chunk_cumsum<DT_>, grid, dim3(256), 0, st, dt, A, dAcs, lut, qdecay, d)
   SSD_DISPATCH_DT(dtype, L_)
 #undef L_
   return hipGetLastError();

@@ -232,6 +232,8 @@ __device__ __forceinline__ void glb_frag8(const void* p, int64_t i, FragF<DT>& f
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index within the workgroup, in a scalar register (it is uniform across
+// the wave, which lets loops and branches on it stay scalar).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 }  // namespace ssd

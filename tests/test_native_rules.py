@@ -17,3 +17,13 @@ def test_int8_quantiser_shortcut_is_exact_for_every_float32(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert " 0 mismatches" in r.stdout
+
+
+def test_rounding_shift_arithmetic_form():
+    """(v + 64 + (v >> 31)) >> 7 (arithmetic shifts) equals sign(v)*((|v| + 64) >> 7)
+    for every product Q(Decay) * state the StatePassing update can form."""
+    import numpy as np
+    v = np.arange(-128 * 127, 128 * 127 + 1, dtype=np.int64)
+    ref = np.sign(v) * ((np.abs(v) + 64) >> 7)
+    fast = (v + 64 + (v >> 63)) >> 7
+    assert np.array_equal(fast, ref)
