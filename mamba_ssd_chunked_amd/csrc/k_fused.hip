@@ -60,11 +60,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // with low row bits, so the 8 or 16 lanes served together hit distinct banks.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int xsw(int p) { return (p ^ (p >> 3)) & 7; }
-// x transposed, [p][s] in 2-byte elements; s aligned to 4 (8-byte units). The
-// two 8-byte halves of a chunk are also swapped when (p >> 3) & 1.
+// x transposed, [p][s'] in 2-byte elements, with s reordered inside each block
+// of 32 positions (two 16-position column tiles 2m and 2m + 1): the 4-position
+// runs s = 32m + 16h + 4g + (0..3) sit at 32m + 8g + 4h + (0..3). A lane's
+// ChunkScan2 operand (group g of tiles 2m and 2m + 1) is then one 16-byte
+// chunk, index 4m + g, XOR-swizzled with the row.
 template <int LC>
-__device__ __forceinline__ int xT_off(int p, int s) {
-  return p * LC + 8 * ((s >> 3) ^ xsw(p)) + 4 * (((s >> 2) & 1) ^ ((p >> 3) & 1));
+__device__ __forceinline__ int xT_pair(int p, int m, int g) {  // 16-byte chunk start
+  return p * LC + 8 * ((4 * m + g) ^ xsw(p));
+}
+template <int LC>
+__device__ __forceinline__ int xT_off(int p, int s) {  // s aligned to 4
+  return xT_pair<LC>(p, s >> 5, (s >> 2) & 3) + 4 * ((s >> 4) & 1);
 }
 // byte tiles [rows][W]; c a byte column aligned to 4
 template <int W>
@@ -73,22 +80,14 @@ __device__ __forceinline__ int b_off(int r, int c) {
   return r * W + 16 * ((c >> 4) ^ (r & (nch - 1) & 7)) + (c & 15);
 }
 
-// Eight 2-byte input values (two runs of four) as an MFMA operand fragment.
+// Eight 2-byte input values read from LDS as an MFMA operand fragment.
 template <int DT>
-__device__ __forceinline__ FragF<DT> frag_from_halves(uint2 lo, uint2 hi) {
+__device__ __forceinline__ FragF<DT> frag16(const u16* p) {
   FragF<DT> f;
-  const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u16 a = (u16)(w4[j] & 0xffff), b2 = (u16)(w4[j] >> 16);
-    if constexpr (DT == DT_F16) {
-      f.v[2 * j] = __builtin_bit_cast(_Float16, a);
-      f.v[2 * j + 1] = __builtin_bit_cast(_Float16, b2);
-    } else {
-      f.v[2 * j] = __builtin_bit_cast(__bf16, a);
-      f.v[2 * j + 1] = __builtin_bit_cast(__bf16, b2);
-    }
-  }
+  if constexpr (DT == DT_F16)
+    f.v = *(const v8h*)p;
+  else
+    f.v = *(const v8bf*)p;
   return f;
 }
 
@@ -174,29 +173,45 @@ struct FusedArgs {
 
 template <int LC, int NS>
 struct Lds {
-  static constexpr int XT = kP * LC * 2;  // bytes of one x^T buffer
-  static constexpr int QB = LC * NS;      // bytes of one Q(B) buffer
-  static constexpr int H8 = kP * NS;
-  static constexpr int VEC = 3 * LC * 4;  // a*log2(e), dt, lut (floats)
+  static constexpr int XT = kP * LC * 2;  // x^T [p][s], 2-byte elements
+  static constexpr int QB = LC * NS;      // Q(B) rows [s][n]
+  static constexpr int QX = kP * LC;      // Q(X_scaled)^T [p][s]
+  static constexpr int H8 = kP * NS;      // passed state [p][n]
+  static constexpr int VEC = 2 * LC * 4;  // a*log2(e), dt
   static constexpr int VW = kWaves * LC * 4;
+  static constexpr int SS = 2 * kP * 4;   // s_S[h, p], inv_X[h, p]
   static constexpr int off_xt = 0;
-  static constexpr int off_qb = off_xt + 2 * XT;
-  static constexpr int off_h8 = off_qb + 2 * QB;
+  static constexpr int off_qb = off_xt + XT;
+  static constexpr int off_qx = off_qb + QB;
+  static constexpr int off_h8 = off_qx + QX;
   static constexpr int off_vec = off_h8 + H8;
-  static constexpr int off_vw = off_vec + 2 * VEC;
-  static constexpr int total = off_vw + VW;
+  static constexpr int off_vw = off_vec + VEC;
+  static constexpr int off_ss = off_vw + VW;
+  static constexpr int total = off_ss + SS;
 };
 
-// Registers holding the next chunk while the current one computes.
+// Q(X_scaled)^T tile [p][s] (bytes); s aligned to 4
+template <int LC>
+__device__ __forceinline__ int qx_off(int p, int s) {
+  return p * LC + 16 * ((s >> 4) ^ xsw(p)) + (s & 15);
+}
+
+// Registers holding the next chunk while the current one computes. Thread
+// (q = tid / 8, c8 = tid % 8) owns x rows 4q .. 4q+3 at p = 8 c8 .. 8 c8 + 7.
+// Every load is unconditional (addresses are clamped into the tensor and
+// out-of-range rows are zeroed when stored to LDS), so no branch forces the
+// compiler to wait for them before the chunk's compute.
 template <int LC, int NS>
 struct Prefetch {
-  static constexpr int XI = (LC / 4) * (kP / 8);     // x items: 4 rows x 16 bytes
-  static constexpr int XPT = (XI + kThreads - 1) / kThreads;
-  static constexpr int QI = LC * NS / 16;            // Q(B) 16-byte chunks
-  static constexpr int QPT = QI / kThreads;
-  uint4 x[XPT][4];
+  static constexpr int XI = (LC / 4) * (kP / 8);
+  static constexpr int QPT = LC * NS / 16 / kThreads;
+  static_assert(XI <= kThreads && QPT >= 1, "tile split");
+  uint4 x[4];
+  float4 lut;
   uint4 q[QPT];
-  float va, vd, vl;
+  float va;     // dAcs (scaled by log2(e) when stored)
+  uint32_t vd;  // dt bits in the input type (converted when stored)
+  uint32_t qd;  // the dword holding Q(Decay) of the chunk
 };
 
 template <int DT, int LC, int NS>
@@ -208,16 +223,17 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)k * LC;
   const int64_t Lp = (int64_t)d.c * LC;
+  const int64_t cs0 = ((b * d.H + h) * d.c + k) * (int64_t)LC;
+  {
+    const int it = tid % PF::XI;
+    const int q = it >> 3, c8 = it & 7;
+    const T* xb = (const T*)a.X + (b * d.L * d.H + h) * (int64_t)kP + 8 * c8;
 #pragma unroll
-  for (int m = 0; m < PF::XPT; ++m) {
-    const int item = tid + m * kThreads;
-    const int q = item >> 3, c8 = item & 7;
-    const int64_t tq = t0 + 4 * q;
-    const T* xrow = (const T*)a.X + ((b * d.L + tq) * d.H + h) * (int64_t)kP + 8 * c8;
-    const int nrow = (item < PF::XI) ? (int)min((int64_t)4, d.L - tq) : 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      pf.x[m][r] = (r < nrow) ? *(const uint4*)(xrow + r * d.H * kP) : make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = min(t0 + 4 * q + r, d.L - 1);
+      pf.x[r] = *(const uint4*)(xb + t * d.H * kP);
+    }
+    pf.lut = *(const float4*)(a.lut + cs0 + 4 * q);
   }
   const int8_t* src = a.qB + ((b * Lp + t0) * d.G + g_h) * (int64_t)NS;
 #pragma unroll
@@ -226,44 +242,79 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
     const int s = id / (NS / 16), c16 = id % (NS / 16);
     pf.q[m] = *(const uint4*)(src + (int64_t)s * d.G * NS + 16 * c16);
   }
-  if (tid < LC) {
-    const int64_t ci = ((b * d.H + h) * d.c + k) * (int64_t)LC + tid;
-    pf.va = a.dAcs[ci] * kLog2e;
-    pf.vl = a.lut[ci];
-    const int64_t t = t0 + tid;
-    pf.vd = (t < d.L) ? Store<DT>::to_f(((const T*)a.dt)[(b * d.L + t) * d.H + h]) : 0.f;
+  {
+    const int sv = tid % LC;
+    pf.va = a.dAcs[cs0 + sv];
+    const int64_t t = min(t0 + sv, d.L - 1);
+    if constexpr (sizeof(T) == 4)
+      pf.vd = ((const uint32_t*)a.dt)[(b * d.L + t) * d.H + h];
+    else
+      pf.vd = ((const u16*)a.dt)[(b * d.L + t) * d.H + h];
   }
+  const int64_t qi = (b * d.H + h) * d.c + k;
+  pf.qd = *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
 }
 
-template <int LC, int NS>
-__device__ __forceinline__ void prefetch_store(char* lds, int buf, const Prefetch<LC, NS>& pf) {
+// Writes the prefetched chunk into LDS: x transposed, Q(X_scaled) =
+// sat(RHAZ(fl32(fl32(lut * x) * inv_X))) transposed (the quantiser of "Key
+// design 1"), Q(B) rows and the per-position vectors.
+template <int DT, int LC, int NS>
+__device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, int64_t b, int h, int k,
+                                               const Prefetch<LC, NS>& pf) {
+  typedef typename Store<DT>::T T;
   typedef Lds<LC, NS> LY;
   typedef Prefetch<LC, NS> PF;
   const int tid = threadIdx.x;
-  u16* xT = (u16*)(lds + LY::off_xt + buf * LY::XT);
+  const int64_t t0 = (int64_t)k * LC;
+  if (tid < PF::XI) {
+    const int q = tid >> 3, c8 = tid & 7;
+    u16* xT = (u16*)(lds + LY::off_xt);
+    int8_t* qx = (int8_t*)(lds + LY::off_qx);
+    uint4 xr[4];
 #pragma unroll
-  for (int m = 0; m < PF::XPT; ++m) {
-    const int item = tid + m * kThreads;
-    if (item < PF::XI) {
-      const int q = item >> 3, c8 = item & 7;
-      const uint32_t* w0 = (const uint32_t*)&pf.x[m][0];
-      const uint32_t* w1 = (const uint32_t*)&pf.x[m][1];
-      const uint32_t* w2 = (const uint32_t*)&pf.x[m][2];
-      const uint32_t* w3 = (const uint32_t*)&pf.x[m][3];
+    for (int r = 0; r < 4; ++r) xr[r] = (t0 + 4 * q + r < a.d.L) ? pf.x[r] : make_uint4(0, 0, 0, 0);
+    const uint32_t* w0 = (const uint32_t*)&xr[0];
+    const uint32_t* w1 = (const uint32_t*)&xr[1];
+    const uint32_t* w2 = (const uint32_t*)&xr[2];
+    const uint32_t* w3 = (const uint32_t*)&xr[3];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // dword e of each row holds p = 8 c8 + 2e (low half) and 2e + 1 (high half)
-        const uint32_t lo01 = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
-        const int p0 = 8 * c8 + 2 * e;
-        *(uint2*)&xT[xT_off<LC>(p0, 4 * q)] = make_uint2(lo01, lo23);
-        *(uint2*)&xT[xT_off<LC>(p0 + 1, 4 * q)] = make_uint2(hi01, hi23);
+    for (int e = 0; e < 4; ++e) {
+      // dword e of each row holds p = 8 c8 + 2e (low half) and 2e + 1 (high half)
+      const uint32_t lo01 = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
+      const int p0 = 8 * c8 + 2 * e;
+      *(uint2*)&xT[xT_off<LC>(p0, 4 * q)] = make_uint2(lo01, lo23);
+      *(uint2*)&xT[xT_off<LC>(p0 + 1, 4 * q)] = make_uint2(hi01, hi23);
+    }
+    const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
+    const float* ixl = (const float*)(lds + LY::off_ss) + kP + 8 * c8;
+    const float4 i0 = *(const float4*)ixl, i1 = *(const float4*)(ixl + 4);
+    const float invx8[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+    int qv[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const T* xe = (const T*)&xr[r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[r][e] = q8((lutv[r] * Store<DT>::to_f(xe[e])) * invx8[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *(uint32_t*)&qx[qx_off<LC>(8 * c8 + e, 4 * q)] = pack4(qv[0][e], qv[1][e], qv[2][e], qv[3][e]);
+    if (a.tap_qxs) {
+      const Dims& d = a.d;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = (int64_t)k * LC + 4 * q + r;
+        if (t < d.L)
+          *(uint2*)(a.tap_qxs + ((b * d.L + t) * d.H + h) * (int64_t)kP + 8 * c8) =
+              make_uint2(pack4(qv[r][0], qv[r][1], qv[r][2], qv[r][3]),
+                         pack4(qv[r][4], qv[r][5], qv[r][6], qv[r][7]));
       }
     }
   }
-  int8_t* qb = (int8_t*)(lds + LY::off_qb + buf * LY::QB);
+  int8_t* qb = (int8_t*)(lds + LY::off_qb);
 #pragma unroll
   for (int m = 0; m < PF::QPT; ++m) {
     const int id = tid + m * kThreads;
@@ -271,10 +322,14 @@ __device__ __forceinline__ void prefetch_store(char* lds, int buf, const Prefetc
     *(uint4*)&qb[b_off<NS>(s, 16 * c16)] = pf.q[m];
   }
   if (tid < LC) {
-    float* vec = (float*)(lds + LY::off_vec + buf * LY::VEC);
-    vec[tid] = pf.va;
-    vec[LC + tid] = pf.vd;
-    vec[2 * LC + tid] = pf.vl;
+    float* vec = (float*)(lds + LY::off_vec);
+    vec[tid] = pf.va * kLog2e;
+    float dtv;
+    if constexpr (sizeof(T) == 4)
+      dtv = __uint_as_float(pf.vd);
+    else
+      dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)pf.vd));
+    vec[LC + tid] = (t0 + tid < a.d.L) ? dtv : 0.f;
   }
 }
 
@@ -282,15 +337,21 @@ template <int DT, int LC, int NS>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   typedef typename Store<DT>::T T;
   typedef Lds<LC, NS> LY;
+  typedef Prefetch<LC, NS> PF;
   constexpr int RT = LC / 16;      // row tiles of the chunk
   constexpr int NT = NS / 16;      // n tiles of the state
-  constexpr int NTW = NT / 2;      // n tiles per wave
+  constexpr int PTW = 4 * NT / kWaves;  // p tiles per wave in ChunkState / StatePassing
   constexpr int KS = LC / 64;      // ChunkState K steps
   constexpr int KN = NS / 64;      // K steps over N
-  constexpr int SPT = LC / 8;      // Q(Xs) positions quantised per thread
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const u16* xT = (const u16*)(lds + LY::off_xt);
+  const int8_t* qBl = (const int8_t*)(lds + LY::off_qb);
+  const int8_t* qxl = (const int8_t*)(lds + LY::off_qx);
   int8_t* H8l = (int8_t*)(lds + LY::off_h8);
+  const float* vA2 = (const float*)(lds + LY::off_vec);
+  const float* vDt = vA2 + LC;
+  float* SSl = (float*)(lds + LY::off_ss);
 
   const Dims& d = a.d;
   const int h = blockIdx.x % d.H;
@@ -301,113 +362,96 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   const int64_t Lp = (int64_t)d.c * LC;
   const int H = d.H;
 
-  const int pt_own = w & 3;                // ChunkState / StatePassing p tile
-  const int ng = w >> 2;                   // half of the n tiles
-  const int p_own = 16 * pt_own + l16;
-  const float mreq = a.sc.M_req[h * kP + p_own];
+  // ChunkState / StatePassing role: n tile nt_own, p tiles pt0 .. pt0 + PTW - 1
+  // (each Q(B)^T row is read by exactly one wave)
+  const int nt_own = w % NT;
+  const int pt0 = (w / NT) * PTW;
+  float mreq[PTW];
+#pragma unroll
+  for (int j = 0; j < PTW; ++j) mreq[j] = a.sc.M_req[h * kP + 16 * (pt0 + j) + l16];
   const float scBC = a.sc.s_C[g_h] * a.sc.s_B[g_h];
   const float sC = a.sc.s_C[g_h];
   const float Dh = a.D[h];
-  float sS[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) sS[pt] = a.sc.s_S[h * kP + 16 * pt + l16];
-  // Q(Xs) quantisation role: p_q = tid % 64, positions [s_q0, s_q0 + SPT)
-  const int p_q = tid & 63;
-  const int s_q0 = (tid >> 6) * SPT;
-  const float invx_q = a.sc.inv_X[h * kP + p_q];
+  if (tid < kP) {
+    SSl[tid] = a.sc.s_S[h * kP + tid];
+    SSl[kP + tid] = a.sc.inv_X[h * kP + tid];
+  }
+  __syncthreads();
   float* Vw = (float*)(lds + LY::off_vw) + w * LC;
 
-  uint32_t H8[NTW];
+  uint32_t H8[PTW];  // passed state: lane (p = 16 (pt0 + j) + l16, n = 16 nt_own + 4 lg + r)
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) H8[j] = 0;
+  for (int j = 0; j < PTW; ++j) H8[j] = 0;
 
-  {  // chunk 0 into buffer 0
-    Prefetch<LC, NS> pf;
+  uint32_t qd_word;  // dword holding Q(Decay) of the current chunk
+  {  // chunk 0
+    PF pf;
     prefetch_load<DT, LC, NS>(a, b, h, g_h, 0, pf);
-    prefetch_store<LC, NS>(lds, 0, pf);
+    prefetch_store<DT, LC, NS>(a, lds, b, h, 0, pf);
+    qd_word = pf.qd;
   }
 
   for (int k = 0; k < d.c; ++k) {
-    const int cur = k & 1;
     const int64_t t0 = (int64_t)k * LC;
-    const u16* xT = (const u16*)(lds + LY::off_xt + cur * LY::XT);
-    const int8_t* qBl = (const int8_t*)(lds + LY::off_qb + cur * LY::QB);
-    int8_t* qxs = (int8_t*)(lds + LY::off_qb + (cur ^ 1) * LY::QB);  // scratch [p][s]
-    const float* vA2 = (const float*)(lds + LY::off_vec + cur * LY::VEC);
-    const float* vDt = vA2 + LC;
-    const float* vLut = vA2 + 2 * LC;
-    __syncthreads();
-
-    // ---- Q(X_scaled) = sat(RHAZ(fl32(fl32(lut * x) * inv_X))) into the scratch tile ----
+    __syncthreads();  // chunk k staged; H8l holds H_{k-1}
+    const int qd = (int)((qd_word >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
+    // Q(C) rows of this wave's row tiles (B operand over N), issued first
+    v4i qc2[2][KN];
 #pragma unroll
-    for (int c8 = 0; c8 < SPT / 8; ++c8) {
-      const int s8 = s_q0 + 8 * c8;
-      uint4 xv = *(const uint4*)&xT[xT_off<LC>(p_q, s8) & ~7];
-      if ((p_q >> 3) & 1) xv = make_uint4(xv.z, xv.w, xv.x, xv.y);
-      const T* xe = (const T*)&xv;
-      int q[8];
+    for (int rr = 0; rr < 2; ++rr) {
+      const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
+      const int8_t* src = a.qC + ((b * Lp + t0 + 16 * i + l16) * d.G + g_h) * (int64_t)NS + 16 * lg;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = q8((vLut[s8 + e] * Store<DT>::to_f(xe[e])) * invx_q);
-      *(uint2*)&qxs[b_off<LC>(p_q, s8)] = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
-      if (a.tap_qxs) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t t = t0 + s8 + e;
-          if (t < d.L) a.tap_qxs[((b * d.L + t) * H + h) * (int64_t)kP + p_q] = (int8_t)q[e];
-        }
-      }
+      for (int kn = 0; kn < KN; ++kn) qc2[rr][kn] = *(const v4i*)(src + 64 * kn);
     }
-    __syncthreads();
+    PF pf;
+    const bool more = k + 1 < d.c;
 
-    // ---- ChunkState^T for (p tile pt_own, n tiles ng*NTW ..) ----
-    uint32_t S8[NTW];
+    // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
+    uint32_t S8[PTW];
     {
-      v4i acc[NTW];
+      v4i acc[PTW];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[j] = v4i{0, 0, 0, 0};
-      const int8_t* qbt = a.qBT + ((b * d.c + k) * d.G + g_h) * (int64_t)NS * LC;
+      for (int j = 0; j < PTW; ++j) acc[j] = v4i{0, 0, 0, 0};
+      const int8_t* qbt = a.qBT + ((b * d.c + k) * d.G + g_h) * (int64_t)NS * LC +
+                          (int64_t)(16 * nt_own + l16) * LC;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int s0 = 64 * ks + 16 * lg;
-        const v4i bq = *(const v4i*)&qxs[b_off<LC>(p_own, s0)];
+        const v4i qa = *(const v4i*)(qbt + s0);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const int nt = ng * NTW + j;
-          const v4i qa = *(const v4i*)(qbt + (int64_t)(16 * nt + l16) * LC + s0);
+        for (int j = 0; j < PTW; ++j) {
+          const v4i bq = *(const v4i*)&qxl[qx_off<LC>(16 * (pt0 + j) + l16, s0)];
           acc[j] = mma_i8(qa, bq, acc[j]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int nt = ng * NTW + j;
+      for (int j = 0; j < PTW; ++j) {
+        const int p = 16 * (pt0 + j) + l16;
         if (a.tap_s32) {
-          const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p_own) * NS + 16 * nt + 4 * lg;
+          const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
           *(int4*)(a.tap_s32 + so) = make_int4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         }
         // requantise in registers (Key design 2)
-        S8[j] = pack4(q8((float)acc[j][0] * mreq), q8((float)acc[j][1] * mreq),
-                      q8((float)acc[j][2] * mreq), q8((float)acc[j][3] * mreq));
+        S8[j] = pack4(q8((float)acc[j][0] * mreq[j]), q8((float)acc[j][1] * mreq[j]),
+                      q8((float)acc[j][2] * mreq[j]), q8((float)acc[j][3] * mreq[j]));
       }
     }
-    __syncthreads();  // scratch free: it becomes the next chunk's Q(B) buffer
 
-    Prefetch<LC, NS> pf;
-    const bool more = k + 1 < d.c;
+    // next chunk: issued after ChunkState's loads (the load counter is in order)
     if (more) prefetch_load<DT, LC, NS>(a, b, h, g_h, k + 1, pf);
 
-    // ---- ChunkScan for row tiles {w, RT-1-w} (balanced under the causal mask) ----
-#pragma unroll 1
+    // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
+    // (outputs land as 4 consecutive p per lane for one position s)
+#pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      // l = 256: tiles w and 15 - w; l = 128: tile w only
+      // l = 256: tiles w and 15 - w (balanced under the causal mask); l = 128: tile w
       const int i = (rr == 0) ? w : 2 * kWaves - 1 - w;
       if (i >= RT) continue;
-      const int s_row = 16 * i + l16;
-      v4i qc[KN];
-      {
-        const int8_t* src = a.qC + ((b * Lp + t0 + s_row) * d.G + g_h) * (int64_t)NS + 16 * lg;
+      const int s_row = 16 * i + l16;   // this lane's position s (B-operand column)
+      v4i qcr[KN];  // (selected, not indexed, so qc2 stays in registers)
 #pragma unroll
-        for (int kn = 0; kn < KN; ++kn) qc[kn] = *(const v4i*)(src + 64 * kn);
-      }
+      for (int kn = 0; kn < KN; ++kn) qcr[kn] = rr ? qc2[1][kn] : qc2[0][kn];
       // V_i[s'] = s_C s_B exp(a_{16i} - a_s') dt_s' for s' < 16 i (this wave's table)
       const float a_ref = vA2[16 * i];
       for (int sp = lane; sp < 16 * i; sp += kWave) Vw[sp] = scBC * fast_exp2(a_ref - vA2[sp]) * vDt[sp];
@@ -415,15 +459,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-      v4f acc_off[4], acc_dg[4];
+      // one accumulator per p tile: off-diagonal tiles are summed unscaled, then
+      // multiplied by u_s; ChunkScan1 and the diagonal tile add on top
+      v4f acc[4];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        acc_off[pt] = v4f{0, 0, 0, 0};
-        acc_dg[pt] = v4f{0, 0, 0, 0};
-      }
-      // off-diagonal column tiles j < i in full pairs (jA, jA + 1); every LDS read
-      // of a pair is issued before its MFMAs
-#pragma unroll 2
+      for (int pt = 0; pt < 4; ++pt) acc[pt] = v4f{0, 0, 0, 0};
+      // off-diagonal column tiles j < i in full pairs (jA, jA + 1)
       for (int jA = 0; jA + 1 < i; jA += 2) {
         const int jB = jA + 1;
         v4i ba[KN], bb[KN];
@@ -434,149 +475,143 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
         }
         const float4 vA = *(const float4*)&Vw[16 * jA + 4 * lg];
         const float4 vB = *(const float4*)&Vw[16 * jB + 4 * lg];
-        uint2 xa[4], xb[4];
+        FragF<DT> xf[4];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          xa[pt] = *(const uint2*)&xT[xT_off<LC>(16 * pt + l16, 16 * jA + 4 * lg)];
-          xb[pt] = *(const uint2*)&xT[xT_off<LC>(16 * pt + l16, 16 * jB + 4 * lg)];
-        }
+        for (int pt = 0; pt < 4; ++pt) xf[pt] = frag16<DT>(&xT[xT_pair<LC>(16 * pt + l16, jA >> 1, lg)]);
         v4i cbA = v4i{0, 0, 0, 0}, cbB = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn) {
-          cbA = mma_i8(ba[kn], qc[kn], cbA);
-          cbB = mma_i8(bb[kn], qc[kn], cbB);
+          cbA = mma_i8(ba[kn], qcr[kn], cbA);
+          cbB = mma_i8(bb[kn], qcr[kn], cbB);
         }
-        FragF<DT> af;
-        af.set(0, (float)cbA[0] * vA.x);
-        af.set(1, (float)cbA[1] * vA.y);
-        af.set(2, (float)cbA[2] * vA.z);
-        af.set(3, (float)cbA[3] * vA.w);
-        af.set(4, (float)cbB[0] * vB.x);
-        af.set(5, (float)cbB[1] * vB.y);
-        af.set(6, (float)cbB[2] * vB.z);
-        af.set(7, (float)cbB[3] * vB.w);
+        FragF<DT> wf;
+        wf.set(0, (float)cbA[0] * vA.x);
+        wf.set(1, (float)cbA[1] * vA.y);
+        wf.set(2, (float)cbA[2] * vA.z);
+        wf.set(3, (float)cbA[3] * vA.w);
+        wf.set(4, (float)cbB[0] * vB.x);
+        wf.set(5, (float)cbB[1] * vB.y);
+        wf.set(6, (float)cbB[2] * vB.z);
+        wf.set(7, (float)cbB[3] * vB.w);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          acc_off[pt] = FragF<DT>::mma(af, frag_from_halves<DT>(xa[pt], xb[pt]), acc_off[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = FragF<DT>::mma(xf[pt], wf, acc[pt]);
       }
-      // diagonal tile j = i, sharing its MFMA with the leftover off-diagonal tile
-      // j = i - 1 when i is odd (that tile's weights carry u_s so it can join the
-      // unscaled diagonal accumulator: u_s V_i[s'] = exp(a_s - a_s') dt_s' s_C s_B)
+      // diagonal tile j = i (with D on its diagonal, so the skip term D x rides the
+      // MFMA). It shares its MFMA with the other tile of its pair (2m, 2m + 1),
+      // m = i / 2: for odd i that is the leftover off-diagonal tile i - 1, whose
+      // weights carry u_s so it can join the unscaled diagonal accumulator; for
+      // even i it is tile i + 1, above the diagonal, with zero weights.
+      const float a_s = vA2[s_row];
+      const float us = fast_exp2(a_s - a_ref);  // u at this lane's position
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[pt] *= us;
+      // ChunkScan1 (inter-chunk), transposed: H8 rows x Q(C) rows, scaled by
+      // exp(a_s) s_C s_S[p] and added to the output accumulator
+      if (k > 0) {
+        const float eo = fast_exp2(a_s) * sC;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          v4i acc1 = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int kn = 0; kn < KN; ++kn) {
+            const v4i hb = *(const v4i*)&H8l[b_off<NS>(16 * pt + l16, 64 * kn + 16 * lg)];
+            acc1 = mma_i8(hb, qcr[kn], acc1);
+          }
+          const float4 ss = *(const float4*)&SSl[16 * pt + 4 * lg];
+          acc[pt][0] = fmaf((float)acc1[0], eo * ss.x, acc[pt][0]);
+          acc[pt][1] = fmaf((float)acc1[1], eo * ss.y, acc[pt][1]);
+          acc[pt][2] = fmaf((float)acc1[2], eo * ss.z, acc[pt][2]);
+          acc[pt][3] = fmaf((float)acc1[3], eo * ss.w, acc[pt][3]);
+        }
+      }
       {
-        const bool odd = i & 1;
-        const int jL = i - 1;
+        const int hd = i & 1;            // half of the pair holding the diagonal tile
+        const int jL = i - 1;            // leftover tile (odd i only)
         v4i bd[KN], bl[KN];
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn) {
           bd[kn] = *(const v4i*)&qBl[b_off<NS>(16 * i + l16, 64 * kn + 16 * lg)];
-          if (odd) bl[kn] = *(const v4i*)&qBl[b_off<NS>(16 * jL + l16, 64 * kn + 16 * lg)];
+          if (hd) bl[kn] = *(const v4i*)&qBl[b_off<NS>(16 * jL + l16, 64 * kn + 16 * lg)];
         }
-        const float a_s = vA2[s_row];
         const float4 ad = *(const float4*)&vA2[16 * i + 4 * lg];
         const float4 dd = *(const float4*)&vDt[16 * i + 4 * lg];
         float4 vL = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (odd) vL = *(const float4*)&Vw[16 * jL + 4 * lg];
-        uint2 xd[4], xl[4];
+        if (hd) vL = *(const float4*)&Vw[16 * jL + 4 * lg];
+        FragF<DT> xf[4];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          xd[pt] = *(const uint2*)&xT[xT_off<LC>(16 * pt + l16, 16 * i + 4 * lg)];
-          xl[pt] = odd ? *(const uint2*)&xT[xT_off<LC>(16 * pt + l16, 16 * jL + 4 * lg)] : make_uint2(0, 0);
-        }
+        for (int pt = 0; pt < 4; ++pt) xf[pt] = frag16<DT>(&xT[xT_pair<LC>(16 * pt + l16, i >> 1, lg)]);
         v4i cbD = v4i{0, 0, 0, 0}, cbL = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn) {
-          cbD = mma_i8(bd[kn], qc[kn], cbD);
-          if (odd) cbL = mma_i8(bl[kn], qc[kn], cbL);
+          cbD = mma_i8(bd[kn], qcr[kn], cbD);
+          if (hd) cbL = mma_i8(bl[kn], qcr[kn], cbL);
         }
         const float adv[4] = {ad.x, ad.y, ad.z, ad.w};
         const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
-        const float us = fast_exp2(a_s - a_ref);  // u at this lane's row
         const float vLv[4] = {vL.x * us, vL.y * us, vL.z * us, vL.w * us};
-        FragF<DT> af;
+        float wd[4], wl[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int sp = 16 * i + 4 * lg + r;
-          const float wv = (sp <= s_row) ? (float)cbD[r] * scBC * fast_exp2(a_s - adv[r]) * ddv[r] : 0.f;
-          af.set(r, wv);
-          af.set(r + 4, (float)cbL[r] * vLv[r]);
+          float wv = (sp <= s_row) ? (float)cbD[r] * scBC * fast_exp2(a_s - adv[r]) * ddv[r] : 0.f;
+          if (sp == s_row) wv += Dh;
+          wd[r] = wv;
+          wl[r] = (float)cbL[r] * vLv[r];
         }
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          acc_dg[pt] = FragF<DT>::mma(af, frag_from_halves<DT>(xd[pt], xl[pt]), acc_dg[pt]);
-      }
-      // ChunkScan1 (inter-chunk)
-      v4i acc1[4];
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc1[pt] = v4i{0, 0, 0, 0};
-      if (k > 0) {
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-#pragma unroll
-          for (int kn = 0; kn < KN; ++kn) {
-            const v4i hb = *(const v4i*)&H8l[b_off<NS>(16 * pt + l16, 64 * kn + 16 * lg)];
-            acc1[pt] = mma_i8(qc[kn], hb, acc1[pt]);
-          }
-        }
-      }
-      // epilogue: rows s_out = 16 i + 4 lg + r, columns p = 16 pt + l16
-      const float4 ao = *(const float4*)&vA2[16 * i + 4 * lg];
-      const float aov[4] = {ao.x, ao.y, ao.z, ao.w};
-      float u[4], eo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u[r] = fast_exp2(aov[r] - a_ref);
-        eo[r] = fast_exp2(aov[r]) * sC;
-      }
-      const int64_t trow = t0 + 16 * i + 4 * lg;   // output row of r = 0
-      T* yrow = (T*)a.Y + ((b * d.L + trow) * H + h) * (int64_t)kP + l16;
-      const int ystride = H * kP;                   // elements between consecutive t
-      const int nrow = (int)min((int64_t)4, d.L - trow);
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const uint2 xr = *(const uint2*)&xT[xT_off<LC>(16 * pt + l16, 16 * i + 4 * lg)];
-        const T* xv = (const T*)&xr;
-        const float so = sS[pt];
+        FragF<DT> wf;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float y = fmaf(u[r], acc_off[pt][r], acc_dg[pt][r]);
-          y = fmaf(Dh, Store<DT>::to_f(xv[r]), y);
-          if (k > 0) y = fmaf((float)acc1[pt][r], eo[r] * so, y);
-          if (r < nrow) yrow[r * ystride + 16 * pt] = Store<DT>::from_f(y);
+          wf.set(r, hd ? wl[r] : wd[r]);
+          wf.set(r + 4, hd ? wd[r] : 0.f);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = FragF<DT>::mma(xf[pt], wf, acc[pt]);
+      }
+      // epilogue: lane holds s = s_row and p = 16 pt + 4 lg + r
+      const int64_t t = t0 + s_row;
+      T* yrow = (T*)a.Y + ((b * d.L + t) * H + h) * (int64_t)kP + 4 * lg;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const float y[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+        if (t < d.L) {
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[0])) |
+                              ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[1])) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[2])) |
+                              ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[3])) << 16);
+          *(uint2*)(yrow + 16 * pt) = make_uint2(lo, hi);
         }
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
     }
-
-    // next chunk into the other buffer (the scratch tile is free since the barrier above)
-    if (more) prefetch_store<LC, NS>(lds, cur ^ 1, pf);
-    __syncthreads();
+    __syncthreads();  // chunk k's tiles and H8l are no longer read
 
     // ---- StatePassing (Eq. 6) in registers; publish H8 for the next ChunkScan1 ----
-    {
-      const int qd = a.qdecay[(b * H + h) * d.c + k];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int nt = ng * NTW + j;
-        if (k == 0) {
-          H8[j] = S8[j];
-        } else {
-          int o[4];
+    for (int j = 0; j < PTW; ++j) {
+      const int p = 16 * (pt0 + j) + l16;
+      if (k == 0) {
+        H8[j] = S8[j];
+      } else {
+        int o[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = sat127(byte_s(S8[j], r) + rsh7_fast(qd * byte_s(H8[j], r)));
-          H8[j] = pack4(o[0], o[1], o[2], o[3]);
-        }
-        *(uint32_t*)&H8l[b_off<NS>(p_own, 16 * nt + 4 * lg)] = H8[j];
-        const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p_own) * NS + 16 * nt + 4 * lg;
-        if (a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = S8[j];
-        if (a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
+        for (int r = 0; r < 4; ++r) o[r] = sat127(byte_s(S8[j], r) + rsh7_fast(qd * byte_s(H8[j], r)));
+        H8[j] = pack4(o[0], o[1], o[2], o[3]);
       }
+      *(uint32_t*)&H8l[b_off<NS>(p, 16 * nt_own + 4 * lg)] = H8[j];
+      const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
+      if (a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = S8[j];
+      if (a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
+    }
+    if (more) {
+      prefetch_store<DT, LC, NS>(a, lds, b, h, k + 1, pf);
+      qd_word = pf.qd;
     }
   }
   if (a.final_state) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int nt = ng * NTW + j;
-      const int64_t fo = ((b * H + h) * (int64_t)kP + p_own) * NS + 16 * nt + 4 * lg;
+    for (int j = 0; j < PTW; ++j) {
+      const int p = 16 * (pt0 + j) + l16;
+      const int64_t fo = ((b * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
       *(uint32_t*)(a.final_state + fo) = H8[j];
     }
   }
