@@ -242,14 +242,15 @@ def rounding_shift(v, shift: int):
 def scale_pack(amax_B, amax_C, amax_Xs, amax_S, nheads: int, bits: int = 8) -> dict:
     """Static scale pack from calibration maxima (R1).
 
-    s = fp32(amax / q_max) (s = 1 when amax is 0); inv = fp32(1 / s);
+    s = fp32(amax / q_max) (s = 1 when amax is 0 or not finite); inv = fp32(1 / s);
     M_req[h,p] = fp32(s_X[h,p] * s_B[g(h)] / s_S[h,p]). Returns float32 arrays.
     """
     qm = float(qmax_of(bits))
 
     def step(a):
         a = np.asarray(a, np.float64)
-        return np.where(a > 0, a / qm, 1.0).astype(np.float32)
+        ok = (a > 0) & np.isfinite(a)
+        return np.where(ok, a / qm, 1.0).astype(np.float32)
 
     s_B, s_C, s_X, s_S = step(amax_B), step(amax_C), step(amax_Xs), step(amax_S)
     G = s_B.shape[0]

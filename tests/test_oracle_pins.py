@@ -244,6 +244,9 @@ def test_scale_pack_algebra():
     assert sc["M_req"][1, 0] == np.float32(m)
     for k in ("s_B", "s_C", "inv_B", "inv_C", "s_X", "inv_X", "s_S", "M_req"):
         assert sc[k].dtype == np.float32
+    # a non-finite maximum also gives a unit step, as in the library's host routine
+    sc2 = O.scale_pack(np.array([np.inf, np.nan]), amC, amX, amS, nheads=2)
+    assert sc2["s_B"][0] == 1.0 and sc2["s_B"][1] == 1.0 and sc2["inv_B"][0] == 1.0
 
 
 # PIN7: high-bit convergence of the INT8 method toward the float64 definition.
