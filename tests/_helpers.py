@@ -70,12 +70,33 @@ def f64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def chan_err(y, ref) -> float:
-    """max over channels (h, p) of max_{b,t} |y - ref| / RMS_{b,t}(ref)."""
+_MANT = {"fp32": 23, "fp16": 10, "bf16": 7}
+_EMIN = {"fp32": -126, "fp16": -14, "bf16": -126}
+
+
+def half_ulp(y, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of |y| in the storage type (the largest
+    error of one round-to-nearest into that type)."""
+    a = np.abs(np.asarray(y, np.float64))
+    e = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0))), _EMIN[dtype])
+    e = np.maximum(e, _EMIN[dtype])
+    return np.ldexp(0.5, (e - _MANT[dtype]).astype(np.int64))
+
+
+def chan_err(y, ref, dtype: str | None = None) -> float:
+    """max over channels (h, p) of max_{b,t} |y - ref| / RMS_{b,t}(ref).
+
+    With ``dtype`` (the type y is stored in), each element's final rounding
+    into that type is allowed for: the error counted is
+    max(|y - ref| - half_ulp(y), 0), which is at most the error of the
+    float32 value before that rounding."""
     y = np.asarray(y, np.float64)
     ref = np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref, axis=(0, 1)))
-    err = np.max(np.abs(y - ref), axis=(0, 1))
+    d = np.abs(y - ref)
+    if dtype is not None:
+        d = np.maximum(d - half_ulp(y, dtype), 0.0)
+    err = np.max(d, axis=(0, 1))
     return float(np.max(err / np.maximum(rms, 1e-30)))
 
 

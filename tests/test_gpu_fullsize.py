@@ -105,7 +105,7 @@ def test_full_size_int8(gpu_lib, wid):
         assert np.array_equal(taps["passed"][b, :, h].cpu().numpy(), r["passed"][0, :, 0]), (b, h)
         assert np.array_equal(fin[b, h].cpu().numpy(), r["passed"][0, -1, 0]), (b, h)
         yg = H.f64(y[b:b + 1, :, h:h + 1])
-        err = H.chan_err(yg, r["y"])
+        err = H.chan_err(yg, r["y"], w.dtype)
         assert err <= 5e-2, (b, h, err)
 
 
@@ -119,7 +119,7 @@ def test_full_size_float(gpu_lib, wid):
     for b, h in samples(w, consts):
         x, dt, Ah, Bm, Cm, Dh, _ = head_inputs(w, consts, ev, sc, b, h)
         yf, hf = O.chunked(x, dt, Ah, Bm, Cm, Dh, w.chunk)[:2]
-        err = H.chan_err(H.f64(y[b:b + 1, :, h:h + 1]), yf)
+        err = H.chan_err(H.f64(y[b:b + 1, :, h:h + 1]), yf, w.dtype)
         assert err <= 2e-2, (b, h, err)
         fg = fin[b, h].cpu().numpy().astype(np.float64)
         assert np.abs(fg - hf[0, 0]).max() <= 2e-1 * np.sqrt(np.mean(hf * hf)), (b, h)

@@ -136,7 +136,7 @@ def test_chunk_scan_int8(gpu_lib, name):
     L.ssd_chunk_scan(sh, L.SSD_PATH_INT8, d["x"], d["dt"], dAcs, _i8(torch, r8["qC"]), cb,
                      _i8(torch, r8["passed"]), d["D"], sc, y)
     torch.cuda.synchronize()
-    assert H.chan_err(H.f64(y), r8["y"]) <= 5e-2
+    assert H.chan_err(H.f64(y), r8["y"], c.w.dtype) <= 5e-2
 
 
 @pytest.mark.parametrize("name", CASE_NAMES)
@@ -179,7 +179,7 @@ def test_float_modules(gpu_lib, name):
     L.ssd_chunk_scan(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], dAcs, d["C"], cb,
                      _dev(Hs, np.float32), d["D"], None, y)
     torch.cuda.synchronize()
-    assert H.chan_err(H.f64(y), yf) <= 2e-2
+    assert H.chan_err(H.f64(y), yf, c.w.dtype) <= 2e-2
 
 
 def _modular_int8(L, torch, c, d, sh, sc):
@@ -224,7 +224,7 @@ def test_forward_int8(gpu_lib, name):
     assert np.array_equal(taps["s8_local"].cpu().numpy(), r8["s8"])
     assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
     assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
-    assert H.chan_err(H.f64(y), r8["y"]) <= 5e-2
+    assert H.chan_err(H.f64(y), r8["y"], c.w.dtype) <= 5e-2
     # determinism: a second run (without taps) is bitwise identical, final state too
     y2 = torch.empty_like(y)
     fin2 = torch.empty_like(fin)
@@ -248,7 +248,7 @@ def test_forward_float(gpu_lib, name):
     L.ssd_forward(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None, y,
                   final_state=fin)
     torch.cuda.synchronize()
-    assert H.chan_err(H.f64(y), yf) <= 2e-2
+    assert H.chan_err(H.f64(y), yf, c.w.dtype) <= 2e-2
     fg = fin.cpu().numpy().astype(np.float64)
     assert np.abs(fg - hf).max() <= 2e-2 * np.sqrt(np.mean(hf * hf)) * 10
 
