@@ -36,6 +36,46 @@ def algorithmic_bytes_per_token(w, int8: bool) -> int:
     return int(round(io + state))
 
 
+def io_bytes_per_token(w) -> int:
+    """X, dt, B, C read once and Y written once (no state exchange)."""
+    esz = {"fp32": 4, "fp16": 2, "bf16": 2}[w.dtype]
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    return esz * (2 * H * P + H + 2 * G * N)
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10) -> float:
+    """Device-to-device copy rate (bytes read + written per second, GB/s)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del a, b
+    return gbs
+
+
+def device_info(torch) -> dict:
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def kernel_source_hash() -> str:
     d = os.path.join(ROOT, "mamba_ssd_chunked_amd", "csrc")
     h = hashlib.sha256()
@@ -57,40 +97,51 @@ def measured_traffic(workload: str, path: str):
     return rec.get("bytes_per_call")
 
 
+CPU_SEQUENCES = 2   # sequences of the batch the CPU baseline runs (a bounded sample)
+
+
 def cpu_baseline(w, consts, ev) -> dict:
-    """The float64 recurrence oracle timed on host cores, on one sequence of the
-    batch (all heads, full length), split by heads over a process pool."""
+    """The float64 recurrence oracle timed on host cores, on the first
+    CPU_SEQUENCES sequences of the batch (all heads, full length), split by
+    (sequence, head block) over a process pool that is started before timing."""
     import concurrent.futures as cf
     import multiprocessing as mp
 
-    import numpy as np
-
     from mamba_ssd_chunked_amd import synth
 
-    x = synth.to_f64(ev["x"][:1], w.dtype)
-    dt = synth.to_f64(ev["dt"][:1], w.dtype)
-    B = synth.to_f64(ev["B"][:1], w.dtype)
-    C = synth.to_f64(ev["C"][:1], w.dtype)
+    nb = min(CPU_SEQUENCES, w.batch)
+    x = synth.to_f64(ev["x"][:nb], w.dtype)
+    dt = synth.to_f64(ev["dt"][:nb], w.dtype)
+    B = synth.to_f64(ev["B"][:nb], w.dtype)
+    C = synth.to_f64(ev["C"][:nb], w.dtype)
     ncpu = len(os.sched_getaffinity(0))
-    workers = max(1, min(16, ncpu, w.nheads))
-    per = -(-w.nheads // workers)
+    workers = max(1, min(16, ncpu))
     hpg = w.nheads // w.ngroups
+    nblk = max(1, -(-workers // nb))
+    per = -(-w.nheads // nblk)
     jobs = []
-    for h0 in range(0, w.nheads, per):
-        h1 = min(w.nheads, h0 + per)
-        g0, g1 = h0 // hpg, (h1 - 1) // hpg + 1
-        # a head block inside whole groups keeps the head -> group map
-        jobs.append((x[:, :, h0:h1], dt[:, :, h0:h1], consts["A"][h0:h1], B[:, :, g0:g1],
-                     C[:, :, g0:g1], consts["D"][h0:h1], h0, hpg, g0))
-    t0 = time.perf_counter()
+    for b in range(nb):
+        for h0 in range(0, w.nheads, per):
+            h1 = min(w.nheads, h0 + per)
+            g0, g1 = h0 // hpg, (h1 - 1) // hpg + 1
+            # a head block inside whole groups keeps the head -> group map
+            jobs.append((x[b:b + 1, :, h0:h1], dt[b:b + 1, :, h0:h1], consts["A"][h0:h1],
+                         B[b:b + 1, :, g0:g1], C[b:b + 1, :, g0:g1], consts["D"][h0:h1], h0, hpg, g0))
     with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_warm, range(workers)))          # workers started and imported
+        t0 = time.perf_counter()
         list(ex.map(_recurrence_job, jobs))
-    t1 = time.perf_counter()
-    tokens_per_s = w.seqlen / (t1 - t0)          # one sequence of L tokens, all heads
+        t1 = time.perf_counter()
+    tokens_per_s = nb * w.seqlen / (t1 - t0)
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"float64 recurrence on 1 of {w.batch} sequences (all {w.nheads} heads, "
-                      f"L={w.seqlen}); {t1 - t0:.1f} s wall on {workers} processes",
-            "seconds": t1 - t0}
+            "sample": f"float64 recurrence on {nb} of {w.batch} sequences (all {w.nheads} heads, "
+                      f"L={w.seqlen}); {t1 - t0:.2f} s wall on {workers} processes",
+            "seconds": t1 - t0, "cpu": cpu_model()}
+
+
+def _warm(_):
+    from oracle import ssd_oracle  # noqa: F401
+    return 0
 
 
 def _recurrence_job(job):
@@ -141,6 +192,7 @@ def main() -> int:
                                                 w.ngroups, w.chunk, w.dtype), cal_dev, A)
     y = torch.empty_like(dev["x"])
     tokens = w.batch * w.seqlen
+    copy_gbs = copy_bandwidth(torch)
     results = {}
     for path_name in args.paths.split(","):
         path = L.SSD_PATH_INT8 if path_name == "int8" else L.SSD_PATH_FLOAT
@@ -180,7 +232,9 @@ def main() -> int:
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                          "kernel": "ssd_forward (all kernels of one call)",
                          "algorithmic_bytes_per_call": bytes_per_call,
-                         "algorithmic_bytes_per_token": bpt},
+                         "algorithmic_bytes_per_token": bpt,
+                         "io_only_frac": io_bytes_per_token(w) * tokens / avg_call_s / 1e9 / HBM_PEAK_GBS,
+                         "frac_of_copy": achieved / copy_gbs},
         }
     head = results.get("int8") or next(iter(results.values()))
     out = {
@@ -202,6 +256,8 @@ def main() -> int:
         "roofline": head["roofline"],
         "paths": results,
         "kernel_source_hash": kernel_source_hash(),
+        "device": device_info(torch),
+        "copy_gbs": copy_gbs,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, consts, ev)
