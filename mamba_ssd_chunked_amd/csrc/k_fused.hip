@@ -1,15 +1,15 @@
 // Fused SSD forward on the persistent-INT8 path ("SSDi8" notes page, "Overall
 // framework" and "Key designs 1-3").
 //
-// Two prologue launches quantise B and C once per group (also writing Q(B)
-// transposed per chunk) and form the float64 in-chunk cumulative sums. The main
-// kernel runs one workgroup of eight waves per (batch, head). It walks that
-// head's chunks in order and keeps the INT8 state in registers, so the state
-// never travels through HBM. Per chunk:
+// A prologue launch quantises B and C once per group and a second forms the
+// float64 in-chunk cumulative sums. The main kernel runs one workgroup of eight
+// waves per (batch, head). It walks that head's chunks in order and keeps the
+// INT8 state in registers, so the state never travels through HBM. Per chunk:
 //
 //   Q(Xs)        X_scaled = LUT_state * x quantised once per (s, p) into LDS;
 //   ChunkState   S32^T[n,p] = sum_s Q(B)^T[n,s] Q(Xs)[s,p]   (int8 MFMA; wave w
-//                owns p-tile w%4 and half of the n tiles), requantised in
+//                owns one n tile and its p tiles; Q(B)^T comes from the Q(B)
+//                rows in LDS through transposing reads), requantised in
 //                registers to S8;
 //   ChunkScan1   Y_off[s,p] = sum_n Q(C)[s,n] H8_{k-1}[p,n]  (int8 MFMA, H8 in LDS);
 //   ChunkBMM     CB^T tiles = Q(B) rows x Q(C) rows          (int8 MFMA; the output
@@ -17,15 +17,17 @@
 //   ChunkScan2   Y_diag = W x, W = CB s_C s_B exp(a_s - a_s') dt_s'  (fp16/bf16 MFMA);
 //   StatePassing H8_k = sat(S8_k + RSH7(Q(Decay_k) H8_{k-1}))  (Eq. 6, in registers).
 //
-// The next chunk's x and Q(B) tiles are loaded into registers while the current
-// chunk computes and then written to the second half of a double-buffered LDS
-// area, so HBM latency overlaps the MFMA/VALU work.
+// While chunk k computes, chunk k+1's Q(B) rows are copied from memory straight
+// into the second of two LDS buffers, and its x tile and per-position vectors
+// are loaded into registers and written to LDS after the chunk, so HBM latency
+// overlaps the MFMA/VALU work.
 //
 // ChunkScan2 factorisation (exact algebra): for a column tile j strictly below
 // row tile i, exp(a_s - a_s') = u_s * V_i[s'] with u_s = exp(a_s - a_{16i}) <= 1
 // and V_i[s'] = exp(a_{16i} - a_s') <= 1, so each row tile needs one table V_i
 // and one factor per output row instead of an exponential per element.
-// Diagonal tiles use exp(a_s - a_s') directly and accumulate separately.
+// Off-diagonal tiles accumulate unscaled and are multiplied by u_s once; the
+// diagonal tile uses exp(a_s - a_s') directly.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -92,7 +94,7 @@ __device__ __forceinline__ FragF<DT> frag16(const u16* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Prologue: Q(B), Q(C) with padded rows (t >= L -> 0) and Q(B)^T per chunk.
+// Prologue: Q(B), Q(C) with padded rows (t >= L -> 0), once per group.
 // grid (c * l/64, B*G), 256 threads; one 64-row x N tile per block.
 // ---------------------------------------------------------------------------
 template <int DT>
@@ -101,11 +103,8 @@ __global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restr
                                                      const float* __restrict__ inv_B,
                                                      const float* __restrict__ inv_C,
                                                      int8_t* __restrict__ qB,
-                                                     int8_t* __restrict__ qC,
-                                                     int8_t* __restrict__ qBT) {
-  constexpr int RB = 64;                 // rows per block
-  constexpr int PT = RB + 4;             // LDS pitch of the transposed tile
-  __shared__ __attribute__((aligned(16))) int8_t tT[128 * PT];  // [n][s]
+                                                     int8_t* __restrict__ qC) {
+  constexpr int RB = 64;  // rows per block
   const int nsb = d.l / RB;
   const int k = blockIdx.x / nsb, sb = blockIdx.x % nsb;
   const int64_t bg = blockIdx.y;
@@ -135,16 +134,6 @@ __global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restr
     const int64_t dst = ((b * Lp + t) * d.G + g) * (int64_t)N + n0;
     *(uint2*)(qB + dst) = make_uint2(pack4(qb[0], qb[1], qb[2], qb[3]), pack4(qb[4], qb[5], qb[6], qb[7]));
     *(uint2*)(qC + dst) = make_uint2(pack4(qc[0], qc[1], qc[2], qc[3]), pack4(qc[4], qc[5], qc[6], qc[7]));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tT[(n0 + j) * PT + sl] = (int8_t)qb[j];
-  }
-  __syncthreads();
-  // Q(B)^T rows [b][k][g][n][s]: 16 bytes per lane
-  int8_t* dstT = qBT + ((b * d.c + k) * d.G + g) * (int64_t)N * l + RB * sb;
-  for (int item = threadIdx.x; item < N * (RB / 16); item += 256) {
-    const int n = item / (RB / 16), s0 = (item % (RB / 16)) * 16;
-    const uint32_t* src = (const uint32_t*)&tT[n * PT + s0];
-    *(uint4*)(dstT + (int64_t)n * l + s0) = make_uint4(src[0], src[1], src[2], src[3]);
   }
 }
 
@@ -156,7 +145,6 @@ struct FusedArgs {
   const void* X;
   const void* dt;
   const int8_t* qB;
-  const int8_t* qBT;
   const int8_t* qC;
   const float* dAcs;
   const float* lut;
@@ -174,7 +162,7 @@ struct FusedArgs {
 template <int LC, int NS>
 struct Lds {
   static constexpr int XT = kP * LC * 2;  // x^T [p][s], 2-byte elements
-  static constexpr int QB = LC * NS;      // Q(B) rows [s][n]
+  static constexpr int QB = LC * NS;      // Q(B) rows [s][n], two buffers
   static constexpr int QX = kP * LC;      // Q(X_scaled)^T [p][s]
   static constexpr int H8 = kP * NS;      // passed state [p][n]
   static constexpr int VEC = 2 * LC * 4;  // a*log2(e), dt
@@ -182,7 +170,7 @@ struct Lds {
   static constexpr int SS = 2 * kP * 4;   // s_S[h, p], inv_X[h, p]
   static constexpr int off_xt = 0;
   static constexpr int off_qb = off_xt + XT;
-  static constexpr int off_qx = off_qb + QB;
+  static constexpr int off_qx = off_qb + 2 * QB;
   static constexpr int off_h8 = off_qx + QX;
   static constexpr int off_vec = off_h8 + H8;
   static constexpr int off_vw = off_vec + VEC;
@@ -196,7 +184,8 @@ __device__ __forceinline__ int qx_off(int p, int s) {
   return p * LC + 16 * ((s >> 4) ^ xsw(p)) + (s & 15);
 }
 
-// Registers holding the next chunk while the current one computes. Thread
+// Registers holding the next chunk's x and per-position vectors while the
+// current chunk computes (Q(B) rows go straight to LDS, see dma_qb). Thread
 // (q = tid / 8, c8 = tid % 8) owns x rows 4q .. 4q+3 at p = 8 c8 .. 8 c8 + 7.
 // Every load is unconditional (addresses are clamped into the tensor and
 // out-of-range rows are zeroed when stored to LDS), so no branch forces the
@@ -204,11 +193,9 @@ __device__ __forceinline__ int qx_off(int p, int s) {
 template <int LC, int NS>
 struct Prefetch {
   static constexpr int XI = (LC / 4) * (kP / 8);
-  static constexpr int QPT = LC * NS / 16 / kThreads;
-  static_assert(XI <= kThreads && QPT >= 1, "tile split");
+  static_assert(XI <= kThreads, "tile split");
   uint4 x[4];
   float4 lut;
-  uint4 q[QPT];
   float va;     // dAcs (scaled by log2(e) when stored)
   uint32_t vd;  // dt bits in the input type (converted when stored)
   uint32_t qd;  // the dword holding Q(Decay) of the chunk
@@ -222,7 +209,6 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
   const Dims& d = a.d;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)k * LC;
-  const int64_t Lp = (int64_t)d.c * LC;
   const int64_t cs0 = ((b * d.H + h) * d.c + k) * (int64_t)LC;
   {
     const int it = tid % PF::XI;
@@ -234,13 +220,6 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
       pf.x[r] = *(const uint4*)(xb + t * d.H * kP);
     }
     pf.lut = *(const float4*)(a.lut + cs0 + 4 * q);
-  }
-  const int8_t* src = a.qB + ((b * Lp + t0) * d.G + g_h) * (int64_t)NS;
-#pragma unroll
-  for (int m = 0; m < PF::QPT; ++m) {
-    const int id = tid + m * kThreads;
-    const int s = id / (NS / 16), c16 = id % (NS / 16);
-    pf.q[m] = *(const uint4*)(src + (int64_t)s * d.G * NS + 16 * c16);
   }
   {
     const int sv = tid % LC;
@@ -255,9 +234,43 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
   pf.qd = *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
 }
 
+// Q(B) rows of chunk k, copied from memory straight into LDS buffer k & 1 (no
+// registers): each wave copy moves 1 KB, lane L filling bytes 16 L .. 16 L + 15
+// of it, so the source address of each lane is chosen to produce the swizzled
+// b_off layout.
+template <int LC, int NS>
+__device__ __forceinline__ void dma_qb(const FusedArgs& a, char* lds, int64_t b, int g_h, int k, int w) {
+  constexpr int OPS = LC * NS / 1024;
+  constexpr int PER = OPS / kWaves;
+  constexpr int nch = NS / 16;
+  static_assert(OPS % kWaves == 0 && PER >= 1, "copy split");
+  const Dims& d = a.d;
+  const int lane = lane_id();
+  const int64_t row0 = b * (int64_t)d.c * LC + (int64_t)k * LC;
+  char* dst = lds + Lds<LC, NS>::off_qb + (k & 1) * Lds<LC, NS>::QB;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int gi = w * PER + m;
+    const int byte = 1024 * gi + 16 * lane;
+    const int r = byte / NS, pc = (byte % NS) / 16;
+    const int c16 = pc ^ (r & (nch - 1) & 7);
+    const int8_t* src = a.qB + ((row0 + r) * d.G + g_h) * (int64_t)NS + 16 * c16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + 1024 * gi),
+                                     16, 0, 0);
+  }
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+// Transposing LDS read (8-bit elements): the 16 lanes of a group each point at
+// 8 bytes; lanes 2r and 2r + 1 form row r (16 bytes) of an 8 x 16 byte matrix,
+// and lane i receives column i, i.e. byte i of every row.
+__device__ __forceinline__ v2i lds_tr8(const int8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(int8_t*)p);
+}
+
 // Writes the prefetched chunk into LDS: x transposed, Q(X_scaled) =
 // sat(RHAZ(fl32(fl32(lut * x) * inv_X))) transposed (the quantiser of "Key
-// design 1"), Q(B) rows and the per-position vectors.
+// design 1") and the per-position vectors.
 template <int DT, int LC, int NS>
 __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, int64_t b, int h, int k,
                                                const Prefetch<LC, NS>& pf) {
@@ -314,13 +327,6 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
       }
     }
   }
-  int8_t* qb = (int8_t*)(lds + LY::off_qb);
-#pragma unroll
-  for (int m = 0; m < PF::QPT; ++m) {
-    const int id = tid + m * kThreads;
-    const int s = id / (NS / 16), c16 = id % (NS / 16);
-    *(uint4*)&qb[b_off<NS>(s, 16 * c16)] = pf.q[m];
-  }
   if (tid < LC) {
     float* vec = (float*)(lds + LY::off_vec);
     vec[tid] = pf.va * kLog2e;
@@ -346,7 +352,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const u16* xT = (const u16*)(lds + LY::off_xt);
-  const int8_t* qBl = (const int8_t*)(lds + LY::off_qb);
   const int8_t* qxl = (const int8_t*)(lds + LY::off_qx);
   int8_t* H8l = (int8_t*)(lds + LY::off_h8);
   const float* vA2 = (const float*)(lds + LY::off_vec);
@@ -354,9 +359,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   float* SSl = (float*)(lds + LY::off_ss);
 
   const Dims& d = a.d;
-  const int h = blockIdx.x % d.H;
-  const int64_t b = blockIdx.x / d.H;
-  const int g_h = h / d.hpg;
+  // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8). When
+  // the (batch, group) units divide evenly, every XCD gets whole units, so the
+  // int8 Q(B)/Q(C) rows its heads share stay in that XCD's L2.
+  int64_t unit, hl;
+  {
+    const int64_t nunits = d.B * d.G;
+    if (nunits % 8 == 0) {
+      const int64_t j = blockIdx.x / 8;
+      unit = (blockIdx.x % 8) + 8 * (j / d.hpg);
+      hl = j % d.hpg;
+    } else {
+      unit = blockIdx.x / d.hpg;
+      hl = blockIdx.x % d.hpg;
+    }
+  }
+  const int64_t b = unit / d.G;
+  const int g_h = (int)(unit % d.G);
+  const int h = g_h * d.hpg + (int)hl;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int l16 = lane & 15, lg = lane >> 4;
   const int64_t Lp = (int64_t)d.c * LC;
@@ -386,6 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   uint32_t qd_word;  // dword holding Q(Decay) of the current chunk
   {  // chunk 0
     PF pf;
+    dma_qb<LC, NS>(a, lds, b, g_h, 0, w);
     prefetch_load<DT, LC, NS>(a, b, h, g_h, 0, pf);
     prefetch_store<DT, LC, NS>(a, lds, b, h, 0, pf);
     qd_word = pf.qd;
@@ -393,6 +414,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 
   for (int k = 0; k < d.c; ++k) {
     const int64_t t0 = (int64_t)k * LC;
+    const int8_t* qBl = (const int8_t*)(lds + LY::off_qb + (k & 1) * LY::QB);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies have landed
     __syncthreads();  // chunk k staged; H8l holds H_{k-1}
     const int qd = (int)((qd_word >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
     // Q(C) rows of this wave's row tiles (B operand over N), issued first
@@ -413,12 +436,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       v4i acc[PTW];
 #pragma unroll
       for (int j = 0; j < PTW; ++j) acc[j] = v4i{0, 0, 0, 0};
-      const int8_t* qbt = a.qBT + ((b * d.c + k) * d.G + g_h) * (int64_t)NS * LC +
-                          (int64_t)(16 * nt_own + l16) * LC;
+      // A operand Q(B)^T[n, s] straight from the Q(B) rows with two transposing
+      // reads: lane (lg, l16) gets n = 16 nt_own + l16 and s = s0 .. s0 + 15
+      const int cB = 16 * nt_own + 8 * (l16 & 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int s0 = 64 * ks + 16 * lg;
-        const v4i qa = *(const v4i*)(qbt + s0);
+        const v2i lo = lds_tr8(qBl + b_off<NS>(s0 + (l16 >> 1), cB));
+        const v2i hi = lds_tr8(qBl + b_off<NS>(s0 + 8 + (l16 >> 1), cB));
+        const v4i qa = v4i{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int j = 0; j < PTW; ++j) {
           const v4i bq = *(const v4i*)&qxl[qx_off<LC>(16 * (pt0 + j) + l16, s0)];
@@ -438,8 +464,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       }
     }
 
-    // next chunk: issued after ChunkState's loads (the load counter is in order)
-    if (more) prefetch_load<DT, LC, NS>(a, b, h, g_h, k + 1, pf);
+    // next chunk: Q(B) rows into the other LDS buffer, x and vectors into registers
+    if (more) {
+      dma_qb<LC, NS>(a, lds, b, g_h, k + 1, w);
+      prefetch_load<DT, LC, NS>(a, b, h, g_h, k + 1, pf);
+    }
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
     // (outputs land as 4 consecutive p per lane for one position s)
@@ -649,7 +678,7 @@ size_t fused_workspace_bytes(const Dims& d, bool) {
   const size_t qbc = (size_t)d.B * Lp * d.G * d.N;
   const size_t cs = (size_t)d.B * d.H * d.c * d.l * sizeof(float);
   const size_t qd = (size_t)d.B * d.H * d.c;
-  return 3 * al(qbc) + 2 * al(cs) + al(qd);
+  return 2 * al(qbc) + 2 * al(cs) + al(qd);
 }
 
 hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void* X,
@@ -666,8 +695,6 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
   w += al(qbc);
   int8_t* qC = (int8_t*)w;
   w += al(qbc);
-  int8_t* qBT = (int8_t*)w;
-  w += al(qbc);
   float* dAcs = (float*)w;
   w += al(cs);
   float* lut = (float*)w;
@@ -676,15 +703,15 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
 
   const dim3 pgrid((unsigned)(d.c * (d.l / 64)), (unsigned)(d.B * d.G));
   if (dtype == DT_F16)
-    hipLaunchKernelGGL(k_prologue_bc<DT_F16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC, qBT);
+    hipLaunchKernelGGL(k_prologue_bc<DT_F16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC);
   else
-    hipLaunchKernelGGL(k_prologue_bc<DT_BF16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC, qBT);
+    hipLaunchKernelGGL(k_prologue_bc<DT_BF16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, qd, st);
   if (e != hipSuccess) return e;
 
-  const FusedArgs fa{d, X, dt, qB, qBT, qC, dAcs, lut, qd, D, sc, Y, (int8_t*)final_state,
+  const FusedArgs fa{d, X, dt, qB, qC, dAcs, lut, qd, D, sc, Y, (int8_t*)final_state,
                      tap_qxs, tap_s32, tap_s8, tap_passed};
   if (dtype == DT_F16) {
     if (d.l == 256 && d.N == 128) return launch_main<DT_F16, 256, 128>(fa, st);
