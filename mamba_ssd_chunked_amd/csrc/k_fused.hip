@@ -167,7 +167,7 @@ struct Lds {
   static constexpr int H8 = kP * NS;      // passed state [p][n]
   static constexpr int VEC = 2 * LC * 4;  // a*log2(e), dt
   static constexpr int VW = kWaves * LC * 4;
-  static constexpr int SS = 2 * kP * 4;   // s_S[h, p], inv_X[h, p]
+  static constexpr int SS = 3 * kP * 4;   // s_S[h, p], inv_X[h, p], M_req[h, p]
   static constexpr int off_xt = 0;
   static constexpr int off_qb = off_xt + XT;
   static constexpr int off_qx = off_qb + 2 * QB;
@@ -203,11 +203,10 @@ struct Prefetch {
 
 template <int DT, int LC, int NS>
 __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int h, int g_h, int k,
-                                              Prefetch<LC, NS>& pf) {
+                                              int tid, Prefetch<LC, NS>& pf) {
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS> PF;
   const Dims& d = a.d;
-  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)k * LC;
   const int64_t cs0 = ((b * d.H + h) * d.c + k) * (int64_t)LC;
   {
@@ -239,13 +238,13 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
 // of it, so the source address of each lane is chosen to produce the swizzled
 // b_off layout.
 template <int LC, int NS>
-__device__ __forceinline__ void dma_qb(const FusedArgs& a, char* lds, int64_t b, int g_h, int k, int w) {
+__device__ __forceinline__ void dma_qb(const FusedArgs& a, char* lds, int64_t b, int g_h, int k, int w,
+                                       int lane) {
   constexpr int OPS = LC * NS / 1024;
   constexpr int PER = OPS / kWaves;
   constexpr int nch = NS / 16;
   static_assert(OPS % kWaves == 0 && PER >= 1, "copy split");
   const Dims& d = a.d;
-  const int lane = lane_id();
   const int64_t row0 = b * (int64_t)d.c * LC + (int64_t)k * LC;
   char* dst = lds + Lds<LC, NS>::off_qb + (k & 1) * Lds<LC, NS>::QB;
 #pragma unroll
@@ -273,11 +272,10 @@ __device__ __forceinline__ v2i lds_tr8(const int8_t* p) {
 // design 1") and the per-position vectors.
 template <int DT, int LC, int NS>
 __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, int64_t b, int h, int k,
-                                               const Prefetch<LC, NS>& pf) {
+                                               int tid, const Prefetch<LC, NS>& pf) {
   typedef typename Store<DT>::T T;
   typedef Lds<LC, NS> LY;
   typedef Prefetch<LC, NS> PF;
-  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)k * LC;
   if (tid < PF::XI) {
     const int q = tid >> 3, c8 = tid & 7;
@@ -377,8 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   const int64_t b = unit / d.G;
   const int g_h = (int)(unit % d.G);
   const int h = g_h * d.hpg + (int)hl;
-  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int w = wave_id();
   const int64_t Lp = (int64_t)d.c * LC;
   const int H = d.H;
 
@@ -386,33 +383,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   // (each Q(B)^T row is read by exactly one wave)
   const int nt_own = w % NT;
   const int pt0 = (w / NT) * PTW;
-  float mreq[PTW];
-#pragma unroll
-  for (int j = 0; j < PTW; ++j) mreq[j] = a.sc.M_req[h * kP + 16 * (pt0 + j) + l16];
   const float scBC = a.sc.s_C[g_h] * a.sc.s_B[g_h];
   const float sC = a.sc.s_C[g_h];
   const float Dh = a.D[h];
-  if (tid < kP) {
-    SSl[tid] = a.sc.s_S[h * kP + tid];
-    SSl[kP + tid] = a.sc.inv_X[h * kP + tid];
+  const int tid0 = threadIdx.x;
+  if (tid0 < kP) {
+    SSl[tid0] = a.sc.s_S[h * kP + tid0];
+    SSl[kP + tid0] = a.sc.inv_X[h * kP + tid0];
+    SSl[2 * kP + tid0] = a.sc.M_req[h * kP + tid0];
   }
   __syncthreads();
   float* Vw = (float*)(lds + LY::off_vw) + w * LC;
 
-  uint32_t H8[PTW];  // passed state: lane (p = 16 (pt0 + j) + l16, n = 16 nt_own + 4 lg + r)
+  uint32_t H8[PTW];  // passed state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
 #pragma unroll
   for (int j = 0; j < PTW; ++j) H8[j] = 0;
 
   uint32_t qd_word;  // dword holding Q(Decay) of the current chunk
   {  // chunk 0
     PF pf;
-    dma_qb<LC, NS>(a, lds, b, g_h, 0, w);
-    prefetch_load<DT, LC, NS>(a, b, h, g_h, 0, pf);
-    prefetch_store<DT, LC, NS>(a, lds, b, h, 0, pf);
+    dma_qb<LC, NS>(a, lds, b, g_h, 0, w, tid0 & (kWave - 1));
+    prefetch_load<DT, LC, NS>(a, b, h, g_h, 0, tid0, pf);
+    prefetch_store<DT, LC, NS>(a, lds, b, h, 0, tid0, pf);
     qd_word = pf.qd;
   }
 
   for (int k = 0; k < d.c; ++k) {
+    // Lane indices re-derived from an opaque copy every chunk: the swizzled LDS
+    // offsets built from them are then recomputed (a few VALU operations)
+    // instead of being hoisted out of the loop and spilled.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int l16 = lane & 15, lg = lane >> 4;
     const int64_t t0 = (int64_t)k * LC;
     const int8_t* qBl = (const int8_t*)(lds + LY::off_qb + (k & 1) * LY::QB);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies have landed
@@ -459,15 +462,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
           *(int4*)(a.tap_s32 + so) = make_int4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         }
         // requantise in registers (Key design 2)
-        S8[j] = pack4(q8((float)acc[j][0] * mreq[j]), q8((float)acc[j][1] * mreq[j]),
-                      q8((float)acc[j][2] * mreq[j]), q8((float)acc[j][3] * mreq[j]));
+        const float mreq = SSl[2 * kP + p];
+        S8[j] = pack4(q8((float)acc[j][0] * mreq), q8((float)acc[j][1] * mreq),
+                      q8((float)acc[j][2] * mreq), q8((float)acc[j][3] * mreq));
       }
     }
 
     // next chunk: Q(B) rows into the other LDS buffer, x and vectors into registers
     if (more) {
-      dma_qb<LC, NS>(a, lds, b, g_h, k + 1, w);
-      prefetch_load<DT, LC, NS>(a, b, h, g_h, k + 1, pf);
+      dma_qb<LC, NS>(a, lds, b, g_h, k + 1, w, lane);
+      prefetch_load<DT, LC, NS>(a, b, h, g_h, k + 1, tid, pf);
     }
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
@@ -632,11 +636,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       if (a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
     if (more) {
-      prefetch_store<DT, LC, NS>(a, lds, b, h, k + 1, pf);
+      prefetch_store<DT, LC, NS>(a, lds, b, h, k + 1, tid, pf);
       qd_word = pf.qd;
     }
   }
   if (a.final_state) {
+    const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       const int p = 16 * (pt0 + j) + l16;

@@ -79,9 +79,17 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const void* __restrict__ d
     const int j = threadIdx.x;
     const double Ah = (double)A[h0 + j];
     double a = 0.0;
-    for (int s = 0; s < l; ++s) {
-      a += (double)sdt[j][s] * Ah;  // the product is exact in float64
-      sa[j][s] = a;
+    // sequence order is kept; the LDS reads of each block of 16 steps are issued
+    // together so only the float64 additions form the dependent chain
+    for (int s0 = 0; s0 < l; s0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = sdt[j][s0 + u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        a += (double)v[u] * Ah;  // the product is exact in float64
+        sa[j][s0 + u] = a;
+      }
     }
   }
   __syncthreads();
