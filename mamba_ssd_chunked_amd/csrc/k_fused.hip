@@ -42,9 +42,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Saturating int8 quantiser with round half away from zero. After the clamp,
 // trunc(c + copysign(0.5 - 2^-25, c)) equals RHAZ(c) for every float32 c
 // (checked exhaustively over all 2^32 bit patterns in the test-suite).
-__device__ __forceinline__ int q8(float v) {
+__device__ __forceinline__ float q8_pre(float v) {
   const float c = fminf(fmaxf(v, -127.f), 127.f);
-  return (int)(c + __builtin_copysignf(0.49999997f, c));
+  return c + __builtin_copysignf(0.49999997f, c);
+}
+__device__ __forceinline__ int q8(float v) { return (int)q8_pre(v); }
+
+// Four such codes packed into one dword (byte j from v_j). The float -> int
+// conversion writes its low byte straight into the destination byte (SDWA
+// dst_sel), so the packing costs no extra instructions.
+__device__ __forceinline__ uint32_t q8x4(float v0, float v1, float v2, float v3) {
+  uint32_t d = (uint32_t)q8(v0);
+  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+      : "+v"(d) : "v"(q8_pre(v1)));
+  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+      : "+v"(d) : "v"(q8_pre(v2)));
+  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+      : "+v"(d) : "v"(q8_pre(v3)));
+  return d;
 }
 
 // Eq. 6 rounding shift sign(v) * ((|v| + 64) >> 7) in arithmetic-shift form:
@@ -207,27 +222,33 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS> PF;
   const Dims& d = a.d;
-  const int64_t t0 = (int64_t)k * LC;
+  // wave-uniform 64-bit bases, per-lane 32-bit offsets (one sequence of x is
+  // below 2 GB, checked by fused_supported)
+  const int t0 = k * LC;
+  const int Lm1 = (int)d.L - 1;
   const int64_t cs0 = ((b * d.H + h) * d.c + k) * (int64_t)LC;
+  const float* lutb = a.lut + cs0;
+  const float* dab = a.dAcs + cs0;
   {
     const int it = tid % PF::XI;
     const int q = it >> 3, c8 = it & 7;
-    const T* xb = (const T*)a.X + (b * d.L * d.H + h) * (int64_t)kP + 8 * c8;
+    const T* xb = (const T*)a.X + (b * d.L * d.H + h) * (int64_t)kP;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t t = min(t0 + 4 * q + r, d.L - 1);
-      pf.x[r] = *(const uint4*)(xb + t * d.H * kP);
+      const int t = min(t0 + 4 * q + r, Lm1);
+      pf.x[r] = *(const uint4*)((const char*)xb + (uint32_t)((t * d.H * kP + 8 * c8) * (int)sizeof(T)));
     }
-    pf.lut = *(const float4*)(a.lut + cs0 + 4 * q);
+    pf.lut = *(const float4*)(lutb + (uint32_t)(4 * q));
   }
   {
     const int sv = tid % LC;
-    pf.va = a.dAcs[cs0 + sv];
-    const int64_t t = min(t0 + sv, d.L - 1);
+    pf.va = dab[(uint32_t)sv];
+    const uint32_t t = (uint32_t)min(t0 + sv, Lm1);
+    const int64_t db = b * d.L * d.H + h;
     if constexpr (sizeof(T) == 4)
-      pf.vd = ((const uint32_t*)a.dt)[(b * d.L + t) * d.H + h];
+      pf.vd = ((const uint32_t*)a.dt + db)[t * (uint32_t)d.H];
     else
-      pf.vd = ((const u16*)a.dt)[(b * d.L + t) * d.H + h];
+      pf.vd = ((const u16*)a.dt + db)[t * (uint32_t)d.H];
   }
   const int64_t qi = (b * d.H + h) * d.c + k;
   pf.qd = *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
@@ -245,7 +266,7 @@ __device__ __forceinline__ void dma_qb(const FusedArgs& a, char* lds, int64_t b,
   constexpr int nch = NS / 16;
   static_assert(OPS % kWaves == 0 && PER >= 1, "copy split");
   const Dims& d = a.d;
-  const int64_t row0 = b * (int64_t)d.c * LC + (int64_t)k * LC;
+  const int8_t* qb = a.qB + ((b * (int64_t)d.c * LC + (int64_t)k * LC) * d.G + g_h) * (int64_t)NS;
   char* dst = lds + Lds<LC, NS>::off_qb + (k & 1) * Lds<LC, NS>::QB;
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
@@ -253,7 +274,7 @@ __device__ __forceinline__ void dma_qb(const FusedArgs& a, char* lds, int64_t b,
     const int byte = 1024 * gi + 16 * lane;
     const int r = byte / NS, pc = (byte % NS) / 16;
     const int c16 = pc ^ (r & (nch - 1) & 7);
-    const int8_t* src = a.qB + ((row0 + r) * d.G + g_h) * (int64_t)NS + 16 * c16;
+    const int8_t* src = qb + (uint32_t)(r * d.G * NS + 16 * c16);
     __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + 1024 * gi),
                                      16, 0, 0);
   }
@@ -276,18 +297,23 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
   typedef typename Store<DT>::T T;
   typedef Lds<LC, NS> LY;
   typedef Prefetch<LC, NS> PF;
-  const int64_t t0 = (int64_t)k * LC;
+  const int t0 = k * LC;
   if (tid < PF::XI) {
     const int q = tid >> 3, c8 = tid & 7;
     u16* xT = (u16*)(lds + LY::off_xt);
     int8_t* qx = (int8_t*)(lds + LY::off_qx);
-    uint4 xr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) xr[r] = (t0 + 4 * q + r < a.d.L) ? pf.x[r] : make_uint4(0, 0, 0, 0);
+    // Rows past L (ragged last chunk) hold copies of row L-1 (finite values):
+    // their LUT_state is 0, so their Q(X_scaled) is 0, and ChunkScan2 never
+    // pairs them with a valid output row (causal mask) and gives them weight 0.
+    const uint4* xr = pf.x;
     const uint32_t* w0 = (const uint32_t*)&xr[0];
     const uint32_t* w1 = (const uint32_t*)&xr[1];
     const uint32_t* w2 = (const uint32_t*)&xr[2];
     const uint32_t* w3 = (const uint32_t*)&xr[3];
+    // x^T: for p = 8 c8 + e' the row swizzle xsw(p) is e' ^ c8, and s = 4q sits in
+    // 16-byte chunk (4 (q >> 3) + (q & 3)) ^ xsw(p), half (q >> 2) & 1 of it
+    char* xTb = lds + LY::off_xt + 16 * LC * c8 + 8 * ((q >> 2) & 1);
+    const int mgc = (4 * (q >> 3) + (q & 3)) ^ c8;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // dword e of each row holds p = 8 c8 + 2e (low half) and 2e + 1 (high half)
@@ -295,33 +321,43 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
       const uint32_t lo23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
       const uint32_t hi01 = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
       const uint32_t hi23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
-      const int p0 = 8 * c8 + 2 * e;
-      *(uint2*)&xT[xT_off<LC>(p0, 4 * q)] = make_uint2(lo01, lo23);
-      *(uint2*)&xT[xT_off<LC>(p0 + 1, 4 * q)] = make_uint2(hi01, hi23);
+      *(uint2*)(xTb + (2 * e) * 2 * LC + 16 * (mgc ^ (2 * e))) = make_uint2(lo01, lo23);
+      *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) = make_uint2(hi01, hi23);
     }
     const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
     const float* ixl = (const float*)(lds + LY::off_ss) + kP + 8 * c8;
     const float4 i0 = *(const float4*)ixl, i1 = *(const float4*)(ixl + 4);
     const float invx8[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-    int qv[4][8];
+    // Q(X_scaled)^T: for p = 8 c8 + e the swizzle is e ^ c8; s = 4q is byte
+    // 4 (q & 3) of 16-byte chunk (q >> 2) ^ xsw(p)
+    char* qxb = lds + LY::off_qx + 8 * LC * c8 + 4 * (q & 3);
+    const int qc = (q >> 2) ^ c8;
+    uint32_t qd4[8];  // byte r: row 4q + r
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const T* xe = (const T*)&xr[r];
+    for (int e = 0; e < 8; ++e) {
+      float v[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[r][e] = q8((lutv[r] * Store<DT>::to_f(xe[e])) * invx8[e]);
+      for (int r = 0; r < 4; ++r) {
+        // fl32(lut * x) (one rounding; with fp16 x a single mixed-precision fma
+        // with a zero addend), then fl32(. * inv_X)
+        const float xs = __builtin_fmaf(lutv[r], Store<DT>::to_f(((const T*)&xr[r])[e]), 0.0f);
+        v[r] = xs * invx8[e];
+      }
+      qd4[e] = q8x4(v[0], v[1], v[2], v[3]);
+      *(uint32_t*)(qxb + e * LC + 16 * (qc ^ e)) = qd4[e];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *(uint32_t*)&qx[qx_off<LC>(8 * c8 + e, 4 * q)] = pack4(qv[0][e], qv[1][e], qv[2][e], qv[3][e]);
     if (a.tap_qxs) {
       const Dims& d = a.d;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = (int64_t)k * LC + 4 * q + r;
-        if (t < d.L)
-          *(uint2*)(a.tap_qxs + ((b * d.L + t) * d.H + h) * (int64_t)kP + 8 * c8) =
-              make_uint2(pack4(qv[r][0], qv[r][1], qv[r][2], qv[r][3]),
-                         pack4(qv[r][4], qv[r][5], qv[r][6], qv[r][7]));
+        const int64_t t = (int64_t)t0 + 4 * q + r;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo |= ((qd4[e] >> (8 * r)) & 0xffu) << (8 * e);
+          hi |= ((qd4[e + 4] >> (8 * r)) & 0xffu) << (8 * e);
+        }
+        if (t < d.L) *(uint2*)(a.tap_qxs + ((b * d.L + t) * d.H + h) * (int64_t)kP + 8 * c8) = make_uint2(lo, hi);
       }
     }
   }
@@ -333,7 +369,7 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
       dtv = __uint_as_float(pf.vd);
     else
       dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)pf.vd));
-    vec[LC + tid] = (t0 + tid < a.d.L) ? dtv : 0.f;
+    vec[LC + tid] = (t0 + tid < (int)a.d.L) ? dtv : 0.f;
   }
 }
 
@@ -378,6 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   const int w = wave_id();
   const int64_t Lp = (int64_t)d.c * LC;
   const int H = d.H;
+  T* const ybase = (T*)a.Y + (b * d.L * H + h) * (int64_t)kP;  // uniform
 
   // ChunkState / StatePassing role: n tile nt_own, p tiles pt0 .. pt0 + PTW - 1
   // (each Q(B)^T row is read by exactly one wave)
@@ -417,6 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     const int lane = tid & (kWave - 1);
     const int l16 = lane & 15, lg = lane >> 4;
     const int64_t t0 = (int64_t)k * LC;
+    const int8_t* qcb = a.qC + ((b * Lp + t0) * d.G + g_h) * (int64_t)NS;  // uniform
     const int8_t* qBl = (const int8_t*)(lds + LY::off_qb + (k & 1) * LY::QB);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies have landed
     __syncthreads();  // chunk k staged; H8l holds H_{k-1}
@@ -426,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
-      const int8_t* src = a.qC + ((b * Lp + t0 + 16 * i + l16) * d.G + g_h) * (int64_t)NS + 16 * lg;
+      const int8_t* src = qcb + (uint32_t)((16 * i + l16) * d.G * NS + 16 * lg);
 #pragma unroll
       for (int kn = 0; kn < KN; ++kn) qc2[rr][kn] = *(const v4i*)(src + 64 * kn);
     }
@@ -602,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       }
       // epilogue: lane holds s = s_row and p = 16 pt + 4 lg + r
       const int64_t t = t0 + s_row;
-      T* yrow = (T*)a.Y + ((b * d.L + t) * H + h) * (int64_t)kP + 4 * lg;
+      char* yrow = (char*)ybase + (uint32_t)(((int)t * H * kP + 4 * lg) * (int)sizeof(T));
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         const float y[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
@@ -611,7 +649,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
                               ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[1])) << 16);
           const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[2])) |
                               ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[3])) << 16);
-          *(uint2*)(yrow + 16 * pt) = make_uint2(lo, hi);
+          *(uint2*)(yrow + 16 * pt * (int)sizeof(T)) = make_uint2(lo, hi);
         }
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
@@ -670,6 +708,8 @@ hipError_t launch_main(const FusedArgs& fa, hipStream_t st) {
 
 bool fused_supported(const Dims& d, int dtype, bool int8) {
   if (!int8) return false;
+  // per-sequence offsets are formed in 32 bits
+  if (d.L * d.H * (int64_t)d.P * 2 >= ((int64_t)1 << 31)) return false;
   if (d.B * d.G > 65535 || d.B * d.H > (int64_t)1 << 30) return false;
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
   if (d.P != kP) return false;

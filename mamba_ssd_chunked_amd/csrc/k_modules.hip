@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_quantize_bc(const void* __restrict__ B,
 // write dAcs / LUT_state with coalesced stores. Padded positions past L carry
 // dt = 0, which leaves the running sum unchanged.
 // ---------------------------------------------------------------------------
-constexpr int kCsHeads = 16;
+constexpr int kCsHeads = 4;
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_chunk_cumsum(const void* __restrict__ dt,
