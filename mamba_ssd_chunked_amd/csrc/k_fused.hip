@@ -172,6 +172,8 @@ struct FusedArgs {
   int32_t* tap_s32;
   int8_t* tap_s8;
   int8_t* tap_passed;
+  int64_t slot0;  // first (batch, head) slot of this launch
+  int xcd_map;    // 1: slots are laid out so each XCD serves whole (batch, group) units
 };
 
 template <int LC, int NS>
@@ -205,9 +207,10 @@ __device__ __forceinline__ int qx_off(int p, int s) {
 // Every load is unconditional (addresses are clamped into the tensor and
 // out-of-range rows are zeroed when stored to LDS), so no branch forces the
 // compiler to wait for them before the chunk's compute.
-template <int LC, int NS>
+template <int LC, int NS, int PW>
 struct Prefetch {
-  static constexpr int XI = (LC / 4) * (kP / 8);
+  static constexpr int C8N = 2 * PW;          // 8-column groups of p per workgroup
+  static constexpr int XI = (LC / 4) * C8N;
   static_assert(XI <= kThreads, "tile split");
   uint4 x[4];
   float4 lut;
@@ -216,11 +219,11 @@ struct Prefetch {
   uint32_t qd;  // the dword holding Q(Decay) of the chunk
 };
 
-template <int DT, int LC, int NS>
+template <int DT, int LC, int NS, int PW>
 __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int h, int g_h, int k,
-                                              int tid, Prefetch<LC, NS>& pf) {
+                                              int tid, int c8base, Prefetch<LC, NS, PW>& pf) {
   typedef typename Store<DT>::T T;
-  typedef Prefetch<LC, NS> PF;
+  typedef Prefetch<LC, NS, PW> PF;
   const Dims& d = a.d;
   // wave-uniform 64-bit bases, per-lane 32-bit offsets (one sequence of x is
   // below 2 GB, checked by fused_supported)
@@ -231,7 +234,7 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
   const float* dab = a.dAcs + cs0;
   {
     const int it = tid % PF::XI;
-    const int q = it >> 3, c8 = it & 7;
+    const int q = it / PF::C8N, c8 = c8base + it % PF::C8N;
     const T* xb = (const T*)a.X + (b * d.L * d.H + h) * (int64_t)kP;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -291,15 +294,15 @@ __device__ __forceinline__ v2i lds_tr8(const int8_t* p) {
 // Writes the prefetched chunk into LDS: x transposed, Q(X_scaled) =
 // sat(RHAZ(fl32(fl32(lut * x) * inv_X))) transposed (the quantiser of "Key
 // design 1") and the per-position vectors.
-template <int DT, int LC, int NS>
+template <int DT, int LC, int NS, int PW>
 __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, int64_t b, int h, int k,
-                                               int tid, const Prefetch<LC, NS>& pf) {
+                                               int tid, int c8base, const Prefetch<LC, NS, PW>& pf) {
   typedef typename Store<DT>::T T;
   typedef Lds<LC, NS> LY;
-  typedef Prefetch<LC, NS> PF;
+  typedef Prefetch<LC, NS, PW> PF;
   const int t0 = k * LC;
   if (tid < PF::XI) {
-    const int q = tid >> 3, c8 = tid & 7;
+    const int q = tid / PF::C8N, c8 = c8base + tid % PF::C8N;
     u16* xT = (u16*)(lds + LY::off_xt);
     int8_t* qx = (int8_t*)(lds + LY::off_qx);
     // Rows past L (ragged last chunk) hold copies of row L-1 (finite values):
@@ -373,14 +376,18 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
   }
 }
 
-template <int DT, int LC, int NS>
+// PW = 4: the workgroup owns a whole head (all four 16-wide p tiles).
+// PW = 2: it owns p tiles 2 ph, 2 ph + 1 of a head; two such workgroups cover
+// the head, each recomputing the head's CB tiles. Used for the last, partial
+// round of heads so that it spreads over every CU.
+template <int DT, int LC, int NS, int PW>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   typedef typename Store<DT>::T T;
   typedef Lds<LC, NS> LY;
-  typedef Prefetch<LC, NS> PF;
+  typedef Prefetch<LC, NS, PW> PF;
   constexpr int RT = LC / 16;      // row tiles of the chunk
   constexpr int NT = NS / 16;      // n tiles of the state
-  constexpr int PTW = 4 * NT / kWaves;  // p tiles per wave in ChunkState / StatePassing
+  constexpr int PTW = PW * NT / kWaves;  // p tiles per wave in ChunkState / StatePassing
   constexpr int KS = LC / 64;      // ChunkState K steps
   constexpr int KN = NS / 64;      // K steps over N
 
@@ -393,21 +400,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   float* SSl = (float*)(lds + LY::off_ss);
 
   const Dims& d = a.d;
-  // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8). When
-  // the (batch, group) units divide evenly, every XCD gets whole units, so the
-  // int8 Q(B)/Q(C) rows its heads share stay in that XCD's L2.
-  int64_t unit, hl;
-  {
-    const int64_t nunits = d.B * d.G;
-    if (nunits % 8 == 0) {
-      const int64_t j = blockIdx.x / 8;
-      unit = (blockIdx.x % 8) + 8 * (j / d.hpg);
-      hl = j % d.hpg;
-    } else {
-      unit = blockIdx.x / d.hpg;
-      hl = blockIdx.x % d.hpg;
-    }
+  // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8). With
+  // xcd_map, slot s runs on XCD s % 8 and every XCD gets whole (batch, group)
+  // units, so the int8 Q(B)/Q(C) rows its heads share stay in that XCD's L2.
+  int64_t slot;
+  int ph = 0;
+  if (PW == 4) {
+    slot = a.slot0 + blockIdx.x;
+  } else if (a.xcd_map) {
+    const int64_t j = blockIdx.x / 8;
+    slot = a.slot0 + (blockIdx.x % 8) + 8 * (j >> 1);
+    ph = (int)(j & 1);
+  } else {
+    slot = a.slot0 + blockIdx.x / 2;
+    ph = blockIdx.x & 1;
   }
+  int64_t unit, hl;
+  if (a.xcd_map) {
+    const int64_t j = slot / 8;
+    unit = (slot % 8) + 8 * (j / d.hpg);
+    hl = j % d.hpg;
+  } else {
+    unit = slot / d.hpg;
+    hl = slot % d.hpg;
+  }
+  const int pt_base = (PW == 4) ? 0 : 2 * ph;  // first p tile of this workgroup
   const int64_t b = unit / d.G;
   const int g_h = (int)(unit % d.G);
   const int h = g_h * d.hpg + (int)hl;
@@ -419,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   // ChunkState / StatePassing role: n tile nt_own, p tiles pt0 .. pt0 + PTW - 1
   // (each Q(B)^T row is read by exactly one wave)
   const int nt_own = w % NT;
-  const int pt0 = (w / NT) * PTW;
+  const int pt0 = pt_base + (w / NT) * PTW;
   const float scBC = a.sc.s_C[g_h] * a.sc.s_B[g_h];
   const float sC = a.sc.s_C[g_h];
   const float Dh = a.D[h];
@@ -440,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   {  // chunk 0
     PF pf;
     dma_qb<LC, NS>(a, lds, b, g_h, 0, w, tid0 & (kWave - 1));
-    prefetch_load<DT, LC, NS>(a, b, h, g_h, 0, tid0, pf);
-    prefetch_store<DT, LC, NS>(a, lds, b, h, 0, tid0, pf);
+    prefetch_load<DT, LC, NS, PW>(a, b, h, g_h, 0, tid0, 2 * pt_base, pf);
+    prefetch_store<DT, LC, NS, PW>(a, lds, b, h, 0, tid0, 2 * pt_base, pf);
     qd_word = pf.qd;
   }
 
@@ -509,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     // next chunk: Q(B) rows into the other LDS buffer, x and vectors into registers
     if (more) {
       dma_qb<LC, NS>(a, lds, b, g_h, k + 1, w, lane);
-      prefetch_load<DT, LC, NS>(a, b, h, g_h, k + 1, tid, pf);
+      prefetch_load<DT, LC, NS, PW>(a, b, h, g_h, k + 1, tid, 2 * pt_base, pf);
     }
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
@@ -532,9 +549,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 
       // one accumulator per p tile: off-diagonal tiles are summed unscaled, then
       // multiplied by u_s; ChunkScan1 and the diagonal tile add on top
-      v4f acc[4];
+      v4f acc[PW];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = v4f{0, 0, 0, 0};
+      for (int jp = 0; jp < PW; ++jp) acc[jp] = v4f{0, 0, 0, 0};
       // off-diagonal column tiles j < i in full pairs (jA, jA + 1)
       for (int jA = 0; jA + 1 < i; jA += 2) {
         const int jB = jA + 1;
@@ -546,9 +563,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
         }
         const float4 vA = *(const float4*)&Vw[16 * jA + 4 * lg];
         const float4 vB = *(const float4*)&Vw[16 * jB + 4 * lg];
-        FragF<DT> xf[4];
+        FragF<DT> xf[PW];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) xf[pt] = frag16<DT>(&xT[xT_pair<LC>(16 * pt + l16, jA >> 1, lg)]);
+        for (int jp = 0; jp < PW; ++jp) xf[jp] = frag16<DT>(&xT[xT_pair<LC>(16 * (pt_base + jp) + l16, jA >> 1, lg)]);
         v4i cbA = v4i{0, 0, 0, 0}, cbB = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn) {
@@ -565,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
         wf.set(6, (float)cbB[2] * vB.z);
         wf.set(7, (float)cbB[3] * vB.w);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = FragF<DT>::mma(xf[pt], wf, acc[pt]);
+        for (int jp = 0; jp < PW; ++jp) acc[jp] = FragF<DT>::mma(xf[jp], wf, acc[jp]);
       }
       // diagonal tile j = i (with D on its diagonal, so the skip term D x rides the
       // MFMA). It shares its MFMA with the other tile of its pair (2m, 2m + 1),
@@ -575,13 +592,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       const float a_s = vA2[s_row];
       const float us = fast_exp2(a_s - a_ref);  // u at this lane's position
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] *= us;
+      for (int jp = 0; jp < PW; ++jp) acc[jp] *= us;
       // ChunkScan1 (inter-chunk), transposed: H8 rows x Q(C) rows, scaled by
       // exp(a_s) s_C s_S[p] and added to the output accumulator
       if (k > 0) {
         const float eo = fast_exp2(a_s) * sC;
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
+        for (int jp = 0; jp < PW; ++jp) {
+          const int pt = pt_base + jp;
           v4i acc1 = v4i{0, 0, 0, 0};
 #pragma unroll
           for (int kn = 0; kn < KN; ++kn) {
@@ -589,10 +607,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
             acc1 = mma_i8(hb, qcr[kn], acc1);
           }
           const float4 ss = *(const float4*)&SSl[16 * pt + 4 * lg];
-          acc[pt][0] = fmaf((float)acc1[0], eo * ss.x, acc[pt][0]);
-          acc[pt][1] = fmaf((float)acc1[1], eo * ss.y, acc[pt][1]);
-          acc[pt][2] = fmaf((float)acc1[2], eo * ss.z, acc[pt][2]);
-          acc[pt][3] = fmaf((float)acc1[3], eo * ss.w, acc[pt][3]);
+          acc[jp][0] = fmaf((float)acc1[0], eo * ss.x, acc[jp][0]);
+          acc[jp][1] = fmaf((float)acc1[1], eo * ss.y, acc[jp][1]);
+          acc[jp][2] = fmaf((float)acc1[2], eo * ss.z, acc[jp][2]);
+          acc[jp][3] = fmaf((float)acc1[3], eo * ss.w, acc[jp][3]);
         }
       }
       {
@@ -608,9 +626,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
         const float4 dd = *(const float4*)&vDt[16 * i + 4 * lg];
         float4 vL = make_float4(0.f, 0.f, 0.f, 0.f);
         if (hd) vL = *(const float4*)&Vw[16 * jL + 4 * lg];
-        FragF<DT> xf[4];
+        FragF<DT> xf[PW];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) xf[pt] = frag16<DT>(&xT[xT_pair<LC>(16 * pt + l16, i >> 1, lg)]);
+        for (int jp = 0; jp < PW; ++jp) xf[jp] = frag16<DT>(&xT[xT_pair<LC>(16 * (pt_base + jp) + l16, i >> 1, lg)]);
         v4i cbD = v4i{0, 0, 0, 0}, cbL = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < KN; ++kn) {
@@ -636,14 +654,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
           wf.set(r + 4, hd ? wd[r] : 0.f);
         }
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = FragF<DT>::mma(xf[pt], wf, acc[pt]);
+        for (int jp = 0; jp < PW; ++jp) acc[jp] = FragF<DT>::mma(xf[jp], wf, acc[jp]);
       }
       // epilogue: lane holds s = s_row and p = 16 pt + 4 lg + r
       const int64_t t = t0 + s_row;
       char* yrow = (char*)ybase + (uint32_t)(((int)t * H * kP + 4 * lg) * (int)sizeof(T));
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const float y[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+      for (int jp = 0; jp < PW; ++jp) {
+        const int pt = pt_base + jp;
+        const float y[4] = {acc[jp][0], acc[jp][1], acc[jp][2], acc[jp][3]};
         if (t < d.L) {
           const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[0])) |
                               ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[1])) << 16);
@@ -674,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       if (a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
     if (more) {
-      prefetch_store<DT, LC, NS>(a, lds, b, h, k + 1, tid, pf);
+      prefetch_store<DT, LC, NS, PW>(a, lds, b, h, k + 1, tid, 2 * pt_base, pf);
       qd_word = pf.qd;
     }
   }
@@ -692,16 +711,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 constexpr size_t kAl = 256;
 size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
-template <int DT, int LC, int NS>
-hipError_t launch_main(const FusedArgs& fa, hipStream_t st) {
+template <int DT, int LC, int NS, int PW>
+hipError_t launch_one(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
   constexpr int lds = Lds<LC, NS>::total;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = k_fused_i8<DT, LC, NS>;
+  auto kern = k_fused_i8<DT, LC, NS, PW>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(fa.d.B * fa.d.H)), dim3(kThreads), lds, st, fa);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, st, fa);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// One workgroup per CU at a time: B*H heads run in ceil(B*H / CUs) rounds. When
+// the last round is at most half full, its heads are split in two p halves so
+// the round spreads over all CUs (each half recomputes the head's CB tiles).
+template <int DT, int LC, int NS>
+hipError_t launch_main(FusedArgs fa, hipStream_t st) {
+  const Dims& d = fa.d;
+  const int64_t BH = d.B * d.H;
+  const int64_t ncu = cu_count();
+  int64_t nhalf = 0;
+  if (ncu > 0) {
+    const int64_t rem = BH % ncu;
+    if (rem != 0 && 2 * rem <= ncu) nhalf = rem;
+  }
+  const int64_t nfull = BH - nhalf;
+  const bool unit_map = (d.B * d.G) % 8 == 0;
+  if (nfull > 0) {
+    fa.slot0 = 0;
+    fa.xcd_map = unit_map;
+    const hipError_t e = launch_one<DT, LC, NS, 4>(fa, nfull, st);
+    if (e != hipSuccess) return e;
+  }
+  if (nhalf > 0) {
+    fa.slot0 = nfull;
+    fa.xcd_map = unit_map && nfull % 8 == 0 && nhalf % 8 == 0;
+    return launch_one<DT, LC, NS, 2>(fa, 2 * nhalf, st);
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -757,7 +817,7 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
   if (e != hipSuccess) return e;
 
   const FusedArgs fa{d, X, dt, qB, qC, dAcs, lut, qd, D, sc, Y, (int8_t*)final_state,
-                     tap_qxs, tap_s32, tap_s8, tap_passed};
+                     tap_qxs, tap_s32, tap_s8, tap_passed, 0, 0};
   if (dtype == DT_F16) {
     if (d.l == 256 && d.N == 128) return launch_main<DT_F16, 256, 128>(fa, st);
     if (d.l == 256 && d.N == 64) return launch_main<DT_F16, 256, 64>(fa, st);
