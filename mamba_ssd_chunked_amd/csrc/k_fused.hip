@@ -176,23 +176,18 @@ struct FusedArgs {
   int xcd_map;    // 1: slots are laid out so each XCD serves whole (batch, group) units
 };
 
+// LDS of one workgroup: separate arrays, so the compiler knows the Q(B) buffer
+// (written by the memory-to-LDS copies) is distinct from the others and does
+// not make their reads wait for the copies.
 template <int LC, int NS>
-struct Lds {
-  static constexpr int XT = kP * LC * 2;  // x^T [p][s], 2-byte elements
-  static constexpr int QB = LC * NS;      // Q(B) rows [s][n], two buffers
-  static constexpr int QX = kP * LC;      // Q(X_scaled)^T [p][s]
-  static constexpr int H8 = kP * NS;      // passed state [p][n]
-  static constexpr int VEC = 2 * LC * 4;  // a*log2(e), dt
-  static constexpr int VW = kWaves * LC * 4;
-  static constexpr int SS = 3 * kP * 4;   // s_S[h, p], inv_X[h, p], M_req[h, p]
-  static constexpr int off_xt = 0;
-  static constexpr int off_qb = off_xt + XT;
-  static constexpr int off_qx = off_qb + 2 * QB;
-  static constexpr int off_h8 = off_qx + QX;
-  static constexpr int off_vec = off_h8 + H8;
-  static constexpr int off_vw = off_vec + VEC;
-  static constexpr int off_ss = off_vw + VW;
-  static constexpr int total = off_ss + SS;
+struct Smem {
+  u16* xT;      // x^T [p][s], 2-byte elements (swizzled, see xT_pair)
+  int8_t* qB;   // Q(B) rows [s][n] (swizzled, see b_off)
+  int8_t* qx;   // Q(X_scaled)^T [p][s] (swizzled, see qx_off)
+  int8_t* h8;   // passed state [p][n]
+  float* vec;   // a * log2(e) [l], dt [l]
+  float* vw;    // one ChunkScan2 table per wave [l]
+  float* ss;    // s_S[h, p], inv_X[h, p], M_req[h, p]
 };
 
 // Q(X_scaled)^T tile [p][s] (bytes); s aligned to 4
@@ -219,40 +214,69 @@ struct Prefetch {
   uint32_t qd;  // the dword holding Q(Decay) of the chunk
 };
 
+// Per-lane byte offsets of the staging loads, computed once per workgroup (the
+// per-chunk parts are wave-uniform and live in scalar registers).
+template <int LC, int NS, int PW>
+struct LaneOff {
+  static constexpr int OPS = LC * NS / 1024;  // 1 KB Q(B) copies per chunk
+  static constexpr int PER = OPS / kWaves;
+  uint32_t q4;        // first x row of this thread (4q)
+  uint32_t xc;        // byte offset of columns 8 c8 .. 8 c8 + 7 within a row
+  uint32_t lut;       // lut / dAcs entries 4q .. 4q + 3
+  uint32_t sv;        // position of the per-position vectors (dAcs, dt)
+  uint32_t dma[PER];  // Q(B) source of each 1 KB copy
+};
+
 template <int DT, int LC, int NS, int PW>
-__device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int h, int g_h, int k,
-                                              int tid, int c8base, Prefetch<LC, NS, PW>& pf) {
+__device__ __forceinline__ LaneOff<LC, NS, PW> lane_offsets(const Dims& d, int tid, int c8base) {
+  typedef typename Store<DT>::T T;
+  typedef Prefetch<LC, NS, PW> PF;
+  typedef LaneOff<LC, NS, PW> LO;
+  constexpr int nch = NS / 16;
+  LO o;
+  const int it = tid % PF::XI;
+  const int q = it / PF::C8N, c8 = c8base + it % PF::C8N;
+  o.q4 = (uint32_t)(4 * q);
+  o.xc = (uint32_t)(8 * c8 * (int)sizeof(T));
+  o.lut = (uint32_t)(16 * q);
+  o.sv = (uint32_t)(tid % LC);
+  const int w = tid >> 6, lane = tid & (kWave - 1);
+#pragma unroll
+  for (int m = 0; m < LO::PER; ++m) {
+    const int byte = 1024 * (w * LO::PER + m) + 16 * lane;
+    const int r = byte / NS, pc = (byte % NS) / 16;
+    const int c16 = pc ^ (r & (nch - 1) & 7);
+    o.dma[m] = (uint32_t)(r * d.G * NS + 16 * c16);
+  }
+  return o;
+}
+
+template <int DT, int LC, int NS, int PW>
+__device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int h, int k, int tid,
+                                              int c8base, const LaneOff<LC, NS, PW>& lo,
+                                              Prefetch<LC, NS, PW>& pf) {
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS, PW> PF;
   const Dims& d = a.d;
-  // wave-uniform 64-bit bases, per-lane 32-bit offsets (one sequence of x is
+  // wave-uniform 64-bit bases plus per-lane 32-bit offsets (one sequence of x is
   // below 2 GB, checked by fused_supported)
   const int t0 = k * LC;
-  const int Lm1 = (int)d.L - 1;
   const int64_t cs0 = ((b * d.H + h) * d.c + k) * (int64_t)LC;
-  const float* lutb = a.lut + cs0;
-  const float* dab = a.dAcs + cs0;
-  {
-    const int it = tid % PF::XI;
-    const int q = it / PF::C8N, c8 = c8base + it % PF::C8N;
-    const T* xb = (const T*)a.X + (b * d.L * d.H + h) * (int64_t)kP;
+  const int64_t rowB = (int64_t)d.H * kP * sizeof(T);  // bytes per position of x
+  const char* xk = (const char*)a.X + (b * d.L * d.H + h) * (int64_t)kP * sizeof(T) + t0 * rowB;
+  const char* dtk = (const char*)a.dt + ((b * d.L + t0) * d.H + h) * (int64_t)sizeof(T);
+  // positions past L (ragged last chunk) read row L - 1; the clamp is a min,
+  // not a branch, so no load has to complete before the chunk's compute
+  const uint32_t lim = (uint32_t)min((int64_t)LC - 1, d.L - 1 - t0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = min(t0 + 4 * q + r, Lm1);
-      pf.x[r] = *(const uint4*)((const char*)xb + (uint32_t)((t * d.H * kP + 8 * c8) * (int)sizeof(T)));
-    }
-    pf.lut = *(const float4*)(lutb + (uint32_t)(4 * q));
-  }
-  {
-    const int sv = tid % LC;
-    pf.va = dab[(uint32_t)sv];
-    const uint32_t t = (uint32_t)min(t0 + sv, Lm1);
-    const int64_t db = b * d.L * d.H + h;
-    if constexpr (sizeof(T) == 4)
-      pf.vd = ((const uint32_t*)a.dt + db)[t * (uint32_t)d.H];
-    else
-      pf.vd = ((const u16*)a.dt + db)[t * (uint32_t)d.H];
-  }
+  for (int r = 0; r < 4; ++r)
+    pf.x[r] = *(const uint4*)(xk + (min(lo.q4 + r, lim) * (uint32_t)rowB + lo.xc));
+  if constexpr (sizeof(T) == 4)
+    pf.vd = *(const uint32_t*)(dtk + min(lo.sv, lim) * (uint32_t)(d.H * sizeof(T)));
+  else
+    pf.vd = *(const u16*)(dtk + min(lo.sv, lim) * (uint32_t)(d.H * sizeof(T)));
+  pf.lut = *(const float4*)((const char*)(a.lut + cs0) + lo.lut);
+  pf.va = *(const float*)((const char*)(a.dAcs + cs0) + 4 * lo.sv);
   const int64_t qi = (b * d.H + h) * d.c + k;
   pf.qd = *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
 }
@@ -261,25 +285,19 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
 // registers): each wave copy moves 1 KB, lane L filling bytes 16 L .. 16 L + 15
 // of it, so the source address of each lane is chosen to produce the swizzled
 // b_off layout.
-template <int LC, int NS>
-__device__ __forceinline__ void dma_qb(const FusedArgs& a, char* lds, int64_t b, int g_h, int k, int w,
-                                       int lane) {
-  constexpr int OPS = LC * NS / 1024;
-  constexpr int PER = OPS / kWaves;
-  constexpr int nch = NS / 16;
-  static_assert(OPS % kWaves == 0 && PER >= 1, "copy split");
+template <int LC, int NS, int PW>
+__device__ __forceinline__ void dma_qb(const FusedArgs& a, int8_t* qBl, int64_t b, int g_h, int k, int w,
+                                       const LaneOff<LC, NS, PW>& lo) {
+  typedef LaneOff<LC, NS, PW> LO;
+  static_assert(LO::OPS % kWaves == 0 && LO::PER >= 1, "copy split");
   const Dims& d = a.d;
   const int8_t* qb = a.qB + ((b * (int64_t)d.c * LC + (int64_t)k * LC) * d.G + g_h) * (int64_t)NS;
-  char* dst = lds + Lds<LC, NS>::off_qb + (k & 1) * Lds<LC, NS>::QB;
+  int8_t* dst = qBl;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int gi = w * PER + m;
-    const int byte = 1024 * gi + 16 * lane;
-    const int r = byte / NS, pc = (byte % NS) / 16;
-    const int c16 = pc ^ (r & (nch - 1) & 7);
-    const int8_t* src = qb + (uint32_t)(r * d.G * NS + 16 * c16);
-    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + 1024 * gi),
-                                     16, 0, 0);
+  for (int m = 0; m < LO::PER; ++m) {
+    const int gi = w * LO::PER + m;
+    __builtin_amdgcn_global_load_lds((const void*)(qb + lo.dma[m]),
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * gi), 16, 0, 0);
   }
 }
 
@@ -295,27 +313,29 @@ __device__ __forceinline__ v2i lds_tr8(const int8_t* p) {
 // sat(RHAZ(fl32(fl32(lut * x) * inv_X))) transposed (the quantiser of "Key
 // design 1") and the per-position vectors.
 template <int DT, int LC, int NS, int PW>
-__device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, int64_t b, int h, int k,
+__device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC, NS>& sm, int64_t b, int h, int k,
                                                int tid, int c8base, const Prefetch<LC, NS, PW>& pf) {
   typedef typename Store<DT>::T T;
-  typedef Lds<LC, NS> LY;
   typedef Prefetch<LC, NS, PW> PF;
   const int t0 = k * LC;
   if (tid < PF::XI) {
     const int q = tid / PF::C8N, c8 = c8base + tid % PF::C8N;
-    u16* xT = (u16*)(lds + LY::off_xt);
-    int8_t* qx = (int8_t*)(lds + LY::off_qx);
     // Rows past L (ragged last chunk) hold copies of row L-1 (finite values):
     // their LUT_state is 0, so their Q(X_scaled) is 0, and ChunkScan2 never
     // pairs them with a valid output row (causal mask) and gives them weight 0.
-    const uint4* xr = pf.x;
+    // The loaded values pass through an empty asm here, so nothing that uses
+    // them (unpacking, conversion) can be scheduled right after the loads, which
+    // would make the prefetch wait for memory.
+    uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
     const uint32_t* w0 = (const uint32_t*)&xr[0];
     const uint32_t* w1 = (const uint32_t*)&xr[1];
     const uint32_t* w2 = (const uint32_t*)&xr[2];
     const uint32_t* w3 = (const uint32_t*)&xr[3];
     // x^T: for p = 8 c8 + e' the row swizzle xsw(p) is e' ^ c8, and s = 4q sits in
     // 16-byte chunk (4 (q >> 3) + (q & 3)) ^ xsw(p), half (q >> 2) & 1 of it
-    char* xTb = lds + LY::off_xt + 16 * LC * c8 + 8 * ((q >> 2) & 1);
+    char* xTb = (char*)sm.xT + 16 * LC * c8 + 8 * ((q >> 2) & 1);
     const int mgc = (4 * (q >> 3) + (q & 3)) ^ c8;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -328,12 +348,12 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
       *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) = make_uint2(hi01, hi23);
     }
     const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
-    const float* ixl = (const float*)(lds + LY::off_ss) + kP + 8 * c8;
+    const float* ixl = sm.ss + kP + 8 * c8;
     const float4 i0 = *(const float4*)ixl, i1 = *(const float4*)(ixl + 4);
     const float invx8[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
     // Q(X_scaled)^T: for p = 8 c8 + e the swizzle is e ^ c8; s = 4q is byte
     // 4 (q & 3) of 16-byte chunk (q >> 2) ^ xsw(p)
-    char* qxb = lds + LY::off_qx + 8 * LC * c8 + 4 * (q & 3);
+    char* qxb = (char*)sm.qx + 8 * LC * c8 + 4 * (q & 3);
     const int qc = (q >> 2) ^ c8;
     uint32_t qd4[8];  // byte r: row 4q + r
 #pragma unroll
@@ -343,7 +363,9 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
       for (int r = 0; r < 4; ++r) {
         // fl32(lut * x) (one rounding; with fp16 x a single mixed-precision fma
         // with a zero addend), then fl32(. * inv_X)
-        const float xs = __builtin_fmaf(lutv[r], Store<DT>::to_f(((const T*)&xr[r])[e]), 0.0f);
+        const uint32_t dw = (e >> 1) == 0 ? xr[r].x : (e >> 1) == 1 ? xr[r].y : (e >> 1) == 2 ? xr[r].z : xr[r].w;
+        const uint32_t hv = (e & 1) ? (dw >> 16) : (dw & 0xffffu);
+        const float xs = __builtin_fmaf(lutv[r], Store<DT>::to_f(__builtin_bit_cast(T, (u16)hv)), 0.0f);
         v[r] = xs * invx8[e];
       }
       qd4[e] = q8x4(v[0], v[1], v[2], v[3]);
@@ -365,7 +387,7 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
     }
   }
   if (tid < LC) {
-    float* vec = (float*)(lds + LY::off_vec);
+    float* vec = sm.vec;
     vec[tid] = pf.va * kLog2e;
     float dtv;
     if constexpr (sizeof(T) == 4)
@@ -383,7 +405,6 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, char* lds, in
 template <int DT, int LC, int NS, int PW>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   typedef typename Store<DT>::T T;
-  typedef Lds<LC, NS> LY;
   typedef Prefetch<LC, NS, PW> PF;
   constexpr int RT = LC / 16;      // row tiles of the chunk
   constexpr int NT = NS / 16;      // n tiles of the state
@@ -391,13 +412,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   constexpr int KS = LC / 64;      // ChunkState K steps
   constexpr int KN = NS / 64;      // K steps over N
 
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const u16* xT = (const u16*)(lds + LY::off_xt);
-  const int8_t* qxl = (const int8_t*)(lds + LY::off_qx);
-  int8_t* H8l = (int8_t*)(lds + LY::off_h8);
-  const float* vA2 = (const float*)(lds + LY::off_vec);
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
+  __shared__ __attribute__((aligned(16))) int8_t s_qB[LC * NS];
+  __shared__ __attribute__((aligned(16))) int8_t s_qx[kP * LC];
+  __shared__ __attribute__((aligned(16))) int8_t s_h8[kP * NS];
+  __shared__ __attribute__((aligned(16))) float s_vec[2 * LC];
+  __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
+  __shared__ __attribute__((aligned(16))) float s_ss[3 * kP];
+  const Smem<LC, NS> sm{s_xT, s_qB, s_qx, s_h8, s_vec, s_vw, s_ss};
+  const u16* xT = s_xT;
+  const int8_t* qxl = s_qx;
+  int8_t* H8l = s_h8;
+  const int8_t* qBl = s_qB;
+  const float* vA2 = s_vec;
   const float* vDt = vA2 + LC;
-  float* SSl = (float*)(lds + LY::off_ss);
+  float* SSl = s_ss;
 
   const Dims& d = a.d;
   // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8). With
@@ -447,18 +476,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     SSl[2 * kP + tid0] = a.sc.M_req[h * kP + tid0];
   }
   __syncthreads();
-  float* Vw = (float*)(lds + LY::off_vw) + w * LC;
+  float* Vw = s_vw + w * LC;
 
   uint32_t H8[PTW];  // passed state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
 #pragma unroll
   for (int j = 0; j < PTW; ++j) H8[j] = 0;
 
+  const LaneOff<LC, NS, PW> lo = lane_offsets<DT, LC, NS, PW>(d, tid0, 2 * pt_base);
+  // Q(C) rows (B operand over N) of this wave's two row tiles {w, 15 - w}
+  const auto load_qc2 = [&](int k, int lane, v4i (&qc)[2][KN]) {
+    const int8_t* qcb = a.qC + ((b * Lp + (int64_t)k * LC) * d.G + g_h) * (int64_t)NS;  // uniform
+    const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
+      const int8_t* src = qcb + (uint32_t)((16 * i + l16) * d.G * NS + 16 * lg);
+#pragma unroll
+      for (int kn = 0; kn < KN; ++kn) qc[rr][kn] = *(const v4i*)(src + 64 * kn);
+    }
+  };
+  v4i qc2[2][KN];
+  load_qc2(0, tid0 & (kWave - 1), qc2);
   uint32_t qd_word;  // dword holding Q(Decay) of the current chunk
   {  // chunk 0
     PF pf;
-    dma_qb<LC, NS>(a, lds, b, g_h, 0, w, tid0 & (kWave - 1));
-    prefetch_load<DT, LC, NS, PW>(a, b, h, g_h, 0, tid0, 2 * pt_base, pf);
-    prefetch_store<DT, LC, NS, PW>(a, lds, b, h, 0, tid0, 2 * pt_base, pf);
+    dma_qb<LC, NS, PW>(a, s_qB, b, g_h, 0, w, lo);
+    prefetch_load<DT, LC, NS, PW>(a, b, h, 0, tid0, 2 * pt_base, lo, pf);
+    prefetch_store<DT, LC, NS, PW>(a, sm, b, h, 0, tid0, 2 * pt_base, pf);
     qd_word = pf.qd;
   }
 
@@ -471,22 +515,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     const int lane = tid & (kWave - 1);
     const int l16 = lane & 15, lg = lane >> 4;
     const int64_t t0 = (int64_t)k * LC;
-    const int8_t* qcb = a.qC + ((b * Lp + t0) * d.G + g_h) * (int64_t)NS;  // uniform
-    const int8_t* qBl = (const int8_t*)(lds + LY::off_qb + (k & 1) * LY::QB);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies have landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies and Q(C) rows have landed
     __syncthreads();  // chunk k staged; H8l holds H_{k-1}
     const int qd = (int)((qd_word >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
-    // Q(C) rows of this wave's row tiles (B operand over N), issued first
-    v4i qc2[2][KN];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
-      const int8_t* src = qcb + (uint32_t)((16 * i + l16) * d.G * NS + 16 * lg);
-#pragma unroll
-      for (int kn = 0; kn < KN; ++kn) qc2[rr][kn] = *(const v4i*)(src + 64 * kn);
-    }
     PF pf;
-    const bool more = k + 1 < d.c;
+    // The next chunk's loads are issued unconditionally (the last chunk reloads
+    // itself): with no branch around them the compiler counts outstanding loads
+    // exactly instead of waiting for all of them where the paths merge.
+    const int kn = min(k + 1, d.c - 1);
 
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
     uint32_t S8[PTW];
@@ -523,11 +559,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       }
     }
 
-    // next chunk: Q(B) rows into the other LDS buffer, x and vectors into registers
-    if (more) {
-      dma_qb<LC, NS>(a, lds, b, g_h, k + 1, w, lane);
-      prefetch_load<DT, LC, NS, PW>(a, b, h, g_h, k + 1, tid, 2 * pt_base, pf);
-    }
+    // The Q(C) rows are complete (they were loaded during the previous chunk's
+    // tail); passing them through an empty asm here keeps the compiler from
+    // placing its own wait for them inside the scan loops, where the in-order
+    // load counter would also wait for every prefetch load.
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int kn = 0; kn < KN; ++kn) asm volatile("" : "+v"(qc2[rr][kn]));
+    // next chunk: x and vectors into registers (Q(B) rows follow after the scan)
+    prefetch_load<DT, LC, NS, PW>(a, b, h, kn, tid, 2 * pt_base, lo, pf);
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
     // (outputs land as 4 consecutive p per lane for one position s)
@@ -674,6 +715,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
     }
     __syncthreads();  // chunk k's tiles and H8l are no longer read
+    // stage the next chunk's x tile, then start its Q(B) rows (straight into the
+    // now free LDS buffer) and Q(C) rows; they land while StatePassing runs
+    prefetch_store<DT, LC, NS, PW>(a, sm, b, h, kn, tid, 2 * pt_base, pf);
+    dma_qb<LC, NS, PW>(a, s_qB, b, g_h, kn, w, lo);
+    load_qc2(kn, lane, qc2);
 
     // ---- StatePassing (Eq. 6) in registers; publish H8 for the next ChunkScan1 ----
 #pragma unroll
@@ -692,11 +738,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       if (a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = S8[j];
       if (a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
-    if (more) {
-      prefetch_store<DT, LC, NS, PW>(a, lds, b, h, k + 1, tid, 2 * pt_base, pf);
-      qd_word = pf.qd;
-    }
+    qd_word = pf.qd;
   }
+  // the last (redundant) Q(B) copy must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (a.final_state) {
     const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
 #pragma unroll
@@ -713,13 +758,7 @@ size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
 template <int DT, int LC, int NS, int PW>
 hipError_t launch_one(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
-  constexpr int lds = Lds<LC, NS>::total;
-  static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = k_fused_i8<DT, LC, NS, PW>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, st, fa);
+  hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, PW>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
   return hipGetLastError();
 }
 
