@@ -753,6 +753,400 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   }
 }
 
+// ===========================================================================
+// Fused float forward (fp16 inputs). The same per-head walk over the chunks as
+// the INT8 kernel, with every contraction on fp16 MFMA (fp32 accumulation):
+//   ChunkState   S^T[n,p] = sum_s B^T[n,s] (LUT x)^T[s,p]  (B^T by transposing
+//                LDS reads of the B rows, LUT x rounded once to fp16);
+//   StatePassing H_k = exp(a_{k,l-1}) H_{k-1} + S_k, in fp32 registers;
+//   ChunkScan1   Y_off = exp(a_s) sum_n C[s,n] H_{k-1}[p,n] (H as fp16 in LDS);
+//   ChunkBMM/Scan2 as in the INT8 kernel, CB from fp16 B and C rows.
+// ===========================================================================
+
+// fp16 tiles [rows][W] (element offsets); 16-byte chunks XOR-swizzled with the
+// low row bits (up to 16 distinct chunks for the 16 lanes read together)
+template <int W>
+__device__ __forceinline__ int h_off(int r, int c) {
+  constexpr int nch = W / 8;
+  constexpr int msk = (nch < 16 ? nch : 16) - 1;
+  return r * W + 8 * ((c >> 3) ^ (r & msk)) + (c & 7);
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+// Transposing LDS read (16-bit elements): the 16 lanes of a group each point at
+// 8 bytes; lanes 4r .. 4r + 3 form row r (16 elements) of a 4 x 16 matrix, and
+// lane i receives column i (element i of rows 0..3).
+__device__ __forceinline__ v4s lds_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(u16*)p);
+}
+
+typedef short v8s __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v8s v8s_join(v4s lo, v4s hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ FragF<DT_F16> frag_u4(const uint4& v) {
+  FragF<DT_F16> f;
+  f.v = __builtin_bit_cast(v8h, v);
+  return f;
+}
+
+struct FusedFArgs {
+  Dims d;
+  const void* X;
+  const void* dt;
+  const void* B;
+  const void* C;
+  const float* dAcs;
+  const float* lut;
+  const float* D;
+  void* Y;
+  float* final_state;
+  int xcd_map;
+};
+
+template <int LC, int NS>
+__global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
+  typedef _Float16 T;
+  typedef FragF<DT_F16> F;
+  constexpr int RT = LC / 16;            // row tiles of the chunk
+  constexpr int NT = NS / 16;            // n tiles of the state
+  constexpr int PTW = 4 * NT / kWaves;   // p tiles per wave in ChunkState / StatePassing
+  constexpr int KSF = LC / 32;           // ChunkState K steps (fp16 MFMA, K = 32)
+  constexpr int KNF = NS / 32;           // K steps over N
+  constexpr int XI = (LC / 4) * 8;       // staging items (4 rows x 8 p each)
+  static_assert(XI <= kThreads, "tile split");
+
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];  // x^T (xT_pair layout)
+  __shared__ __attribute__((aligned(16))) u16 s_xs[kP * LC];  // fp16(LUT x)^T [p][s] (h_off<LC>)
+  __shared__ __attribute__((aligned(16))) u16 s_B[LC * NS];   // B rows [s][n] (h_off<NS>)
+  __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];   // fp16 passed state [p][n] (h_off<NS>)
+  __shared__ __attribute__((aligned(16))) float s_vec[2 * LC];  // a*log2(e), dt
+  __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
+  const float* vA2 = s_vec;
+  const float* vDt = s_vec + LC;
+
+  const Dims& d = a.d;
+  const int64_t slot = blockIdx.x;
+  int64_t unit, hl;
+  if (a.xcd_map) {
+    const int64_t j = slot / 8;
+    unit = (slot % 8) + 8 * (j / d.hpg);
+    hl = j % d.hpg;
+  } else {
+    unit = slot / d.hpg;
+    hl = slot % d.hpg;
+  }
+  const int64_t b = unit / d.G;
+  const int g_h = (int)(unit % d.G);
+  const int h = g_h * d.hpg + (int)hl;
+  const int w = wave_id();
+  const int H = d.H;
+  const int nt_own = w % NT;
+  const int pt0 = (w / NT) * PTW;
+  const float Dh = a.D[h];
+  const int tid0 = threadIdx.x;
+  float* Vw = s_vw + w * LC;
+  T* const ybase = (T*)a.Y + (b * d.L * H + h) * (int64_t)kP;
+  const T* const Xb = (const T*)a.X + (b * d.L * H + h) * (int64_t)kP;
+  const T* const Bb = (const T*)a.B + (b * d.L * d.G + g_h) * (int64_t)NS;
+  const T* const Cb = (const T*)a.C + (b * d.L * d.G + g_h) * (int64_t)NS;
+  const int rowB = d.G * NS;  // elements between consecutive positions of B / C
+  const int rowX = H * kP;    // elements between consecutive positions of x
+
+  // staging of chunk kc: x^T, fp16(LUT x)^T and the per-position vectors
+  struct Pf {
+    uint4 x[4];
+    float4 lut;
+    float va;
+    uint32_t vd;
+  };
+  const auto stage_load = [&](int kc, int tid, Pf& pf) {
+    const int t0 = kc * LC;
+    const int lim = min(LC - 1, (int)d.L - 1 - t0);
+    const int it = tid % XI;
+    const int q = it >> 3, c8 = it & 7;
+    const T* xk = Xb + (int64_t)t0 * rowX + 8 * c8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pf.x[r] = *(const uint4*)(xk + (uint32_t)(min(4 * q + r, lim) * rowX));
+    const int64_t cs0 = ((b * H + h) * d.c + kc) * (int64_t)LC;
+    pf.lut = *(const float4*)(a.lut + cs0 + 4 * q);
+    const int sv = tid % LC;
+    pf.va = a.dAcs[cs0 + sv];
+    pf.vd = ((const u16*)a.dt)[((b * d.L + t0) * H + h) + (uint32_t)(min(sv, lim) * H)];
+  };
+  const auto stage_store = [&](int kc, int tid, const Pf& pf) {
+    const int t0 = kc * LC;
+    if (tid < XI) {
+      const int q = tid >> 3, c8 = tid & 7;
+      uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
+      const uint32_t* w0 = (const uint32_t*)&xr[0];
+      const uint32_t* w1 = (const uint32_t*)&xr[1];
+      const uint32_t* w2 = (const uint32_t*)&xr[2];
+      const uint32_t* w3 = (const uint32_t*)&xr[3];
+      char* xTb = (char*)s_xT + 16 * LC * c8 + 8 * ((q >> 2) & 1);
+      const int mgc = (4 * (q >> 3) + (q & 3)) ^ c8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *(uint2*)(xTb + (2 * e) * 2 * LC + 16 * (mgc ^ (2 * e))) =
+            make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u), __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u));
+        *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) =
+            make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u), __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
+      }
+      // fp16(fl32(LUT x)) for 4 rows of each p
+      const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t dw = (e >> 1) == 0 ? xr[r].x : (e >> 1) == 1 ? xr[r].y : (e >> 1) == 2 ? xr[r].z : xr[r].w;
+          const uint32_t hv = (e & 1) ? (dw >> 16) : (dw & 0xffffu);
+          v[r] = __builtin_fmaf(lutv[r], (float)__builtin_bit_cast(_Float16, (u16)hv), 0.0f);
+        }
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)v[0]) |
+                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v[1]) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)v[2]) |
+                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v[3]) << 16);
+        *(uint2*)&s_xs[h_off<LC>(8 * c8 + e, 4 * q)] = make_uint2(lo, hi);
+      }
+    }
+    if (tid < LC) {
+      s_vec[tid] = pf.va * kLog2e;
+      const float dtv = (float)__builtin_bit_cast(_Float16, (u16)pf.vd);
+      s_vec[LC + tid] = (t0 + tid < (int)d.L) ? dtv : 0.f;
+    }
+  };
+  // B rows of chunk kc straight into LDS (1 KB per copy; lane L fills bytes
+  // 16 L .. 16 L + 15, its source chosen to give the h_off<NS> layout)
+  const auto dma_B = [&](int kc, int lane) {
+    constexpr int OPS = LC * NS * 2 / 1024;
+    constexpr int msk = (NS / 8 < 16 ? NS / 8 : 16) - 1;
+    const int t0 = kc * LC;
+    const int lim = min(LC - 1, (int)d.L - 1 - t0);
+    const T* src0 = Bb + (int64_t)t0 * rowB;
+#pragma unroll
+    for (int gi = w; gi < OPS; gi += kWaves) {
+      const int byte = 1024 * gi + 16 * lane;
+      const int r = byte / (2 * NS), pc = (byte % (2 * NS)) / 16;
+      const int c = pc ^ (r & msk);
+      __builtin_amdgcn_global_load_lds((const void*)(src0 + (uint32_t)(min(r, lim) * rowB + 8 * c)),
+                                       (__attribute__((address_space(3))) void*)((char*)s_B + 1024 * gi), 16, 0, 0);
+    }
+  };
+  // C rows (B operand over N) of this wave's row tiles {w, 15 - w}
+  const auto load_C = [&](int kc, int lane, uint4 (&cf)[2][KNF]) {
+    const int t0 = kc * LC;
+    const int lim = min(LC - 1, (int)d.L - 1 - t0);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const T* c0 = Cb + (int64_t)t0 * rowB;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
+      const T* src = c0 + (uint32_t)(min(16 * i + l16, lim) * rowB + 8 * lg);
+#pragma unroll
+      for (int kn = 0; kn < KNF; ++kn) cf[rr][kn] = *(const uint4*)(src + 32 * kn);
+    }
+  };
+
+  float Hs[PTW][4];  // fp32 state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
+#pragma unroll
+  for (int j = 0; j < PTW; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Hs[j][r] = 0.f;
+
+  uint4 cf2[2][KNF];
+  {  // chunk 0
+    Pf pf;
+    dma_B(0, tid0 & (kWave - 1));
+    load_C(0, tid0 & (kWave - 1), cf2);
+    stage_load(0, tid0, pf);
+    stage_store(0, tid0, pf);
+  }
+
+  for (int k = 0; k < d.c; ++k) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int64_t t0 = (int64_t)k * LC;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // B rows and C rows have landed
+    __syncthreads();  // chunk k staged; s_H holds H_{k-1}
+    const float alast2 = vA2[LC - 1];  // a_{k,l-1} log2(e): StatePassing decay
+
+    // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
+    v4f sacc[PTW];
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) sacc[j] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KSF; ++ks) {
+      // A: B^T rows n = 16 nt_own + l16, K = s0 .. s0 + 7 (two reads of 4 rows)
+      const int s0 = 32 * ks + 8 * lg;
+      const int cn = 16 * nt_own + 4 * (l16 & 3);
+      const v4s lo = lds_tr16(s_B + h_off<NS>(s0 + (l16 >> 2), cn));
+      const v4s hi = lds_tr16(s_B + h_off<NS>(s0 + 4 + (l16 >> 2), cn));
+      F fa;
+      fa.v = __builtin_bit_cast(v8h, v8s_join(lo, hi));
+#pragma unroll
+      for (int j = 0; j < PTW; ++j) {
+        const F fb = frag16<DT_F16>(&s_xs[h_off<LC>(16 * (pt0 + j) + l16, s0)]);
+        sacc[j] = F::mma(fa, fb, sacc[j]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int kn = 0; kn < KNF; ++kn)
+        asm volatile("" : "+v"(cf2[rr][kn].x), "+v"(cf2[rr][kn].y), "+v"(cf2[rr][kn].z), "+v"(cf2[rr][kn].w));
+    const int kn1 = min(k + 1, d.c - 1);
+    Pf pf;
+    stage_load(kn1, tid, pf);
+
+    // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int i = (rr == 0) ? w : 2 * kWaves - 1 - w;
+      if (i >= RT) continue;
+      const int s_row = 16 * i + l16;
+      F cr[KNF];
+#pragma unroll
+      for (int kn = 0; kn < KNF; ++kn) cr[kn] = frag_u4(rr ? cf2[1][kn] : cf2[0][kn]);
+      // V_i[s'] = exp(a_{16i} - a_s') dt_s' for s' < 16 i
+      const float a_ref = vA2[16 * i];
+      for (int sp = lane; sp < 16 * i; sp += kWave) Vw[sp] = fast_exp2(a_ref - vA2[sp]) * vDt[sp];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      v4f acc[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[pt] = v4f{0, 0, 0, 0};
+      for (int jA = 0; jA + 1 < i; jA += 2) {
+        const int jB = jA + 1;
+        v4f cbA = v4f{0, 0, 0, 0}, cbB = v4f{0, 0, 0, 0};
+#pragma unroll
+        for (int kn = 0; kn < KNF; ++kn)
+          cbA = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * jA + l16, 32 * kn + 8 * lg)]), cr[kn], cbA);
+#pragma unroll
+        for (int kn = 0; kn < KNF; ++kn)
+          cbB = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * jB + l16, 32 * kn + 8 * lg)]), cr[kn], cbB);
+        const float4 vA = *(const float4*)&Vw[16 * jA + 4 * lg];
+        const float4 vB = *(const float4*)&Vw[16 * jB + 4 * lg];
+        F wf;
+        wf.set(0, cbA[0] * vA.x);
+        wf.set(1, cbA[1] * vA.y);
+        wf.set(2, cbA[2] * vA.z);
+        wf.set(3, cbA[3] * vA.w);
+        wf.set(4, cbB[0] * vB.x);
+        wf.set(5, cbB[1] * vB.y);
+        wf.set(6, cbB[2] * vB.z);
+        wf.set(7, cbB[3] * vB.w);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          acc[pt] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * pt + l16, jA >> 1, lg)]), wf, acc[pt]);
+      }
+      const float a_s = vA2[s_row];
+      const float us = fast_exp2(a_s - a_ref);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[pt] *= us;
+      // ChunkScan1: exp(a_s) sum_n C[s,n] H_{k-1}[p,n]
+      if (k > 0) {
+        const float eo = fast_exp2(a_s);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          v4f acc1 = v4f{0, 0, 0, 0};
+#pragma unroll
+          for (int kn = 0; kn < KNF; ++kn)
+            acc1 = F::mma(frag16<DT_F16>(&s_H[h_off<NS>(16 * pt + l16, 32 * kn + 8 * lg)]), cr[kn], acc1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(acc1[r], eo, acc[pt][r]);
+        }
+      }
+      {  // diagonal tile (D on its diagonal), sharing its MFMA with tile i - 1 (odd i)
+        const int hd = i & 1;
+        const int jL = i - 1;
+        v4f cbD = v4f{0, 0, 0, 0}, cbL = v4f{0, 0, 0, 0};
+#pragma unroll
+        for (int kn = 0; kn < KNF; ++kn)
+          cbD = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * i + l16, 32 * kn + 8 * lg)]), cr[kn], cbD);
+        if (hd) {
+#pragma unroll
+          for (int kn = 0; kn < KNF; ++kn)
+            cbL = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * jL + l16, 32 * kn + 8 * lg)]), cr[kn], cbL);
+        }
+        const float4 ad = *(const float4*)&vA2[16 * i + 4 * lg];
+        const float4 dd = *(const float4*)&vDt[16 * i + 4 * lg];
+        float4 vL = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (hd) vL = *(const float4*)&Vw[16 * jL + 4 * lg];
+        const float adv[4] = {ad.x, ad.y, ad.z, ad.w};
+        const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+        const float vLv[4] = {vL.x * us, vL.y * us, vL.z * us, vL.w * us};
+        float wd[4], wl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sp = 16 * i + 4 * lg + r;
+          float wv = (sp <= s_row) ? cbD[r] * fast_exp2(a_s - adv[r]) * ddv[r] : 0.f;
+          if (sp == s_row) wv += Dh;
+          wd[r] = wv;
+          wl[r] = cbL[r] * vLv[r];
+        }
+        F wf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          wf.set(r, hd ? wl[r] : wd[r]);
+          wf.set(r + 4, hd ? wd[r] : 0.f);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          acc[pt] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * pt + l16, i >> 1, lg)]), wf, acc[pt]);
+      }
+      const int64_t t = t0 + s_row;
+      char* yrow = (char*)ybase + (uint32_t)(((int)t * H * kP + 4 * lg) * 2);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        if (t < d.L) {
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][0]) |
+                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][1]) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][2]) |
+                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][3]) << 16);
+          *(uint2*)(yrow + 32 * pt) = make_uint2(lo, hi);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();  // chunk k's tiles and s_H are no longer read
+    stage_store(kn1, tid, pf);
+    dma_B(kn1, lane);
+    load_C(kn1, lane, cf2);
+
+    // ---- StatePassing in fp32 registers; fp16 copy for the next ChunkScan1 ----
+    const float decay = fast_exp2(alast2);
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Hs[j][r] = (k == 0) ? sacc[j][r] : fmaf(decay, Hs[j][r], sacc[j][r]);
+      const int p = 16 * (pt0 + j) + l16;
+      const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][0]) |
+                          ((uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][1]) << 16);
+      const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][2]) |
+                          ((uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][3]) << 16);
+      *(uint2*)&s_H[h_off<NS>(p, 16 * nt_own + 4 * lg)] = make_uint2(lo, hi);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (a.final_state) {
+    const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) {
+      const int p = 16 * (pt0 + j) + l16;
+      const int64_t fo = ((b * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
+      *(float4*)(a.final_state + fo) = make_float4(Hs[j][0], Hs[j][1], Hs[j][2], Hs[j][3]);
+    }
+  }
+}
+
 constexpr size_t kAl = 256;
 size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
@@ -806,7 +1200,14 @@ hipError_t launch_main(FusedArgs fa, hipStream_t st) {
 }  // namespace
 
 bool fused_supported(const Dims& d, int dtype, bool int8) {
-  if (!int8) return false;
+  if (!int8) {
+    if (dtype != DT_F16 || d.P != kP) return false;
+    if (d.N != 64 && d.N != 128) return false;
+    if (d.l != 128 && d.l != 256) return false;
+    if (d.B * d.H > (int64_t)1 << 30) return false;
+    if (d.L * d.H * (int64_t)d.P * 2 >= ((int64_t)1 << 31)) return false;
+    return d.L * d.G * (int64_t)d.N * 2 < ((int64_t)1 << 31);
+  }
   // per-sequence offsets are formed in 32 bits
   if (d.L * d.H * (int64_t)d.P * 2 >= ((int64_t)1 << 31)) return false;
   if (d.B * d.G > 65535 || d.B * d.H > (int64_t)1 << 30) return false;
@@ -817,7 +1218,8 @@ bool fused_supported(const Dims& d, int dtype, bool int8) {
   return true;
 }
 
-size_t fused_workspace_bytes(const Dims& d, bool) {
+size_t fused_workspace_bytes(const Dims& d, bool int8) {
+  if (!int8) return 2 * al((size_t)d.B * d.H * d.c * d.l * sizeof(float));
   const size_t Lp = (size_t)d.c * d.l;
   const size_t qbc = (size_t)d.B * Lp * d.G * d.N;
   const size_t cs = (size_t)d.B * d.H * d.c * d.l * sizeof(float);
@@ -831,6 +1233,20 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
                                 void* ws, int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
                                 int8_t* tap_passed, hipStream_t st) {
   if (!fused_supported(d, dtype, int8)) return hipErrorNotSupported;
+  if (!int8) {
+    const size_t cs = (size_t)d.B * d.H * d.c * d.l * sizeof(float);
+    float* dAcs = (float*)ws;
+    float* lut = (float*)((char*)ws + al(cs));
+    hipError_t e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st);
+    if (e != hipSuccess) return e;
+    const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (float*)final_state, (d.B * d.G) % 8 == 0};
+    const dim3 grid((unsigned)(d.B * d.H));
+    if (d.l == 256 && d.N == 128) hipLaunchKernelGGL((k_fused_f16<256, 128>), grid, dim3(kThreads), 0, st, fa);
+    else if (d.l == 256) hipLaunchKernelGGL((k_fused_f16<256, 64>), grid, dim3(kThreads), 0, st, fa);
+    else if (d.N == 128) hipLaunchKernelGGL((k_fused_f16<128, 128>), grid, dim3(kThreads), 0, st, fa);
+    else hipLaunchKernelGGL((k_fused_f16<128, 64>), grid, dim3(kThreads), 0, st, fa);
+    return hipGetLastError();
+  }
   const size_t Lp = (size_t)d.c * d.l;
   const size_t qbc = (size_t)d.B * Lp * d.G * d.N;
   const size_t cs = (size_t)d.B * d.H * d.c * d.l * sizeof(float);
