@@ -802,19 +802,23 @@ struct FusedFArgs {
   const float* D;
   void* Y;
   float* final_state;
+  int64_t slot0;
   int xcd_map;
 };
 
-template <int LC, int NS>
+// PW = 4: a whole head per workgroup; PW = 2: p tiles 2 ph, 2 ph + 1 of a head
+// (the partial last round, as in the INT8 kernel).
+template <int LC, int NS, int PW>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   typedef _Float16 T;
   typedef FragF<DT_F16> F;
   constexpr int RT = LC / 16;            // row tiles of the chunk
   constexpr int NT = NS / 16;            // n tiles of the state
-  constexpr int PTW = 4 * NT / kWaves;   // p tiles per wave in ChunkState / StatePassing
+  constexpr int PTW = PW * NT / kWaves;  // p tiles per wave in ChunkState / StatePassing
   constexpr int KSF = LC / 32;           // ChunkState K steps (fp16 MFMA, K = 32)
   constexpr int KNF = NS / 32;           // K steps over N
-  constexpr int XI = (LC / 4) * 8;       // staging items (4 rows x 8 p each)
+  constexpr int C8N = 2 * PW;            // 8-column groups of p staged by this workgroup
+  constexpr int XI = (LC / 4) * C8N;     // staging items (4 rows x 8 p each)
   static_assert(XI <= kThreads, "tile split");
 
   __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];  // x^T (xT_pair layout)
@@ -827,7 +831,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   const float* vDt = s_vec + LC;
 
   const Dims& d = a.d;
-  const int64_t slot = blockIdx.x;
+  int64_t slot;
+  int ph = 0;
+  if (PW == 4) {
+    slot = a.slot0 + blockIdx.x;
+  } else if (a.xcd_map) {
+    const int64_t j = blockIdx.x / 8;
+    slot = a.slot0 + (blockIdx.x % 8) + 8 * (j >> 1);
+    ph = (int)(j & 1);
+  } else {
+    slot = a.slot0 + blockIdx.x / 2;
+    ph = blockIdx.x & 1;
+  }
+  const int pt_base = (PW == 4) ? 0 : 2 * ph;
+  const int c8b = 2 * pt_base;  // first 8-column group of p
   int64_t unit, hl;
   if (a.xcd_map) {
     const int64_t j = slot / 8;
@@ -843,7 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   const int w = wave_id();
   const int H = d.H;
   const int nt_own = w % NT;
-  const int pt0 = (w / NT) * PTW;
+  const int pt0 = pt_base + (w / NT) * PTW;
   const float Dh = a.D[h];
   const int tid0 = threadIdx.x;
   float* Vw = s_vw + w * LC;
@@ -865,7 +882,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     const int t0 = kc * LC;
     const int lim = min(LC - 1, (int)d.L - 1 - t0);
     const int it = tid % XI;
-    const int q = it >> 3, c8 = it & 7;
+    const int q = it / C8N, c8 = c8b + it % C8N;
     const T* xk = Xb + (int64_t)t0 * rowX + 8 * c8;
 #pragma unroll
     for (int r = 0; r < 4; ++r) pf.x[r] = *(const uint4*)(xk + (uint32_t)(min(4 * q + r, lim) * rowX));
@@ -878,7 +895,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   const auto stage_store = [&](int kc, int tid, const Pf& pf) {
     const int t0 = kc * LC;
     if (tid < XI) {
-      const int q = tid >> 3, c8 = tid & 7;
+      const int q = tid / C8N, c8 = c8b + tid % C8N;
       uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
 #pragma unroll
       for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
@@ -1020,9 +1037,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-      v4f acc[4];
+      v4f acc[PW];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = v4f{0, 0, 0, 0};
+      for (int jp = 0; jp < PW; ++jp) acc[jp] = v4f{0, 0, 0, 0};
       for (int jA = 0; jA + 1 < i; jA += 2) {
         const int jB = jA + 1;
         v4f cbA = v4f{0, 0, 0, 0}, cbB = v4f{0, 0, 0, 0};
@@ -1044,24 +1061,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
         wf.set(6, cbB[2] * vB.z);
         wf.set(7, cbB[3] * vB.w);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          acc[pt] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * pt + l16, jA >> 1, lg)]), wf, acc[pt]);
+        for (int jp = 0; jp < PW; ++jp)
+          acc[jp] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, jA >> 1, lg)]), wf, acc[jp]);
       }
       const float a_s = vA2[s_row];
       const float us = fast_exp2(a_s - a_ref);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] *= us;
+      for (int jp = 0; jp < PW; ++jp) acc[jp] *= us;
       // ChunkScan1: exp(a_s) sum_n C[s,n] H_{k-1}[p,n]
       if (k > 0) {
         const float eo = fast_exp2(a_s);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
+        for (int jp = 0; jp < PW; ++jp) {
+          const int pt = pt_base + jp;
           v4f acc1 = v4f{0, 0, 0, 0};
 #pragma unroll
           for (int kn = 0; kn < KNF; ++kn)
             acc1 = F::mma(frag16<DT_F16>(&s_H[h_off<NS>(16 * pt + l16, 32 * kn + 8 * lg)]), cr[kn], acc1);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pt][r] = fmaf(acc1[r], eo, acc[pt][r]);
+          for (int r = 0; r < 4; ++r) acc[jp][r] = fmaf(acc1[r], eo, acc[jp][r]);
         }
       }
       {  // diagonal tile (D on its diagonal), sharing its MFMA with tile i - 1 (odd i)
@@ -1099,18 +1117,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
           wf.set(r + 4, hd ? wd[r] : 0.f);
         }
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          acc[pt] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * pt + l16, i >> 1, lg)]), wf, acc[pt]);
+        for (int jp = 0; jp < PW; ++jp)
+          acc[jp] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, i >> 1, lg)]), wf, acc[jp]);
       }
       const int64_t t = t0 + s_row;
       char* yrow = (char*)ybase + (uint32_t)(((int)t * H * kP + 4 * lg) * 2);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
+      for (int jp = 0; jp < PW; ++jp) {
+        const int pt = pt_base + jp;
         if (t < d.L) {
-          const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][0]) |
-                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][1]) << 16);
-          const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][2]) |
-                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[pt][3]) << 16);
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][0]) |
+                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][1]) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][2]) |
+                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][3]) << 16);
           *(uint2*)(yrow + 32 * pt) = make_uint2(lo, hi);
         }
       }
@@ -1171,8 +1190,8 @@ int cu_count() {
 // One workgroup per CU at a time: B*H heads run in ceil(B*H / CUs) rounds. When
 // the last round is at most half full, its heads are split in two p halves so
 // the round spreads over all CUs (each half recomputes the head's CB tiles).
-template <int DT, int LC, int NS>
-hipError_t launch_main(FusedArgs fa, hipStream_t st) {
+template <class K, class Args>
+hipError_t launch_split(Args fa, hipStream_t st) {
   const Dims& d = fa.d;
   const int64_t BH = d.B * d.H;
   const int64_t ncu = cu_count();
@@ -1186,15 +1205,37 @@ hipError_t launch_main(FusedArgs fa, hipStream_t st) {
   if (nfull > 0) {
     fa.slot0 = 0;
     fa.xcd_map = unit_map;
-    const hipError_t e = launch_one<DT, LC, NS, 4>(fa, nfull, st);
+    const hipError_t e = K::template launch<4>(fa, nfull, st);
     if (e != hipSuccess) return e;
   }
   if (nhalf > 0) {
     fa.slot0 = nfull;
     fa.xcd_map = unit_map && nfull % 8 == 0 && nhalf % 8 == 0;
-    return launch_one<DT, LC, NS, 2>(fa, 2 * nhalf, st);
+    return K::template launch<2>(fa, 2 * nhalf, st);
   }
   return hipSuccess;
+}
+
+template <int LC, int NS>
+struct FloatLaunch {
+  template <int PW>
+  static hipError_t launch(const FusedFArgs& fa, int64_t blocks, hipStream_t st) {
+    hipLaunchKernelGGL((k_fused_f16<LC, NS, PW>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int LC, int NS>
+struct Int8Launch {
+  template <int PW>
+  static hipError_t launch(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
+    return launch_one<DT, LC, NS, PW>(fa, blocks, st);
+  }
+};
+
+template <int DT, int LC, int NS>
+hipError_t launch_main(const FusedArgs& fa, hipStream_t st) {
+  return launch_split<Int8Launch<DT, LC, NS>>(fa, st);
 }
 
 }  // namespace
@@ -1239,13 +1280,11 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
     float* lut = (float*)((char*)ws + al(cs));
     hipError_t e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st);
     if (e != hipSuccess) return e;
-    const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (float*)final_state, (d.B * d.G) % 8 == 0};
-    const dim3 grid((unsigned)(d.B * d.H));
-    if (d.l == 256 && d.N == 128) hipLaunchKernelGGL((k_fused_f16<256, 128>), grid, dim3(kThreads), 0, st, fa);
-    else if (d.l == 256) hipLaunchKernelGGL((k_fused_f16<256, 64>), grid, dim3(kThreads), 0, st, fa);
-    else if (d.N == 128) hipLaunchKernelGGL((k_fused_f16<128, 128>), grid, dim3(kThreads), 0, st, fa);
-    else hipLaunchKernelGGL((k_fused_f16<128, 64>), grid, dim3(kThreads), 0, st, fa);
-    return hipGetLastError();
+    const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (float*)final_state, 0, 0};
+    if (d.l == 256 && d.N == 128) return launch_split<FloatLaunch<256, 128>>(fa, st);
+    if (d.l == 256) return launch_split<FloatLaunch<256, 64>>(fa, st);
+    if (d.N == 128) return launch_split<FloatLaunch<128, 128>>(fa, st);
+    return launch_split<FloatLaunch<128, 64>>(fa, st);
   }
   const size_t Lp = (size_t)d.c * d.l;
   const size_t qbc = (size_t)d.B * Lp * d.G * d.N;
