@@ -44,6 +44,12 @@ same way on the GPU side):
   R9  calibration: amax of |B|, |C| per g; of |LUT*x| per (h,p) with the
       float64 LUT; of the float64 chunk states max(|S_k|, |H_k|) per (h,p)
       over (b, k, n), over two calibration sequences.
+  R13 an initial state (chunked-prefill continuation) is the state before
+      chunk 0: the float path starts the recurrence from h_0; the INT8 path
+      takes it as the passed int8 state H_{-1} in the scale s_S, so Eq. 6 and
+      ChunkScan1 apply from chunk 0 on. A sequence split at a chunk boundary
+      and continued from the first part's final state then gives the same
+      integers and outputs as the unsplit sequence.
 
 Where exactness is claimed, float64 matmuls are used on integer-valued
 operands whose partial sums stay below 2^53, so they are exact in any order.
@@ -352,16 +358,22 @@ def requantize_state(s32, M_req, bits: int = 8):
     return saturate(rhaz(fl32(fl32(s32.astype(np.float64)) * m)), qmax_of(bits)).astype(np.int64)
 
 
-def state_passing_int(s8, qdecay, bits: int = 8):
+def state_passing_int(s8, qdecay, bits: int = 8, h_init=None):
     """Eq. 6 of [SSDi8] Key design 2 with S = 2^(bits-1) (R3):
 
     H_0 = S8_0;  H_k = sat(S8_k + RSH(Q(Decay_k) * H_{k-1})).
-    s8 [b,c,H,P,N], qdecay [b,H,c]. Returns passed states [b,c,H,P,N].
+    With an initial state (R13), H_{-1} = h_init and the update applies from
+    k = 0 as well. s8 [b,c,H,P,N], qdecay [b,H,c], h_init [b,H,P,N] int.
+    Returns passed states [b,c,H,P,N].
     """
     qm = qmax_of(bits)
     out = np.empty_like(s8)
     c = s8.shape[1]
-    hk = s8[:, 0].astype(np.int64)
+    if h_init is None:
+        hk = s8[:, 0].astype(np.int64)
+    else:
+        qd0 = qdecay[:, :, 0].astype(np.int64)[:, :, None, None]
+        hk = saturate(s8[:, 0] + rounding_shift(qd0 * np.asarray(h_init, np.int64), bits - 1), qm)
     out[:, 0] = hk
     for k in range(1, c):
         qd = qdecay[:, :, k].astype(np.int64)[:, :, None, None]
@@ -383,10 +395,11 @@ def chunk_bmm_int(qC, qB, chunk: int):
     return np.matmul(qc, qb).astype(np.int64)
 
 
-def chunk_scan_int8(x, dt, a, qC, cb, passed, D, scales: dict, chunk: int):
+def chunk_scan_int8(x, dt, a, qC, cb, passed, D, scales: dict, chunk: int, h_init=None):
     """ChunkScan1 + ChunkScan2 + D skip of the INT8 path ([SSDi8] Key design 2).
 
-    Scan1: Y_off[s,p] = exp(a_s) s_C s_S[h,p] sum_n Q(C)[s,n] H_{k-1}[p,n] (k >= 1).
+    Scan1: Y_off[s,p] = exp(a_s) s_C s_S[h,p] sum_n Q(C)[s,n] H_{k-1}[p,n] (k >= 1;
+    for k = 0 with H_{-1} = h_init when an initial state is given, R13).
     Scan2: Y_diag[s,p] = sum_{s'<=s} CB[s,s'] s_C s_B exp(a_s - a_s') dt_s' x[s',p].
     Evaluated in float64. a [b,H,c,l] float64. Returns y [b,L,H,P].
     """
@@ -409,8 +422,8 @@ def chunk_scan_int8(x, dt, a, qC, cb, passed, D, scales: dict, chunk: int):
     for k in range(c):
         ak = a[:, :, k, :]                                                # [b,H,l]
         xs = xp[:, k].transpose(0, 2, 1, 3)                               # [b,H,l,P]
-        if k > 0:
-            prev = passed[:, k - 1].astype(np.float64)                    # [b,H,P,N]
+        if k > 0 or h_init is not None:
+            prev = (passed[:, k - 1] if k > 0 else np.asarray(h_init)).astype(np.float64)  # [b,H,P,N]
             qcs = qc[:, k][:, :, g].transpose(0, 2, 1, 3)                 # [b,H,l,N]
             acc1 = np.matmul(qcs, prev.transpose(0, 1, 3, 2))             # [b,H,l,P] exact
             y_off = acc1 * (np.exp(ak)[..., None] * (s_C[:, None] * s_S)[None, :, None, :])
@@ -425,10 +438,12 @@ def chunk_scan_int8(x, dt, a, qC, cb, passed, D, scales: dict, chunk: int):
     return y.reshape(b, c * l, H, P)[:, :L]
 
 
-def forward_int8(x, dt, A, B, C, D, scales: dict, chunk: int) -> dict:
+def forward_int8(x, dt, A, B, C, D, scales: dict, chunk: int, h_init=None) -> dict:
     """The whole persistent-INT8 SSD forward, step by step ([SSDi8] Overall framework).
 
     Inputs are float64 widenings of the stored tensors; A, D float32 values.
+    h_init: optional int8-valued initial state [b,H,P,N] in the state scale s_S
+    (R13: the passed state before chunk 0, e.g. a previous call's final state).
     Returns every intermediate: qB, qC, cumsum dict, qxs, s32, s8 (local chunk
     states), passed (states after StatePassing), cb, y.
     """
@@ -441,9 +456,9 @@ def forward_int8(x, dt, A, B, C, D, scales: dict, chunk: int) -> dict:
     qxs = quantize_xs(x, cs["lut"], scales["inv_X"], chunk, bits)
     s32 = chunk_state_int(qxs, qB, chunk)
     s8 = requantize_state(s32, scales["M_req"], bits)
-    passed = state_passing_int(s8, cs["qdecay"], bits)
+    passed = state_passing_int(s8, cs["qdecay"], bits, h_init)
     cb = chunk_bmm_int(qC, qB, chunk)
-    y = chunk_scan_int8(x, dt, cs["a"], qC, cb, passed, D, scales, chunk)
+    y = chunk_scan_int8(x, dt, cs["a"], qC, cb, passed, D, scales, chunk, h_init)
     assert H % G == 0
     return {"qB": qB, "qC": qC, "cumsum": cs, "qxs": qxs, "s32": s32, "s8": s8,
             "passed": passed, "cb": cb, "y": y}

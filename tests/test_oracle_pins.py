@@ -12,6 +12,7 @@ import pytest
 
 from mamba_ssd_chunked_amd import synth
 from oracle import ssd_oracle as O
+from tests import _helpers as H
 
 
 def _rand_inputs(rng, b, L, H, P, N, G, dt_scale=0.1):
@@ -311,3 +312,57 @@ def test_constants_match_the_page():
     assert O.rounding_shift(np.array([g["S"]["value"] * 5]), g["shift_k"]["value"])[0] == 5
     cs = O.chunk_cumsum(np.zeros((1, 4, 1)), np.array([-1.0], np.float32), 4)
     assert cs["qdecay"].max() == g["S"]["value"]      # decay 1 maps to S
+
+
+# R13: continuation from an initial state. Splitting a sequence at a chunk
+# boundary and continuing from the first part's final state reproduces the
+# unsplit run: exactly for the INT8 integers, to rounding for the float path.
+def test_int8_continuation_at_a_chunk_boundary():
+    w = synth.WORKLOADS[0]
+    c = H.make_case(w)
+    e = c.ev64
+    full = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales, w.chunk)
+    L1 = 2 * w.chunk
+    sl = lambda v, a_, b_: v[:, a_:b_]  # noqa: E731
+    p1 = O.forward_int8(sl(e["x"], 0, L1), sl(e["dt"], 0, L1), c.consts["A"], sl(e["B"], 0, L1),
+                        sl(e["C"], 0, L1), c.consts["D"], c.scales, w.chunk)
+    p2 = O.forward_int8(sl(e["x"], L1, None), sl(e["dt"], L1, None), c.consts["A"], sl(e["B"], L1, None),
+                        sl(e["C"], L1, None), c.consts["D"], c.scales, w.chunk, h_init=p1["passed"][:, -1])
+    k1 = L1 // w.chunk
+    assert np.array_equal(np.concatenate([p1["passed"], p2["passed"]], axis=1), full["passed"])
+    assert np.array_equal(p2["s8"], full["s8"][:, k1:])
+    y = np.concatenate([p1["y"], p2["y"]], axis=1)
+    assert np.allclose(y, full["y"], rtol=0, atol=1e-12 * np.abs(full["y"]).max())
+
+
+def test_int8_zero_initial_state_is_no_initial_state():
+    w = synth.WORKLOADS[0]
+    c = H.make_case(w)
+    e = c.ev64
+    r0 = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales, w.chunk)
+    z = np.zeros((w.batch, w.nheads, w.headdim, w.dstate), np.int64)
+    r1 = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales, w.chunk, h_init=z)
+    assert np.array_equal(r0["passed"], r1["passed"]) and np.array_equal(r0["y"], r1["y"])
+
+
+def test_int8_initial_state_enters_eq6_and_scan1():
+    """With B = 0 the local states vanish: H_0 = RSH(Q(Decay_0) h_init), and
+    ChunkScan1 of chunk 0 reads h_init itself."""
+    w = synth.WORKLOADS[0]
+    c = H.make_case(w)
+    e = dict(c.ev64)
+    e["B"] = np.zeros_like(e["B"])
+    rng = np.random.default_rng(5)
+    h0 = rng.integers(-127, 128, size=(w.batch, w.nheads, w.headdim, w.dstate))
+    r = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales, w.chunk, h_init=h0)
+    qd0 = r["cumsum"]["qdecay"][:, :, 0][:, :, None, None]
+    assert np.array_equal(r["passed"][:, 0], O.saturate(O.rounding_shift(qd0 * h0, 7), 127))
+    # chunk 0 output = Scan1 on h_init + the diagonal part, which is D x alone when B = 0
+    l = w.chunk
+    a0 = r["cumsum"]["a"][:, :, 0, :]                                     # [b,H,l]
+    g = O.head_group(w.nheads, w.ngroups)
+    qc = r["qC"][:, :l][:, :, g].astype(np.float64)                      # [b,l,H,N]
+    acc = np.einsum("blhn,bhpn->blhp", qc, h0.astype(np.float64))
+    sc = np.asarray(c.scales["s_C"], np.float64)[g][None, None, :, None] * np.asarray(c.scales["s_S"], np.float64)[None, None]
+    y0 = acc * np.exp(a0).transpose(0, 2, 1)[..., None] * sc + c.consts["D"].astype(np.float64)[None, None, :, None] * e["x"][:, :l]
+    assert np.allclose(r["y"][:, :l], y0, rtol=1e-12, atol=1e-12 * np.abs(y0).max())
