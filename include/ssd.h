@@ -141,10 +141,15 @@ int ssd_chunk_state(const ssd_shape* shape, int path, const void* X, const float
  * over chunks. INT8: H_0 = S_0, H_k = sat127(S_k + RSH7(qdecay_k * H_{k-1}))
  * with RSH7(v) = sign(v) * ((|v| + 64) >> 7); qdecay required, dAcs unused.
  * FLOAT: H_k = exp(dAcs[k, l-1]) * H_{k-1} + S_k in fp32; qdecay unused.
+ * initial_state (may be NULL): the state before chunk 0, [B,H,P,N], int8 in
+ * the state scale s_S (INT8) or fp32 (FLOAT); when given, the update applies
+ * from k = 0 with H_{-1} = initial_state (a previous call's final_state
+ * continues that sequence).
  * On return slot k holds H_k (the state after chunk k). final_state (may be
  * NULL) receives H_{c-1}. */
 int ssd_state_passing(const ssd_shape* shape, int path, void* states, const float* dAcs,
-                      const uint8_t* qdecay, void* final_state, void* stream);
+                      const uint8_t* qdecay, const void* initial_state, void* final_state,
+                      void* stream);
 
 /* ChunkBMM ("Key design 2": reuses the INT8 B and C):
  * CB[b,k,g,i,j] = sum_n Cq[k*l+i, g, n] * Bq[k*l+j, g, n] for j <= i, 0 above
@@ -160,21 +165,27 @@ int ssd_chunk_bmm(const ssd_shape* shape, int path, const void* Cq, const void* 
  *   Scan2: Y_diag[s,p] = sum_{s'<=s} CB[s,s'] exp(dAcs_s - dAcs_s') dt_s' x[s',p]
  *     (INT8: CB int32 with its dequant s_C * s_B folded into the LUT).
  *   Y = Y_off + Y_diag + D[h] x, stored in shape->dtype.
- * states are the passed states (slot k-1 feeds chunk k). */
+ * states are the passed states (slot k-1 feeds chunk k); initial_state (may
+ * be NULL, same type and layout as in ssd_state_passing) feeds chunk 0. */
 int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* dt,
                    const float* dAcs, const void* Cq, const void* CB, const void* states,
-                   const float* D, const ssd_scales* scales, void* Y, void* stream);
+                   const void* initial_state, const float* D, const ssd_scales* scales, void* Y,
+                   void* stream);
 
 /* The whole SSD forward in one call ("Overall framework": all modules).
  * B, C, X, dt in shape->dtype; Y in shape->dtype. INT8 needs scales.
+ * initial_state (may be NULL): the state before the first position, int8 in
+ * the state scale (INT8) or fp32 (FLOAT) [B,H,P,N]; passing a previous call's
+ * final_state continues that sequence (exactly, when the previous call's
+ * length was a multiple of the chunk size).
  * final_state (may be NULL): int8 (INT8) or fp32 (FLOAT) [B,H,P,N].
  * workspace: device memory of at least ssd_workspace_bytes(shape, path) bytes
  * (may be NULL when that is 0). taps: INT8 only, may be NULL. The integer
  * intermediates are bit-identical to those of the module calls above. */
 int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
                 const float* A, const void* B, const void* C, const float* D,
-                const ssd_scales* scales, void* Y, void* final_state, void* workspace,
-                size_t workspace_bytes, const ssd_taps* taps, void* stream);
+                const ssd_scales* scales, void* Y, const void* initial_state, void* final_state,
+                void* workspace, size_t workspace_bytes, const ssd_taps* taps, void* stream);
 
 /* Workspace bytes ssd_forward needs (0 for an invalid shape). Host only. */
 size_t ssd_workspace_bytes(const ssd_shape* shape, int path);

@@ -79,10 +79,10 @@ def _load() -> ctypes.CDLL:
         "ssd_chunk_cumsum": [SP, P, P, P, P, P, P],
         "ssd_chunk_state": [SP, ctypes.c_int, P, P, P, ctypes.POINTER(SsdScales), P,
                             ctypes.POINTER(SsdTaps), P],
-        "ssd_state_passing": [SP, ctypes.c_int, P, P, P, P, P],
+        "ssd_state_passing": [SP, ctypes.c_int, P, P, P, P, P, P],
         "ssd_chunk_bmm": [SP, ctypes.c_int, P, P, P, P],
-        "ssd_chunk_scan": [SP, ctypes.c_int, P, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P],
-        "ssd_forward": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P, P,
+        "ssd_chunk_scan": [SP, ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P],
+        "ssd_forward": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P, P, P,
                         ctypes.c_size_t, ctypes.POINTER(SsdTaps), P],
         "ssd_calibrate_amax": [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P],
         "ssd_scales_from_amax": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P],
@@ -207,10 +207,10 @@ def ssd_chunk_state(shape, path, X, lut, Bq, scales, states, taps=None, stream=N
 
 
 def ssd_state_passing(shape, path, states, dAcs=None, qdecay=None, final_state=None,
-                      stream=None):
+                      stream=None, initial_state=None):
     _check("ssd_state_passing", LIB.ssd_state_passing(ctypes.byref(shape), path, _p(states),
-                                                      _p(dAcs), _p(qdecay), _p(final_state),
-                                                      _stream(stream)))
+                                                      _p(dAcs), _p(qdecay), _p(initial_state),
+                                                      _p(final_state), _stream(stream)))
 
 
 def ssd_chunk_bmm(shape, path, Cq, Bq, CB, stream=None):
@@ -218,10 +218,12 @@ def ssd_chunk_bmm(shape, path, Cq, Bq, CB, stream=None):
                                               _stream(stream)))
 
 
-def ssd_chunk_scan(shape, path, X, dt, dAcs, Cq, CB, states, D, scales, Y, stream=None):
+def ssd_chunk_scan(shape, path, X, dt, dAcs, Cq, CB, states, D, scales, Y, stream=None,
+                   initial_state=None):
     _check("ssd_chunk_scan", LIB.ssd_chunk_scan(ctypes.byref(shape), path, _p(X), _p(dt),
-                                                _p(dAcs), _p(Cq), _p(CB), _p(states), _p(D),
-                                                _scales(scales), _p(Y), _stream(stream)))
+                                                _p(dAcs), _p(Cq), _p(CB), _p(states),
+                                                _p(initial_state), _p(D), _scales(scales), _p(Y),
+                                                _stream(stream)))
 
 
 def ssd_workspace_bytes(shape, path) -> int:
@@ -229,15 +231,17 @@ def ssd_workspace_bytes(shape, path) -> int:
 
 
 def ssd_forward(shape, path, X, dt, A, B, C, D, scales, Y, final_state=None, workspace=None,
-                taps=None, stream=None):
-    """Whole forward. ``workspace`` (a uint8 device tensor) is allocated here if None."""
+                taps=None, stream=None, initial_state=None):
+    """Whole forward. ``workspace`` (a uint8 device tensor) is allocated here if None.
+    ``initial_state`` continues a sequence from a previous call's final state."""
     need = ssd_workspace_bytes(shape, path)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ssd_forward", LIB.ssd_forward(ctypes.byref(shape), path, _p(X), _p(dt), _p(A), _p(B),
                                           _p(C), _p(D), _scales(scales), _p(Y),
-                                          _p(final_state), _p(workspace), wsb, _taps(taps),
+                                          _p(initial_state), _p(final_state), _p(workspace), wsb,
+                                          _taps(taps),
                                           _stream(stream)))
     return workspace
 

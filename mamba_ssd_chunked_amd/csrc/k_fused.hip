@@ -167,6 +167,7 @@ struct FusedArgs {
   const float* D;
   ScalePtrs sc;
   void* Y;
+  const int8_t* init;  // optional initial state [B,H,P,N] (the passed state before chunk 0)
   int8_t* final_state;
   int8_t* tap_qxs;
   int32_t* tap_s32;
@@ -479,8 +480,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   float* Vw = s_vw + w * LC;
 
   uint32_t H8[PTW];  // passed state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
+  const bool has_init = a.init != nullptr;
+  {
+    const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
 #pragma unroll
-  for (int j = 0; j < PTW; ++j) H8[j] = 0;
+    for (int j = 0; j < PTW; ++j) {
+      const int p = 16 * (pt0 + j) + l16;
+      H8[j] = has_init ? *(const uint32_t*)(a.init + ((b * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg)
+                       : 0u;
+      // the initial state feeds chunk 0's ChunkScan1
+      if (has_init) *(uint32_t*)&H8l[b_off<NS>(p, 16 * nt_own + 4 * lg)] = H8[j];
+    }
+  }
 
   const LaneOff<LC, NS, PW> lo = lane_offsets<DT, LC, NS, PW>(d, tid0, 2 * pt_base);
   // Q(C) rows (B operand over N) of this wave's two row tiles {w, 15 - w}
@@ -636,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       for (int jp = 0; jp < PW; ++jp) acc[jp] *= us;
       // ChunkScan1 (inter-chunk), transposed: H8 rows x Q(C) rows, scaled by
       // exp(a_s) s_C s_S[p] and added to the output accumulator
-      if (k > 0) {
+      if (k > 0 || has_init) {
         const float eo = fast_exp2(a_s) * sC;
 #pragma unroll
         for (int jp = 0; jp < PW; ++jp) {
@@ -725,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       const int p = 16 * (pt0 + j) + l16;
-      if (k == 0) {
+      if (k == 0 && !has_init) {
         H8[j] = S8[j];
       } else {
         int o[4];
@@ -801,6 +812,7 @@ struct FusedFArgs {
   const float* lut;
   const float* D;
   void* Y;
+  const float* init;  // optional initial state [B,H,P,N] fp32
   float* final_state;
   int64_t slot0;
   int xcd_map;
@@ -969,10 +981,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   };
 
   float Hs[PTW][4];  // fp32 state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
+  const bool has_init = a.init != nullptr;
+  {
+    const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
 #pragma unroll
-  for (int j = 0; j < PTW; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Hs[j][r] = 0.f;
+    for (int j = 0; j < PTW; ++j) {
+      const int p = 16 * (pt0 + j) + l16;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (has_init) v = *(const float4*)(a.init + ((b * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg);
+      Hs[j][0] = v.x;
+      Hs[j][1] = v.y;
+      Hs[j][2] = v.z;
+      Hs[j][3] = v.w;
+      if (has_init) {  // fp16 copy for chunk 0's ChunkScan1
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)v.x) |
+                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v.y) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)v.z) |
+                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v.w) << 16);
+        *(uint2*)&s_H[h_off<NS>(p, 16 * nt_own + 4 * lg)] = make_uint2(lo, hi);
+      }
+    }
+  }
 
   uint4 cf2[2][KNF];
   {  // chunk 0
@@ -1068,8 +1097,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       const float us = fast_exp2(a_s - a_ref);
 #pragma unroll
       for (int jp = 0; jp < PW; ++jp) acc[jp] *= us;
-      // ChunkScan1: exp(a_s) sum_n C[s,n] H_{k-1}[p,n]
-      if (k > 0) {
+      // ChunkScan1: exp(a_s) sum_n C[s,n] H_{k-1}[p,n] (H_{-1}: the initial state)
+      if (k > 0 || has_init) {
         const float eo = fast_exp2(a_s);
 #pragma unroll
         for (int jp = 0; jp < PW; ++jp) {
@@ -1145,7 +1174,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Hs[j][r] = (k == 0) ? sacc[j][r] : fmaf(decay, Hs[j][r], sacc[j][r]);
+      for (int r = 0; r < 4; ++r) Hs[j][r] = (k == 0 && !has_init) ? sacc[j][r] : fmaf(decay, Hs[j][r], sacc[j][r]);
       const int p = 16 * (pt0 + j) + l16;
       const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][0]) |
                           ((uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][1]) << 16);
@@ -1270,8 +1299,9 @@ size_t fused_workspace_bytes(const Dims& d, bool int8) {
 
 hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void* X,
                                 const void* dt, const float* A, const void* B, const void* C,
-                                const float* D, const ScalePtrs& sc, void* Y, void* final_state,
-                                void* ws, int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
+                                const float* D, const ScalePtrs& sc, void* Y,
+                                const void* initial_state, void* final_state, void* ws,
+                                int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
                                 int8_t* tap_passed, hipStream_t st) {
   if (!fused_supported(d, dtype, int8)) return hipErrorNotSupported;
   if (!int8) {
@@ -1280,7 +1310,8 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
     float* lut = (float*)((char*)ws + al(cs));
     hipError_t e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st);
     if (e != hipSuccess) return e;
-    const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (float*)final_state, 0, 0};
+    const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (const float*)initial_state,
+                        (float*)final_state, 0, 0};
     if (d.l == 256 && d.N == 128) return launch_split<FloatLaunch<256, 128>>(fa, st);
     if (d.l == 256) return launch_split<FloatLaunch<256, 64>>(fa, st);
     if (d.N == 128) return launch_split<FloatLaunch<128, 128>>(fa, st);
@@ -1310,8 +1341,8 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
   e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, qd, st);
   if (e != hipSuccess) return e;
 
-  const FusedArgs fa{d, X, dt, qB, qC, dAcs, lut, qd, D, sc, Y, (int8_t*)final_state,
-                     tap_qxs, tap_s32, tap_s8, tap_passed, 0, 0};
+  const FusedArgs fa{d, X, dt, qB, qC, dAcs, lut, qd, D, sc, Y, (const int8_t*)initial_state,
+                     (int8_t*)final_state, tap_qxs, tap_s32, tap_s8, tap_passed, 0, 0};
   if (dtype == DT_F16) {
     if (d.l == 256 && d.N == 128) return launch_main<DT_F16, 256, 128>(fa, st);
     if (d.l == 256 && d.N == 64) return launch_main<DT_F16, 256, 64>(fa, st);

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(Dims d, const void* __restr
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_state_passing_i8(Dims d, int8_t* __restrict__ states,
                                                           const uint8_t* __restrict__ qdecay,
+                                                          const int8_t* __restrict__ init,
                                                           int8_t* __restrict__ final_state) {
   const int64_t per_b = (int64_t)d.H * d.P * d.N / 4;  // dwords per (b, chunk) slot
   const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -270,9 +271,10 @@ __global__ __launch_bounds__(256) void k_state_passing_i8(Dims d, int8_t* __rest
   uint32_t* st = (uint32_t*)states;
   const int64_t slot = per_b;  // dwords per chunk slot
   const int64_t base = b * d.c * slot + r;
-  uint32_t prev = st[base];
+  // without an initial state H_0 = S_0; with one, Eq. 6 applies from chunk 0
+  uint32_t prev = init ? ((const uint32_t*)init)[b * per_b + r] : st[base];
   const uint8_t* qd = qdecay + (b * d.H + h) * d.c;
-  for (int k0 = 1; k0 < d.c; k0 += 8) {
+  for (int k0 = init ? 0 : 1; k0 < d.c; k0 += 8) {
     uint32_t v[8];
     int q[8];
 #pragma unroll
@@ -301,6 +303,7 @@ __global__ __launch_bounds__(256) void k_state_passing_i8(Dims d, int8_t* __rest
 
 __global__ __launch_bounds__(256) void k_state_passing_f(Dims d, float* __restrict__ states,
                                                          const float* __restrict__ dAcs,
+                                                         const float* __restrict__ init,
                                                          float* __restrict__ final_state) {
   const int64_t per_b = (int64_t)d.H * d.P * d.N / 4;  // float4 per slot
   const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -310,9 +313,9 @@ __global__ __launch_bounds__(256) void k_state_passing_f(Dims d, float* __restri
   float4* st = (float4*)states;
   const int64_t slot = per_b;
   const int64_t base = b * d.c * slot + r;
-  float4 prev = st[base];
+  float4 prev = init ? ((const float4*)init)[b * per_b + r] : st[base];
   const float* da = dAcs + (b * d.H + h) * (int64_t)d.c * d.l;
-  for (int k0 = 1; k0 < d.c; k0 += 8) {
+  for (int k0 = init ? 0 : 1; k0 < d.c; k0 += 8) {
     float4 v[8];
     float dec[8];
 #pragma unroll
@@ -399,6 +402,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
                                                     const void* __restrict__ Cq,
                                                     const void* __restrict__ CB,
                                                     const void* __restrict__ states,
+                                                    const void* __restrict__ init,
                                                     const float* __restrict__ D,
                                                     const float* __restrict__ s_C,
                                                     const float* __restrict__ s_B,
@@ -472,12 +476,15 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
         }
       }
     }
-    // ChunkScan1 (inter-chunk), k >= 1
+    // ChunkScan1 (inter-chunk): the passed state of chunk k - 1, or the initial
+    // state for chunk 0 when one is given
     v4f yoff[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) yoff[pt] = v4f{0, 0, 0, 0};
-    if (k > 0) {
-      const int64_t st0 = ((b * d.c + (k - 1)) * H + h) * (int64_t)P * N;
+    const bool has_prev = k > 0 || init != nullptr;
+    const void* const sprev = k > 0 ? states : init;
+    if (has_prev) {
+      const int64_t st0 = (k > 0 ? ((b * d.c + (k - 1)) * H + h) : (b * H + h)) * (int64_t)P * N;
       const int64_t ts = t0 + s;
       if constexpr (INT8) {
         v4i acc1[4];
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
             if (pt < PT) {
               v4i hb = {0, 0, 0, 0};
               if (n < N)
-                hb = *(const v4i*)((const int8_t*)states + st0 + (int64_t)(pt * 16 + (lane & 15)) * N + n);
+                hb = *(const v4i*)((const int8_t*)sprev + st0 + (int64_t)(pt * 16 + (lane & 15)) * N + n);
               acc1[pt] = mma_i8(a, hb, acc1[pt]);
             }
           }
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
               FragC<DT> hb;
               hb.zero();
               if (n < N) {
-                const float* hp = (const float*)states + st0 + (int64_t)(pt * 16 + (lane & 15)) * N + n;
+                const float* hp = (const float*)sprev + st0 + (int64_t)(pt * 16 + (lane & 15)) * N + n;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hb.set(e, hp[e]);
               }
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
           const int p = pt * 16 + (lane & 15);
           const float xv = (float)Store<DT>::to_f(sxT[p][sr]);
           float y = acc[pt][r] + Dh * xv;
-          if (k > 0) {
+          if (has_prev) {
             float f = expf(sdA[sr]);
             if (INT8) f *= s_C[g] * s_S[h * P + p];
             y += yoff[pt][r] * f;
@@ -596,15 +603,16 @@ hipError_t launch_chunk_state(const Dims& d, int dtype, bool int8, const void* X
 }
 
 hipError_t launch_state_passing(const Dims& d, bool int8, void* states, const float* dAcs,
-                                const uint8_t* qdecay, void* final_state, hipStream_t st) {
+                                const uint8_t* qdecay, const void* init, void* final_state,
+                                hipStream_t st) {
   const int64_t n = d.B * (int64_t)d.H * d.P * d.N / 4;
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (int8) {
     hipLaunchKernelGGL(k_state_passing_i8, dim3(grid), dim3(256), 0, st, d, (int8_t*)states,
-                       qdecay, (int8_t*)final_state);
+                       qdecay, (const int8_t*)init, (int8_t*)final_state);
   } else {
     hipLaunchKernelGGL(k_state_passing_f, dim3(grid), dim3(256), 0, st, d, (float*)states, dAcs,
-                       (float*)final_state);
+                       (const float*)init, (float*)final_state);
   }
   return hipGetLastError();
 }
@@ -624,15 +632,16 @@ hipError_t launch_chunk_bmm(const Dims& d, int dtype, bool int8, const void* Cq,
 
 hipError_t launch_chunk_scan(const Dims& d, int dtype, bool int8, const void* X, const void* dt,
                              const float* dAcs, const void* Cq, const void* CB,
-                             const void* states, const float* D, const float* s_C,
-                             const float* s_B, const float* s_S, void* Y, hipStream_t st) {
+                             const void* states, const void* init, const float* D,
+                             const float* s_C, const float* s_B, const float* s_S, void* Y,
+                             hipStream_t st) {
   const dim3 grid(d.H, d.c, (unsigned)d.B);
   if (int8) {
-#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, true>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, D, s_C, s_B, s_S, Y)
+#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, true>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, init, D, s_C, s_B, s_S, Y)
     SSD_DISPATCH_DT(dtype, L_)
 #undef L_
   } else {
-#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, false>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, D, s_C, s_B, s_S, Y)
+#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, false>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, init, D, s_C, s_B, s_S, Y)
     SSD_DISPATCH_DT(dtype, L_)
 #undef L_
   }

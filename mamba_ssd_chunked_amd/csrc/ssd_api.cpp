@@ -206,7 +206,8 @@ int ssd_chunk_state(const ssd_shape* shape, int path, const void* X, const float
 }
 
 int ssd_state_passing(const ssd_shape* shape, int path, void* states, const float* dAcs,
-                      const uint8_t* qdecay, void* final_state, void* stream) {
+                      const uint8_t* qdecay, const void* initial_state, void* final_state,
+                      void* stream) {
   Dims d;
   bool empty;
   int rc = check_shape(shape, &d, &empty);
@@ -214,10 +215,10 @@ int ssd_state_passing(const ssd_shape* shape, int path, void* states, const floa
   if ((rc = check_path(path))) return rc;
   const bool i8 = path == SSD_PATH_INT8;
   if ((rc = check_ptrs({states, i8 ? (const void*)qdecay : (const void*)dAcs}))) return rc;
-  if ((rc = check_opt({final_state}))) return rc;
+  if ((rc = check_opt({initial_state, final_state}))) return rc;
   if (empty) return SSD_OK;
-  return hip_status(ssd::launch_state_passing(d, i8, states, dAcs, qdecay, final_state,
-                                              (hipStream_t)stream));
+  return hip_status(ssd::launch_state_passing(d, i8, states, dAcs, qdecay, initial_state,
+                                              final_state, (hipStream_t)stream));
 }
 
 int ssd_chunk_bmm(const ssd_shape* shape, int path, const void* Cq, const void* Bq, void* CB,
@@ -235,7 +236,8 @@ int ssd_chunk_bmm(const ssd_shape* shape, int path, const void* Cq, const void* 
 
 int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* dt,
                    const float* dAcs, const void* Cq, const void* CB, const void* states,
-                   const float* D, const ssd_scales* scales, void* Y, void* stream) {
+                   const void* initial_state, const float* D, const ssd_scales* scales, void* Y,
+                   void* stream) {
   Dims d;
   bool empty;
   int rc = check_shape(shape, &d, &empty);
@@ -243,9 +245,11 @@ int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* 
   if ((rc = check_path(path))) return rc;
   const bool i8 = path == SSD_PATH_INT8;
   if ((rc = check_ptrs({X, dt, dAcs, Cq, CB, states, D, Y}))) return rc;
+  if ((rc = check_opt({initial_state}))) return rc;
   if (i8 && (rc = check_scales(scales))) return rc;
   if (empty) return SSD_OK;
-  return hip_status(ssd::launch_chunk_scan(d, shape->dtype, i8, X, dt, dAcs, Cq, CB, states, D,
+  return hip_status(ssd::launch_chunk_scan(d, shape->dtype, i8, X, dt, dAcs, Cq, CB, states,
+                                           initial_state, D,
                                            i8 ? scales->s_C : nullptr,
                                            i8 ? scales->s_B : nullptr,
                                            i8 ? scales->s_S : nullptr, Y, (hipStream_t)stream));
@@ -263,8 +267,8 @@ size_t ssd_workspace_bytes(const ssd_shape* shape, int path) {
 
 int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt, const float* A,
                 const void* B, const void* C, const float* D, const ssd_scales* scales, void* Y,
-                void* final_state, void* workspace, size_t workspace_bytes,
-                const ssd_taps* taps, void* stream) {
+                const void* initial_state, void* final_state, void* workspace,
+                size_t workspace_bytes, const ssd_taps* taps, void* stream) {
   Dims d;
   bool empty;
   int rc = check_shape(shape, &d, &empty);
@@ -277,7 +281,7 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
   int32_t* ts = (i8 && taps) ? taps->s32 : nullptr;
   int8_t* t8 = (i8 && taps) ? taps->s8_local : nullptr;
   int8_t* tp = (i8 && taps) ? taps->passed : nullptr;
-  if ((rc = check_opt({final_state, workspace, tq, ts, t8, tp}))) return rc;
+  if ((rc = check_opt({initial_state, final_state, workspace, tq, ts, t8, tp}))) return rc;
   if (empty) return SSD_OK;
   const size_t need = ssd_workspace_bytes(shape, path);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_E_WORKSPACE;
@@ -286,8 +290,8 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
   const ssd::ScalePtrs sp = scale_ptrs(scales);
 
   if (ssd::fused_supported(d, dtype, i8)) {
-    hipError_t e = ssd::launch_forward_fused(d, dtype, i8, X, dt, A, B, C, D, sp, Y, final_state,
-                                             workspace, tq, ts, t8, tp, st);
+    hipError_t e = ssd::launch_forward_fused(d, dtype, i8, X, dt, A, B, C, D, sp, Y, initial_state,
+                                             final_state, workspace, tq, ts, t8, tp, st);
     return hip_status(e);
   }
 
@@ -314,11 +318,12 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
     if ((e = ssd::launch_chunk_state(d, dtype, true, X, lut, qB, sp.inv_X, sp.M_req, states, tq, ts, st)))
       return SSD_E_HIP;
     if (t8 && (e = hipMemcpyAsync(t8, states, z.st_i8, hipMemcpyDeviceToDevice, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_state_passing(d, true, states, dAcs, qd, final_state, st))) return SSD_E_HIP;
+    if ((e = ssd::launch_state_passing(d, true, states, dAcs, qd, initial_state, final_state, st)))
+      return SSD_E_HIP;
     if (tp && (e = hipMemcpyAsync(tp, states, z.st_i8, hipMemcpyDeviceToDevice, st))) return SSD_E_HIP;
     if ((e = ssd::launch_chunk_bmm(d, dtype, true, qC, qB, CB, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_chunk_scan(d, dtype, true, X, dt, dAcs, qC, CB, states, D, sp.s_C, sp.s_B,
-                                    sp.s_S, Y, st)))
+    if ((e = ssd::launch_chunk_scan(d, dtype, true, X, dt, dAcs, qC, CB, states, initial_state, D,
+                                    sp.s_C, sp.s_B, sp.s_S, Y, st)))
       return SSD_E_HIP;
   } else {
     float* states = (float*)w;
@@ -326,11 +331,11 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
     if ((e = ssd::launch_chunk_state(d, dtype, false, X, lut, B, nullptr, nullptr, states, nullptr,
                                      nullptr, st)))
       return SSD_E_HIP;
-    if ((e = ssd::launch_state_passing(d, false, states, dAcs, nullptr, final_state, st)))
+    if ((e = ssd::launch_state_passing(d, false, states, dAcs, nullptr, initial_state, final_state, st)))
       return SSD_E_HIP;
     if ((e = ssd::launch_chunk_bmm(d, dtype, false, C, B, CB, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_chunk_scan(d, dtype, false, X, dt, dAcs, C, CB, states, D, nullptr,
-                                    nullptr, nullptr, Y, st)))
+    if ((e = ssd::launch_chunk_scan(d, dtype, false, X, dt, dAcs, C, CB, states, initial_state, D,
+                                    nullptr, nullptr, nullptr, Y, st)))
       return SSD_E_HIP;
   }
   return SSD_OK;
@@ -376,7 +381,7 @@ int ssd_calibrate_amax(const ssd_shape* shape, const void* X, const void* dt, co
                               nullptr, st))
     return SSD_E_HIP;
   if (ssd::launch_amax_states(d, states, amS, st)) return SSD_E_HIP;
-  if (ssd::launch_state_passing(d, false, states, dAcs, nullptr, nullptr, st)) return SSD_E_HIP;
+  if (ssd::launch_state_passing(d, false, states, dAcs, nullptr, nullptr, nullptr, st)) return SSD_E_HIP;
   if (ssd::launch_amax_states(d, states, amS, st)) return SSD_E_HIP;
   return SSD_OK;
 }

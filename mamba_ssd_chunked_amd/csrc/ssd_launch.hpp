@@ -32,20 +32,23 @@ hipError_t launch_chunk_state(const Dims& d, int dtype, bool int8, const void* X
                               const float* M_req, void* states, int8_t* tap_qxs,
                               int32_t* tap_s32, hipStream_t st);
 hipError_t launch_state_passing(const Dims& d, bool int8, void* states, const float* dAcs,
-                                const uint8_t* qdecay, void* final_state, hipStream_t st);
+                                const uint8_t* qdecay, const void* init, void* final_state,
+                                hipStream_t st);
 hipError_t launch_chunk_bmm(const Dims& d, int dtype, bool int8, const void* Cq,
                             const void* Bq, void* CB, hipStream_t st);
 hipError_t launch_chunk_scan(const Dims& d, int dtype, bool int8, const void* X, const void* dt,
                              const float* dAcs, const void* Cq, const void* CB,
-                             const void* states, const float* D, const float* s_C,
-                             const float* s_B, const float* s_S, void* Y, hipStream_t st);
+                             const void* states, const void* init, const float* D,
+                             const float* s_C, const float* s_B, const float* s_S, void* Y,
+                             hipStream_t st);
 
 // Fused forward (defined in k_fused.hip). Returns hipErrorNotSupported when the
 // fused kernels do not cover the shape; the caller then composes the modules.
 hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void* X,
                                 const void* dt, const float* A, const void* B, const void* C,
-                                const float* D, const ScalePtrs& sc, void* Y, void* final_state,
-                                void* ws, int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
+                                const float* D, const ScalePtrs& sc, void* Y,
+                                const void* initial_state, void* final_state, void* ws,
+                                int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
                                 int8_t* tap_passed, hipStream_t st);
 size_t fused_workspace_bytes(const Dims& d, bool int8);
 bool fused_supported(const Dims& d, int dtype, bool int8);

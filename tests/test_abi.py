@@ -53,13 +53,13 @@ def fwd(sh, path=L.SSD_PATH_FLOAT, scales=None, ws=_UNSET, wsb=_UNSET, **ptr):
     """ssd_forward on fake addresses. Every use expects a validation error (or the
     empty no-op), so nothing is ever enqueued; a call that would pass validation
     is refused here instead of being sent to the library."""
-    p = dict(X=A16, dt=A16, A=A16, B=A16, C=A16, D=A16, Y=A16, final=None)
+    p = dict(X=A16, dt=A16, A=A16, B=A16, C=A16, D=A16, Y=A16, init=None, final=None)
     p.update(ptr)
     need = L.LIB.ssd_workspace_bytes(ctypes.byref(sh), path)
     ws = A16 if ws is _UNSET else ws
     wsb = need if wsb is _UNSET else wsb
     args = (ctypes.byref(sh), path, p["X"], p["dt"], p["A"], p["B"], p["C"], p["D"], scales,
-            p["Y"], p["final"], ws, wsb, None, None)
+            p["Y"], p["init"], p["final"], ws, wsb, None, None)
     return L.LIB.ssd_forward(*args)
 
 
@@ -93,7 +93,9 @@ def test_null_and_alignment():
     assert fwd(sh, Y=None) == L.SSD_E_NULL
     assert fwd(sh, B=MIS) == L.SSD_E_ALIGN
     assert fwd(sh, final=MIS) == L.SSD_E_ALIGN
-    assert L.LIB.ssd_forward(None, 0, A16, A16, A16, A16, A16, A16, None, A16, None, A16, 0, None, None) == L.SSD_E_NULL
+    assert fwd(sh, init=MIS) == L.SSD_E_ALIGN
+    assert L.LIB.ssd_forward(None, 0, A16, A16, A16, A16, A16, A16, None, A16, None, None, A16, 0, None,
+                             None) == L.SSD_E_NULL
 
 
 def test_bad_path_and_missing_scales():
@@ -133,10 +135,12 @@ def test_module_calls_validate():
     assert L.LIB.ssd_chunk_cumsum(b(sh), A16, A16, A16, MIS, None, None) == L.SSD_E_ALIGN
     assert L.LIB.ssd_chunk_state(b(sh), 1, A16, A16, A16, None, A16, None, None) == L.SSD_E_NULL
     assert L.LIB.ssd_chunk_state(b(sh), 3, A16, A16, A16, None, A16, None, None) == L.SSD_E_UNSUPPORTED
-    assert L.LIB.ssd_state_passing(b(sh), 1, A16, None, None, None, None) == L.SSD_E_NULL
-    assert L.LIB.ssd_state_passing(b(sh), 0, A16, None, None, None, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_state_passing(b(sh), 1, A16, None, None, None, None, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_state_passing(b(sh), 0, A16, None, None, None, None, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_state_passing(b(sh), 1, A16, None, A16, MIS, None, None) == L.SSD_E_ALIGN
     assert L.LIB.ssd_chunk_bmm(b(shape(chunk=48)), 1, A16, A16, A16, None) == L.SSD_E_UNSUPPORTED
-    assert L.LIB.ssd_chunk_scan(b(sh), 1, A16, A16, A16, A16, A16, A16, A16, None, A16, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_chunk_scan(b(sh), 1, A16, A16, A16, A16, A16, A16, None, A16, None, A16, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_chunk_scan(b(sh), 0, A16, A16, A16, A16, A16, A16, MIS, A16, None, A16, None) == L.SSD_E_ALIGN
     assert L.LIB.ssd_calibrate_amax(b(sh), A16, A16, A16, A16, A16, A16, A16, 0, None) == L.SSD_E_WORKSPACE
 
 

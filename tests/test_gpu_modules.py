@@ -275,3 +275,81 @@ def test_calibrate_amax(gpu_lib, name):
     asx = a[2 * G + HP:].reshape(ref["S"].shape)
     tol = {"fp32": 1e-4, "fp16": 2e-2, "bf16": 5e-2}[w.dtype]
     assert np.all(np.abs(asx - ref["S"]) <= tol * ref["S"] + 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Initial state (chunked-prefill continuation)
+# ---------------------------------------------------------------------------
+def _init_int8(w, seed=7):
+    rng = np.random.default_rng(seed)
+    return rng.integers(-127, 128, size=(w.batch, w.nheads, w.headdim, w.dstate)).astype(np.int8)
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_forward_int8_initial_state(gpu_lib, name):
+    L = gpu_lib
+    torch, c, _, _, d, sh, sc = _setup(L, name)
+    w, e = c.w, c.ev64
+    h0 = _init_int8(w)
+    r = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales, w.chunk,
+                       h_init=h0.astype(np.int64))
+    y = torch.empty_like(d["x"])
+    fin = torch.empty(h0.shape, dtype=torch.int8, device="cuda")
+    stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
+    taps = {"passed": torch.empty(stshape, dtype=torch.int8, device="cuda")}
+    L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], sc, y,
+                  final_state=fin, taps=taps, initial_state=_i8(torch, h0))
+    torch.cuda.synchronize()
+    assert np.array_equal(taps["passed"].cpu().numpy(), r["passed"])
+    assert np.array_equal(fin.cpu().numpy(), r["passed"][:, -1])
+    assert H.chan_err(H.f64(y), r["y"], w.dtype) <= 5e-2
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_forward_float_initial_state(gpu_lib, name):
+    L = gpu_lib
+    torch, c, _, (yf, hf, _, _), d, sh, sc = _setup(L, name)
+    w, e = c.w, c.ev64
+    h0 = hf[:, ::-1].copy()  # a state of realistic size (the heads' final states, reordered)
+    yr, hr = O.chunked(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], w.chunk, h0=h0)[:2]
+    y = torch.empty_like(d["x"])
+    fin = torch.empty(h0.shape, dtype=torch.float32, device="cuda")
+    L.ssd_forward(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None, y,
+                  final_state=fin, initial_state=_dev(h0, np.float32))
+    torch.cuda.synchronize()
+    assert H.chan_err(H.f64(y), yr, w.dtype) <= 2e-2
+    fg = fin.cpu().numpy().astype(np.float64)
+    assert np.abs(fg - hr).max() <= 2e-1 * np.sqrt(np.mean(hr * hr))
+
+
+@pytest.mark.parametrize("path", ["int8", "float"])
+@pytest.mark.parametrize("name", ["f16_ragged", "bf16_n64_l128", "w0"])
+def test_continuation_at_a_chunk_boundary(gpu_lib, name, path):
+    """Two calls (the second starting from the first's final state) give bitwise
+    the outputs and final state of one call over the whole sequence."""
+    L = gpu_lib
+    torch, c, _, _, d, sh, sc = _setup(L, name)
+    w = c.w
+    i8 = path == "int8"
+    p = L.SSD_PATH_INT8 if i8 else L.SSD_PATH_FLOAT
+    scales = sc if i8 else None
+    fdt = torch.int8 if i8 else torch.float32
+    fshape = (w.batch, w.nheads, w.headdim, w.dstate)
+    y = torch.empty_like(d["x"])
+    fin = torch.empty(fshape, dtype=fdt, device="cuda")
+    L.ssd_forward(sh, p, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], scales, y, final_state=fin)
+    L1 = w.chunk
+    part = lambda t, a_, b_: t[:, a_:b_].contiguous()  # noqa: E731
+    sh1 = H.shape_of(L, w, seqlen=L1)
+    sh2 = H.shape_of(L, w, seqlen=w.seqlen - L1)
+    y1 = torch.empty_like(part(d["x"], 0, L1))
+    y2 = torch.empty_like(part(d["x"], L1, None))
+    f1 = torch.empty(fshape, dtype=fdt, device="cuda")
+    f2 = torch.empty(fshape, dtype=fdt, device="cuda")
+    L.ssd_forward(sh1, p, part(d["x"], 0, L1), part(d["dt"], 0, L1), d["A"], part(d["B"], 0, L1),
+                  part(d["C"], 0, L1), d["D"], scales, y1, final_state=f1)
+    L.ssd_forward(sh2, p, part(d["x"], L1, None), part(d["dt"], L1, None), d["A"], part(d["B"], L1, None),
+                  part(d["C"], L1, None), d["D"], scales, y2, final_state=f2, initial_state=f1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], dim=1), y)
+    assert torch.equal(f2, fin)
