@@ -50,6 +50,10 @@ same way on the GPU side):
       ChunkScan1 apply from chunk 0 on. A sequence split at a chunk boundary
       and continued from the first part's final state then gives the same
       integers and outputs as the unsplit sequence.
+  R14 the single-token decode step is the INT8 method with a chunk of one
+      position (LUT_state = dt, Q(Decay) from exp(dt A)), updating the
+      persistent int8 state with Eq. 6; its output reads the state before the
+      step (ChunkScan1) plus the position's own diagonal term (ChunkScan2).
 
 Where exactness is claimed, float64 matmuls are used on integer-valued
 operands whose partial sums stay below 2^53, so they are exact in any order.
@@ -469,3 +473,67 @@ def rel_max_err(y, ref) -> float:
     ref = np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     return float(np.max(np.abs(np.asarray(y, np.float64) - ref)) / rms)
+
+
+# ---------------------------------------------------------------------------
+# Single-token decode step (the recurrent mode of the same layer)
+# ---------------------------------------------------------------------------
+
+
+def decode_step_float(x, dt, A, B, C, D, h):
+    """[SSM] one step of the recurrence: h' = exp(dt A) h + dt x (x) B,
+    y = C . h' + D x. x [b,H,P], dt [b,H], B/C [b,G,N], h [b,H,P,N] (float64).
+    Returns (y [b,H,P], h')."""
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    A = np.asarray(A, np.float64)
+    D = np.asarray(D, np.float64)
+    H = x.shape[1]
+    g = head_group(H, np.asarray(B).shape[1])
+    Bh = np.asarray(B, np.float64)[:, g]                                 # [b,H,N]
+    Ch = np.asarray(C, np.float64)[:, g]
+    hn = np.exp(dt * A)[..., None, None] * np.asarray(h, np.float64) + \
+        (dt[..., None] * x)[..., None] * Bh[:, :, None, :]
+    y = np.einsum("bhpn,bhn->bhp", hn, Ch) + D[None, :, None] * x
+    return y, hn
+
+
+def decode_step_int8(x, dt, A, B, C, D, scales: dict, h):
+    """One token of the persistent-INT8 path ([SSDi8] Key design 2 with a chunk
+    of one position, R14): Q(Decay) = min(S, RHAZ(S exp(dt A))) decided in
+    float64 with dt A exact; LUT_state = dt, Q(Xs) = sat(RHAZ(fl32(fl32(dt x) inv_X)));
+    S8 = requant(Q(Xs) Q(B)); h' = sat(S8 + RSH(Q(Decay) h)) (Eq. 6);
+    y = exp(dt A) s_C s_S sum_n Q(C) h + (Q(C).Q(B)) s_C s_B dt x + D x (ChunkScan1 on
+    the state before the step, ChunkScan2 on its single diagonal entry).
+    x [b,H,P], dt [b,H], B/C [b,G,N] float64 widenings; h [b,H,P,N] int.
+    Returns dict(y, h (int64), qdecay, qxs, s8)."""
+    bits = int(scales.get("bits", 8))
+    qm = qmax_of(bits)
+    S = float(1 << (bits - 1))
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    H = x.shape[1]
+    G = np.asarray(B).shape[1]
+    g = head_group(H, G)
+    qB = quantize(B, np.asarray(scales["inv_B"], np.float64)[None, :, None], bits)   # [b,G,N]
+    qC = quantize(C, np.asarray(scales["inv_C"], np.float64)[None, :, None], bits)
+    a = dt * np.asarray(A, np.float64)[None, :]                                     # exact
+    qdecay = np.minimum(rhaz(np.exp(a) * S), S).astype(np.int64)                     # [b,H]
+    lut32 = fl32(dt)                                                                # exp(0) = 1
+    qxs = saturate(rhaz(fl32(fl32(lut32[..., None] * x) * np.asarray(scales["inv_X"], np.float64)[None])),
+                   qm).astype(np.int64)                                             # [b,H,P]
+    s32 = qxs[..., None] * qB[:, g][:, :, None, :]                                   # [b,H,P,N]
+    m = np.asarray(scales["M_req"], np.float64).reshape(H, -1)[None, :, :, None]
+    s8 = saturate(rhaz(fl32(fl32(s32.astype(np.float64)) * m)), qm).astype(np.int64)
+    h = np.asarray(h, np.int64)
+    hn = saturate(s8 + rounding_shift(qdecay[..., None, None] * h, bits - 1), qm)
+    s_C = np.asarray(scales["s_C"], np.float64)[g]
+    s_B = np.asarray(scales["s_B"], np.float64)[g]
+    s_S = np.asarray(scales["s_S"], np.float64)
+    qCh = qC[:, g].astype(np.float64)                                              # [b,H,N]
+    y_off = np.einsum("bhpn,bhn->bhp", h.astype(np.float64), qCh) * \
+        (np.exp(a)[..., None] * (s_C[:, None] * s_S)[None])
+    cb = np.einsum("bhn,bhn->bh", qCh, qB[:, g].astype(np.float64))                 # exact
+    y_diag = (cb * s_C[None] * s_B[None] * dt)[..., None] * x
+    y = y_off + y_diag + np.asarray(D, np.float64)[None, :, None] * x
+    return {"y": y, "h": hn, "qdecay": qdecay, "qxs": qxs, "s8": s8}

@@ -366,3 +366,42 @@ def test_int8_initial_state_enters_eq6_and_scan1():
     sc = np.asarray(c.scales["s_C"], np.float64)[g][None, None, :, None] * np.asarray(c.scales["s_S"], np.float64)[None, None]
     y0 = acc * np.exp(a0).transpose(0, 2, 1)[..., None] * sc + c.consts["D"].astype(np.float64)[None, None, :, None] * e["x"][:, :l]
     assert np.allclose(r["y"][:, :l], y0, rtol=1e-12, atol=1e-12 * np.abs(y0).max())
+
+
+# R14: the decode step is the chunked method with a single position.
+def _token(e, t):
+    return {k: v[:, t] for k, v in e.items()}
+
+
+def test_int8_decode_equals_one_position_forward():
+    w = synth.WORKLOADS[0]
+    c = H.make_case(w)
+    e = c.ev64
+    rng = np.random.default_rng(3)
+    h0 = rng.integers(-127, 128, size=(w.batch, w.nheads, w.headdim, w.dstate))
+    for t in (0, 5, 200):
+        tok = _token(e, t)
+        dec = O.decode_step_int8(tok["x"], tok["dt"], c.consts["A"], tok["B"], tok["C"], c.consts["D"],
+                                 c.scales, h0)
+        one = {k: v[:, t:t + 1] for k, v in e.items()}
+        fwd = O.forward_int8(one["x"], one["dt"], c.consts["A"], one["B"], one["C"], c.consts["D"],
+                             c.scales, w.chunk, h_init=h0)
+        assert np.array_equal(dec["h"], fwd["passed"][:, 0])
+        assert np.array_equal(dec["qxs"], fwd["qxs"][:, 0])
+        assert np.array_equal(dec["qdecay"], fwd["cumsum"]["qdecay"][:, :, 0])
+        assert np.allclose(dec["y"], fwd["y"][:, 0], rtol=1e-12, atol=1e-12 * np.abs(dec["y"]).max())
+
+
+def test_float_decode_steps_equal_the_recurrence():
+    w = synth.WORKLOADS[0]
+    c = H.make_case(w)
+    e = c.ev64
+    T = 40
+    yr, hr = O.recurrence(e["x"][:, :T], e["dt"][:, :T], c.consts["A"], e["B"][:, :T], e["C"][:, :T],
+                          c.consts["D"])
+    h = np.zeros_like(hr)
+    for t in range(T):
+        tok = _token(e, t)
+        y, h = O.decode_step_float(tok["x"], tok["dt"], c.consts["A"], tok["B"], tok["C"], c.consts["D"], h)
+        assert np.allclose(y, yr[:, t], rtol=1e-12, atol=1e-12 * np.abs(yr).max())
+    assert np.allclose(h, hr, rtol=1e-12, atol=1e-12 * np.abs(hr).max())
