@@ -97,6 +97,61 @@ def measured_traffic(workload: str, path: str):
     return rec.get("bytes_per_call")
 
 
+DECODE_BATCHES = (8, 1024)   # the layer's batch (latency) and a serving batch (bandwidth)
+
+
+def decode_bytes_per_step(w, batch: int, int8: bool) -> int:
+    """One decode position: the state read and written once (int8, or fp32 on
+    the float path), x, dt, B, C read and y written once."""
+    esz = {"fp32": 4, "fp16": 2, "bf16": 2}[w.dtype]
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    state = (1 if int8 else 4) * 2 * H * P * N
+    return batch * (state + esz * (2 * H * P + H + 2 * G * N))
+
+
+def bench_decode(torch, np, L, synth, w, consts, scales, steps, warmup) -> dict:
+    """ssd_decode_step at each batch of DECODE_BATCHES on both paths; inputs
+    resident in HBM, the state updated in place each step."""
+    A = torch.from_numpy(consts["A"]).cuda()
+    D = torch.from_numpy(consts["D"]).cuda()
+    out = {}
+    for batch in DECODE_BATCHES:
+        ev = synth.evaluation_batch(w, consts, batch=batch, seqlen=1)
+        dev = {k: torch.from_numpy(np.ascontiguousarray(v[:, 0])).cuda() for k, v in ev.items()}
+        h8 = torch.from_numpy(synth.int8_state(w, batch)).cuda()
+        sh = L.make_shape(batch, 1, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+        y = torch.empty_like(dev["x"])
+        for path_name in ("int8", "float"):
+            i8 = path_name == "int8"
+            path = L.SSD_PATH_INT8 if i8 else L.SSD_PATH_FLOAT
+            st = h8 if i8 else h8.float()
+            sc = scales if i8 else None
+
+            def step():
+                L.ssd_decode_step(sh, path, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, sc, st, y)
+
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            nbytes = decode_bytes_per_step(w, batch, i8)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[f"{path_name}_b{batch}"] = {
+                "us_per_step": us, "tokens_per_s": batch / (us * 1e-6),
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes}}
+            del st
+        del h8, dev, y
+        torch.cuda.empty_cache()
+    return out
+
+
 CPU_SEQUENCES = 2   # sequences of the batch the CPU baseline runs (a bounded sample)
 
 
@@ -165,6 +220,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paths", default="int8,float")
+    ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the SSD layer runs on a single MI355X here "
@@ -259,6 +315,8 @@ def main() -> int:
         "device": device_info(torch),
         "copy_gbs": copy_gbs,
     }
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, np, L, synth, w, consts, scales, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, consts, ev)
     print(json.dumps(out), flush=True)

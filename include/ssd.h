@@ -187,6 +187,29 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
                 const ssd_scales* scales, void* Y, const void* initial_state, void* final_state,
                 void* workspace, size_t workspace_bytes, const ssd_taps* taps, void* stream);
 
+/* Single-token decode step: the recurrent form of the same block, one
+ * position per call, continuing from a forward's final_state or an earlier
+ * step's state. shape->seqlen must be 1 (or batch 0); shape->chunk is not
+ * used but must be a supported value; batch * nheads <= 2^24.
+ * X [B,H,P], dt [B,H], B, C [B,G,N] in shape->dtype; Y [B,H,P] in
+ * shape->dtype; state [B,H,P,N] int8 (INT8, in the state scale s_S) or fp32
+ * (FLOAT), read and overwritten in place with the state after the position.
+ *   FLOAT: h' = exp(dt A) h + dt x B,  y = C . h' + D x  (fp32).
+ *   INT8 ("Key design 2", Eq. 6 with a chunk of one position; the chunk
+ *   algebra of "Overall framework" reduces to this for l = 1):
+ *     Q(Decay) = min(128, RHAZ(128 exp(dt A))) decided in float64,
+ *     Q(Xs) = sat127(RHAZ(fl32(fl32(dt x) inv_X))), S8 = sat127(RHAZ(fl32(
+ *     fl32(Q(Xs) Q(B)) M_req))), h' = sat127(S8 + RSH7(Q(Decay) h)),
+ *     y = exp(dt A) s_C s_S (Q(C) . h) + (Q(C) . Q(B)) s_C s_B dt x + D x
+ *     with h the state before the position (ChunkScan1) and the single
+ *     diagonal term of ChunkScan2. The state integers equal those of
+ *     ssd_forward over a chunk of one position. Needs scales.
+ * The state is 16-byte aligned; X, dt, B, C, Y need only element alignment
+ * but are checked for 16 bytes like every other buffer. */
+int ssd_decode_step(const ssd_shape* shape, int path, const void* X, const void* dt,
+                    const float* A, const void* B, const void* C, const float* D,
+                    const ssd_scales* scales, void* state, void* Y, void* stream);
+
 /* Workspace bytes ssd_forward needs (0 for an invalid shape). Host only. */
 size_t ssd_workspace_bytes(const ssd_shape* shape, int path);
 

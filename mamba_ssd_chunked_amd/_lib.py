@@ -84,6 +84,8 @@ def _load() -> ctypes.CDLL:
         "ssd_chunk_scan": [SP, ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P],
         "ssd_forward": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P, P, P,
                         ctypes.c_size_t, ctypes.POINTER(SsdTaps), P],
+        "ssd_decode_step": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P,
+                            P],
         "ssd_calibrate_amax": [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P],
         "ssd_scales_from_amax": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P],
     }
@@ -105,7 +107,8 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTED = ("ssd_quantize_bc", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-            "ssd_chunk_bmm", "ssd_chunk_scan", "ssd_forward", "ssd_workspace_bytes",
+            "ssd_chunk_bmm", "ssd_chunk_scan", "ssd_forward", "ssd_decode_step",
+            "ssd_workspace_bytes",
             "ssd_calibrate_amax", "ssd_calibrate_workspace_bytes", "ssd_scales_from_amax",
             "ssd_status_string")
 
@@ -244,6 +247,14 @@ def ssd_forward(shape, path, X, dt, A, B, C, D, scales, Y, final_state=None, wor
                                           _taps(taps),
                                           _stream(stream)))
     return workspace
+
+
+def ssd_decode_step(shape, path, X, dt, A, B, C, D, scales, state, Y, stream=None):
+    """One position: ``state`` [B,H,P,N] (int8 or fp32) is updated in place,
+    Y [B,H,P] receives the output. ``shape.seqlen`` must be 1."""
+    _check("ssd_decode_step", LIB.ssd_decode_step(ctypes.byref(shape), path, _p(X), _p(dt), _p(A),
+                                                  _p(B), _p(C), _p(D), _scales(scales),
+                                                  _p(state), _p(Y), _stream(stream)))
 
 
 def ssd_calibrate_workspace_bytes(shape) -> int:

@@ -39,35 +39,6 @@ constexpr int kThreads = 512;  // eight waves
 constexpr int kWaves = kThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Saturating int8 quantiser with round half away from zero. After the clamp,
-// trunc(c + copysign(0.5 - 2^-25, c)) equals RHAZ(c) for every float32 c
-// (checked exhaustively over all 2^32 bit patterns in the test-suite).
-__device__ __forceinline__ float q8_pre(float v) {
-  const float c = fminf(fmaxf(v, -127.f), 127.f);
-  return c + __builtin_copysignf(0.49999997f, c);
-}
-__device__ __forceinline__ int q8(float v) { return (int)q8_pre(v); }
-
-// Four such codes packed into one dword (byte j from v_j). The float -> int
-// conversion writes its low byte straight into the destination byte (SDWA
-// dst_sel), so the packing costs no extra instructions.
-__device__ __forceinline__ uint32_t q8x4(float v0, float v1, float v2, float v3) {
-  uint32_t d = (uint32_t)q8(v0);
-  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
-      : "+v"(d) : "v"(q8_pre(v1)));
-  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
-      : "+v"(d) : "v"(q8_pre(v2)));
-  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
-      : "+v"(d) : "v"(q8_pre(v3)));
-  return d;
-}
-
-// Eq. 6 rounding shift sign(v) * ((|v| + 64) >> 7) in arithmetic-shift form:
-// (v + 64 + (v >> 31)) >> 7 (equal for every |v| <= 128 * 127; tested).
-__device__ __forceinline__ int rsh7_fast(int v) { return (v + 64 + (v >> 31)) >> 7; }
-
-__device__ __forceinline__ int sat127(int v) { return min(max(v, -127), 127); }
-
 // 2^x with the hardware transcendental (arguments here are <= 0; results that
 // would be denormal flush to 0, far below anything that reaches the output).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

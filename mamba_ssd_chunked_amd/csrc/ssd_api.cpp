@@ -341,6 +341,25 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
   return SSD_OK;
 }
 
+int ssd_decode_step(const ssd_shape* shape, int path, const void* X, const void* dt,
+                    const float* A, const void* B, const void* C, const float* D,
+                    const ssd_scales* scales, void* state, void* Y, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_path(path))) return rc;
+  if (d.B > 0 && d.L != 1) return SSD_E_SHAPE;
+  // one wave per (batch, head): keep the grid's thread count below 2^32
+  if (d.B * (int64_t)d.H > (int64_t)1 << 24) return SSD_E_SHAPE;
+  const bool i8 = path == SSD_PATH_INT8;
+  if ((rc = check_ptrs({X, dt, A, B, C, D, state, Y}))) return rc;
+  if (i8 && (rc = check_scales(scales))) return rc;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_decode_step(d, shape->dtype, i8, X, dt, A, B, C, D,
+                                            scale_ptrs(scales), state, Y, (hipStream_t)stream));
+}
+
 size_t ssd_calibrate_workspace_bytes(const ssd_shape* shape) {
   Dims d;
   bool empty;

@@ -165,6 +165,13 @@ def evaluation_batch(w: Workload, consts: dict | None = None, batch: int | None 
     return sequence(w, 3, batch, consts, seqlen, seed_base)
 
 
+def int8_state(w: Workload, batch: int, seed: int | None = None) -> np.ndarray:
+    """A persistent INT8 state [batch, H, P, N], uniform over [-127, 127]
+    (seeded; role 4 of the workload unless a seed is given)."""
+    rng = np.random.Generator(np.random.PCG64(1000 * w.wid + 4 if seed is None else seed))
+    return rng.integers(-127, 128, size=(batch, w.nheads, w.headdim, w.dstate), dtype=np.int8)
+
+
 def as_f64(seq: dict, dtype: str) -> dict:
     """Widen every stored tensor of a sequence dict to float64 (exact)."""
     return {k: to_f64(v, dtype) for k, v in seq.items()}

@@ -161,3 +161,29 @@ def test_scales_from_amax_matches_the_oracle_rule():
     for k in ("s_B", "s_C", "inv_B", "inv_C", "s_X", "inv_X", "s_S", "M_req"):
         assert np.array_equal(got[k], ref[k].reshape(-1)), k
     assert L.LIB.ssd_scales_from_amax(2, 5, 16, amax.ctypes.data, got["s_B"].ctypes.data) == L.SSD_E_SHAPE
+
+
+def test_decode_step_validates():
+    b = ctypes.byref
+    sc = L.SsdScales(*([A16] * 7))
+
+    def dec(sh, path=L.SSD_PATH_INT8, scales=b(sc), **ptr):
+        p = dict(X=A16, dt=A16, A=A16, B=A16, C=A16, D=A16, state=A16, Y=A16)
+        p.update(ptr)
+        return L.LIB.ssd_decode_step(b(sh), path, p["X"], p["dt"], p["A"], p["B"], p["C"], p["D"],
+                                     scales, p["state"], p["Y"], None)
+
+    one = shape(seqlen=1)
+    # only one position per call
+    assert dec(shape(seqlen=2)) == L.SSD_E_SHAPE
+    assert dec(shape(seqlen=0, batch=3)) == L.SSD_E_SHAPE
+    # the one-wave-per-(batch, head) grid bound
+    assert dec(shape(seqlen=1, batch=65535, nheads=512, ngroups=1)) == L.SSD_E_SHAPE
+    assert dec(one, state=None) == L.SSD_E_NULL
+    assert dec(one, Y=None) == L.SSD_E_NULL
+    assert dec(one, state=MIS) == L.SSD_E_ALIGN
+    assert dec(one, scales=None) == L.SSD_E_NULL
+    assert dec(one, path=4) == L.SSD_E_UNSUPPORTED
+    assert dec(shape(seqlen=1, dstate=256)) == L.SSD_E_UNSUPPORTED
+    # empty batch: nothing to do
+    assert dec(shape(seqlen=1, batch=0)) == L.SSD_OK
