@@ -111,7 +111,9 @@ def decode_bytes_per_step(w, batch: int, int8: bool) -> int:
 
 def bench_decode(torch, np, L, synth, w, consts, scales, steps, warmup) -> dict:
     """ssd_decode_step at each batch of DECODE_BATCHES on both paths; inputs
-    resident in HBM, the state updated in place each step."""
+    resident in HBM, the state updated in place each step. us_per_step comes
+    from `steps` steps replayed as one HIP graph; eager_us_per_step from the
+    same steps called one by one from Python (host-bound at small batch)."""
     A = torch.from_numpy(consts["A"]).cuda()
     D = torch.from_numpy(consts["D"]).cuda()
     out = {}
@@ -139,11 +141,25 @@ def bench_decode(torch, np, L, synth, w, consts, scales, steps, warmup) -> dict:
                 step()
             e1.record()
             torch.cuda.synchronize()
+            eager_us = e0.elapsed_time(e1) * 1e3 / steps
+            # the same steps captured in one HIP graph: a serving loop's launch
+            # path, without the host cost of one Python call per step
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(steps):
+                    step()
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / steps
+            del g
             nbytes = decode_bytes_per_step(w, batch, i8)
             gbs = nbytes / (us * 1e-6) / 1e9
             out[f"{path_name}_b{batch}"] = {
-                "us_per_step": us, "tokens_per_s": batch / (us * 1e-6),
+                "us_per_step": us, "eager_us_per_step": eager_us, "tokens_per_s": batch / (us * 1e-6),
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes}}
             del st

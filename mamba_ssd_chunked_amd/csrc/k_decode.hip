@@ -14,7 +14,10 @@
 // rows of N values; lane L owns the 16-byte column slice L % R of rows
 // L / R + i * (64 / R), R = 16-byte slices per row, so every load and store
 // instruction of the wave covers contiguous memory. The row sums of C . h
-// reduce over the R lanes of a row with LDS swizzles (no LDS traffic).
+// reduce over the R lanes of a row with LDS swizzles (no LDS traffic). The
+// state is touched once per step, so its loads and stores carry the
+// non-temporal hint (streaming past the caches measured faster on the
+// in-place read-then-write pattern).
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -70,55 +73,124 @@ __device__ __forceinline__ uint32_t perm_pack4(int a, int b, int c, int d) {
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// LDS of one wave: per-position vectors of its head.
+// Packed 16-bit helpers of the Eq. 6 update (two state elements per lane op).
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// Two int8 codes from float values prepared by q8_pre, as int16 halves of one
+// dword: the second conversion writes its low 16 bits into the high half.
+__device__ __forceinline__ v2s cvt_pair(float c0, float c1) {
+  uint32_t d = (uint32_t)(int)c0;
+  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+      : "+v"(d) : "v"(c1));
+  return __builtin_bit_cast(v2s, d);
+}
+
+// Two signed bytes of w (picked by the permute selector into bits 15:8 and
+// 31:24) as sign-extended int16 halves.
+__device__ __forceinline__ v2s unpack_pair(uint32_t w, uint32_t sel) {
+  return __builtin_bit_cast(v2s, __builtin_amdgcn_perm(w, w, sel)) >> (short)8;
+}
+
+// RSH7(qd h) = (qd h + 64 + [qd h < 0 ? -1 : 0]) >> 7 per half. qd >= 0, so the
+// sign of h stands for the sign of the product (a zero product rounds to 0
+// either way); |qd h| <= 128 * 127 fits int16.
+__device__ __forceinline__ v2s rsh7_pair(v2s qd, v2s h) {
+  return (v2s)(qd * h + (short)64 + (h >> (short)15)) >> (short)7;
+}
+
+__device__ __forceinline__ v2s sat127_pair(v2s v) {
+  return __builtin_elementwise_min(__builtin_elementwise_max(v, (v2s){-127, -127}), (v2s){127, 127});
+}
+
+// Low bytes of the four int16 halves of (lo, hi) as one dword.
+__device__ __forceinline__ uint32_t pack_pairs(v2s lo, v2s hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                               0x06040200u);
+}
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// LDS of one wave: the per-position vectors of its head.
 template <int P, int NS>
-struct DecLds {
-  float b[NS];   // INT8: float(Q(B)); FLOAT: B
-  float c[NS];   // FLOAT: C
-  int8_t qc[NS]; // INT8: Q(C)
-  float x[P];    // x
-  int qx[P];     // INT8: Q(Xs)
+struct DecLdsI8 {
+  float b[NS];     // float(Q(B))
+  int8_t qc[NS];   // Q(C)
+  float4 rv[P];    // per state row p: float(Q(Xs)), M_req, x, exp(dt A) s_C s_S
+};
+template <int P, int NS>
+struct DecLdsF {
+  float b[NS];     // B
+  float c[NS];     // C
+  float x[P];      // x
 };
 
 // ---------------------------------------------------------------------------
 // INT8 step
 // ---------------------------------------------------------------------------
-template <int DT, int P, int NS>
+template <int DT, int P, int NS, int SPLIT>
 __global__ __launch_bounds__(256) void k_decode_i8(DecodeArgs a) {
   constexpr int R = NS / 16;        // 16-byte slices per state row
   constexpr int RPI = kWave / R;    // rows per wave pass
-  constexpr int ITER = (P + RPI - 1) / RPI;
-  __shared__ __attribute__((aligned(16))) DecLds<P, NS> lds[kDecWaves];
+  constexpr int ITER = (P + RPI - 1) / RPI / SPLIT;  // passes of this wave
+  __shared__ __attribute__((aligned(16))) DecLdsI8<P, NS> lds[kDecWaves];
 
   const int w = wave_id(), lane = lane_id();
-  const int64_t unit = (int64_t)blockIdx.x * kDecWaves + w;
-  if (unit >= a.units) return;  // uniform per wave
-  DecLds<P, NS>& L = lds[w];
+  const int64_t item = (int64_t)blockIdx.x * kDecWaves + w;
+  if (item >= a.units * SPLIT) return;  // uniform per wave
+  const int64_t unit = item / SPLIT;
+  // the state rows are loaded first: they depend on nothing else
+  const int col = lane % R, r0 = lane / R + (int)(item % SPLIT) * ITER * RPI;
+  v4u* st = (v4u*)((int8_t*)a.state + unit * (int64_t)P * NS);
+  v4u hv[ITER];
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int row = r0 + i * RPI;
+    if (row < P) hv[i] = __builtin_nontemporal_load(&st[row * R + col]);
+  }
+  DecLdsI8<P, NS>& L = lds[w];
   const int64_t b = unit / a.H;
   const int h = (int)(unit % a.H);
   const int g = h / a.hpg;
 
+  // every per-position input is loaded before any of it is used, so the
+  // prologue costs one memory round trip
+  constexpr int NB = (NS + kWave - 1) / kWave;
+  float bq[NB], cq[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int n = lane + k * kWave;
+    const int64_t o = (b * a.G + g) * NS + n;
+    bq[k] = n < NS ? ld_f<DT>(a.B, o) : 0.f;
+    cq[k] = n < NS ? ld_f<DT>(a.C, o) : 0.f;
+  }
+  const bool pl = lane < P;  // P <= 64: one state row per lane
+  const int hp = h * P + (pl ? lane : 0);
+  const float xv = pl ? ld_f<DT>(a.X, unit * P + lane) : 0.f;
+  const float ixv = a.sc.inv_X[hp], mv = a.sc.M_req[hp], ssv = a.sc.s_S[hp];
   const float dtv = ld_f<DT>(a.dt, unit);
   const float Ah = a.A[h];
+  const float ib = a.sc.inv_B[g], ic = a.sc.inv_C[g], sC = a.sc.s_C[g];
+
   // Q(Decay): the product dt A is exact in float64, the decision is taken there
   const int qd = (int)fmin(round(exp((double)dtv * (double)Ah) * 128.0), 128.0);
   const float decay = __expf(dtv * Ah);
 
   // Q(B), Q(C) of this position and group; Q(Xs) of this head
-  const float ib = a.sc.inv_B[g], ic = a.sc.inv_C[g];
   int cbp = 0;
-  for (int n = lane; n < NS; n += kWave) {
-    const int64_t o = (b * a.G + g) * NS + n;
-    const int qb = q8(__fmul_rn(ld_f<DT>(a.B, o), ib));
-    const int qc = q8(__fmul_rn(ld_f<DT>(a.C, o), ic));
-    L.b[n] = (float)qb;
-    L.qc[n] = (int8_t)qc;
-    cbp += qb * qc;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int n = lane + k * kWave;
+    const int qb = q8(__fmul_rn(bq[k], ib));
+    const int qc = q8(__fmul_rn(cq[k], ic));
+    if (n < NS) {
+      L.b[n] = (float)qb;
+      L.qc[n] = (int8_t)qc;
+      cbp += qb * qc;
+    }
   }
-  for (int p = lane; p < P; p += kWave) {
-    const float xv = ld_f<DT>(a.X, unit * P + p);
-    L.x[p] = xv;
-    L.qx[p] = q8(__fmul_rn(__fmul_rn(dtv, xv), a.sc.inv_X[h * P + p]));
+  if (pl) {
+    const int qx = q8(__fmul_rn(__fmul_rn(dtv, xv), ixv));
+    L.rv[lane] = make_float4((float)qx, mv, xv, decay * sC * ssv);
   }
   int cb = lane_sum_i<32>(cbp);
   cb += __shfl_xor(cb, 32);
@@ -126,7 +198,6 @@ __global__ __launch_bounds__(256) void k_decode_i8(DecodeArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const int col = lane % R, r0 = lane / R;
   float fb[16];
 #pragma unroll
   for (int e = 0; e < 16; e += 4) {
@@ -136,42 +207,34 @@ __global__ __launch_bounds__(256) void k_decode_i8(DecodeArgs a) {
   const uint4 qcv = *(const uint4*)&L.qc[16 * col];
   const uint32_t qcw[4] = {qcv.x, qcv.y, qcv.z, qcv.w};
 
-  uint4* st = (uint4*)((int8_t*)a.state + unit * (int64_t)P * NS);
-  uint4 hv[ITER];
-#pragma unroll
-  for (int i = 0; i < ITER; ++i) {
-    const int row = r0 + i * RPI;
-    if (row < P) hv[i] = st[row * R + col];
-  }
-  const float sC = a.sc.s_C[g];
   const float ydiag = (float)cb * sC * a.sc.s_B[g] * dtv;
   const float Dh = a.D[h];
+  const v2s qd2 = {(short)qd, (short)qd};
 #pragma unroll
   for (int i = 0; i < ITER; ++i) {
     const int row = r0 + i * RPI;
     const bool ok = row < P;
     const int rr = ok ? row : 0;
-    const float fqx = (float)L.qx[rr];
-    const float M = a.sc.M_req[h * P + rr];
-    const uint32_t hw[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+    const float4 rv = L.rv[rr];
+    const float fqx = rv.x, M = rv.y;
+    const uint32_t hw[4] = {hv[i][0], hv[i][1], hv[i][2], hv[i][3]};
     uint32_t nw[4];
     int acc = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int o[4];
+      float c[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s8 = q8(__fmul_rn(__fmul_rn(fqx, fb[4 * j + e]), M));
-        o[e] = sat127(s8 + rsh7_fast(__mul24(qd, byte_s(hw[j], e))));
-      }
-      nw[j] = perm_pack4(o[0], o[1], o[2], o[3]);
+      for (int e = 0; e < 4; ++e) c[e] = q8_pre(__fmul_rn(__fmul_rn(fqx, fb[4 * j + e]), M));
+      const v2s s01 = cvt_pair(c[0], c[1]), s23 = cvt_pair(c[2], c[3]);
+      const v2s r01 = rsh7_pair(qd2, unpack_pair(hw[j], 0x010c000cu));
+      const v2s r23 = rsh7_pair(qd2, unpack_pair(hw[j], 0x030c020cu));
+      nw[j] = pack_pairs(sat127_pair(s01 + r01), sat127_pair(s23 + r23));
       acc = __builtin_amdgcn_sdot4((int)qcw[j], (int)hw[j], acc, false);
     }
-    if (ok) st[row * R + col] = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+    if (ok) __builtin_nontemporal_store((v4u){nw[0], nw[1], nw[2], nw[3]}, &st[row * R + col]);
     acc = lane_sum_i<R>(acc);
     if (ok && col == 0) {
-      const float xv = L.x[row];
-      const float y = (float)acc * (decay * sC * a.sc.s_S[h * P + row]) + ydiag * xv + Dh * xv;
+      const float y = (float)acc * rv.w + ydiag * rv.z + Dh * rv.z;
       ((typename Store<DT>::T*)a.Y)[unit * P + row] = to_store<DT>(y);
     }
   }
@@ -180,47 +243,68 @@ __global__ __launch_bounds__(256) void k_decode_i8(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // FLOAT step (fp32 state)
 // ---------------------------------------------------------------------------
-template <int DT, int P, int NS>
+template <int DT, int P, int NS, int SPLIT>
 __global__ __launch_bounds__(256) void k_decode_f(DecodeArgs a) {
   constexpr int R = NS / 4;         // float4 slices per state row
   constexpr int RPI = kWave / R;
-  constexpr int ITER = (P + RPI - 1) / RPI;
+  constexpr int ITER = (P + RPI - 1) / RPI / SPLIT;
   constexpr int KB = ITER < 8 ? ITER : 8;  // rows in flight per lane
-  __shared__ __attribute__((aligned(16))) DecLds<P, NS> lds[kDecWaves];
+  __shared__ __attribute__((aligned(16))) DecLdsF<P, NS> lds[kDecWaves];
 
   const int w = wave_id(), lane = lane_id();
-  const int64_t unit = (int64_t)blockIdx.x * kDecWaves + w;
-  if (unit >= a.units) return;
-  DecLds<P, NS>& L = lds[w];
+  const int64_t item = (int64_t)blockIdx.x * kDecWaves + w;
+  if (item >= a.units * SPLIT) return;
+  const int64_t unit = item / SPLIT;
+  // rows are processed in batches of KB per lane; the next batch's loads are
+  // issued before the current batch is updated, the first before the prologue
+  const int col = lane % R, r0 = lane / R + (int)(item % SPLIT) * ITER * RPI;
+  v4f* st = (v4f*)((float*)a.state + unit * (int64_t)P * NS);
+  auto load_batch = [&](int i0, v4f* hv) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int row = r0 + (i0 + j) * RPI;
+      if (i0 + j < ITER && row < P) hv[j] = __builtin_nontemporal_load(&st[row * R + col]);
+    }
+  };
+  v4f cur[KB];
+  load_batch(0, cur);
+  DecLdsF<P, NS>& L = lds[w];
   const int64_t b = unit / a.H;
   const int h = (int)(unit % a.H);
   const int g = h / a.hpg;
 
+  constexpr int NB = (NS + kWave - 1) / kWave;
+  float bq[NB], cq[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int n = lane + k * kWave;
+    const int64_t o = (b * a.G + g) * NS + n;
+    bq[k] = n < NS ? ld_f<DT>(a.B, o) : 0.f;
+    cq[k] = n < NS ? ld_f<DT>(a.C, o) : 0.f;
+  }
+  const float xv0 = lane < P ? ld_f<DT>(a.X, unit * P + lane) : 0.f;  // P <= 64
   const float dtv = ld_f<DT>(a.dt, unit);
   const float decay = __expf(dtv * a.A[h]);
-  for (int n = lane; n < NS; n += kWave) {
-    const int64_t o = (b * a.G + g) * NS + n;
-    L.b[n] = ld_f<DT>(a.B, o);
-    L.c[n] = ld_f<DT>(a.C, o);
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int n = lane + k * kWave;
+    if (n < NS) {
+      L.b[n] = bq[k];
+      L.c[n] = cq[k];
+    }
   }
-  for (int p = lane; p < P; p += kWave) L.x[p] = ld_f<DT>(a.X, unit * P + p);
+  if (lane < P) L.x[lane] = xv0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const int col = lane % R, r0 = lane / R;
   const float4 bv = *(const float4*)&L.b[4 * col];
   const float4 cv = *(const float4*)&L.c[4 * col];
   const float Dh = a.D[h];
-  float4* st = (float4*)((float*)a.state + unit * (int64_t)P * NS);
 #pragma unroll
   for (int i0 = 0; i0 < ITER; i0 += KB) {
-    float4 hv[KB];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int row = r0 + (i0 + j) * RPI;
-      if (i0 + j < ITER && row < P) hv[j] = st[row * R + col];
-    }
+    v4f nxt[KB];
+    if (i0 + KB < ITER) load_batch(i0 + KB, nxt);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (i0 + j >= ITER) break;
@@ -228,39 +312,56 @@ __global__ __launch_bounds__(256) void k_decode_f(DecodeArgs a) {
       const bool ok = row < P;
       const float xv = L.x[ok ? row : 0];
       const float dx = dtv * xv;
-      float4 n;
-      n.x = fmaf(decay, hv[j].x, dx * bv.x);
-      n.y = fmaf(decay, hv[j].y, dx * bv.y);
-      n.z = fmaf(decay, hv[j].z, dx * bv.z);
-      n.w = fmaf(decay, hv[j].w, dx * bv.w);
-      if (ok) st[row * R + col] = n;
-      float acc = cv.x * n.x + cv.y * n.y + cv.z * n.z + cv.w * n.w;
+      v4f n;
+      n[0] = fmaf(decay, cur[j][0], dx * bv.x);
+      n[1] = fmaf(decay, cur[j][1], dx * bv.y);
+      n[2] = fmaf(decay, cur[j][2], dx * bv.z);
+      n[3] = fmaf(decay, cur[j][3], dx * bv.w);
+      if (ok) __builtin_nontemporal_store(n, &st[row * R + col]);
+      float acc = cv.x * n[0] + cv.y * n[1] + cv.z * n[2] + cv.w * n[3];
       acc = lane_sum_f<R>(acc);
       if (ok && col == 0)
         ((typename Store<DT>::T*)a.Y)[unit * P + row] = to_store<DT>(acc + Dh * xv);
     }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) cur[j] = nxt[j];
   }
 }
 
-template <int DT, int P, int NS>
-hipError_t launch_dec(bool int8, const DecodeArgs& a, hipStream_t st) {
-  const int64_t blocks = (a.units + kDecWaves - 1) / kDecWaves;
-  if (int8)
-    hipLaunchKernelGGL((k_decode_i8<DT, P, NS>), dim3((unsigned)blocks), dim3(kDecWaves * kWave), 0,
-                       st, a);
+template <bool I8, int DT, int P, int NS, int SPLIT>
+hipError_t launch_dec_s(const DecodeArgs& a, hipStream_t st) {
+  const int64_t blocks = (a.units * SPLIT + kDecWaves - 1) / kDecWaves;
+  if constexpr (I8)
+    hipLaunchKernelGGL((k_decode_i8<DT, P, NS, SPLIT>), dim3((unsigned)blocks),
+                       dim3(kDecWaves * kWave), 0, st, a);
   else
-    hipLaunchKernelGGL((k_decode_f<DT, P, NS>), dim3((unsigned)blocks), dim3(kDecWaves * kWave), 0,
-                       st, a);
+    hipLaunchKernelGGL((k_decode_f<DT, P, NS, SPLIT>), dim3((unsigned)blocks),
+                       dim3(kDecWaves * kWave), 0, st, a);
   return hipGetLastError();
+}
+
+// A head's rows are split over SPLIT = 4 waves when one wave per head would
+// leave the chip short of waves (fewer than 16 per CU): a small batch is
+// latency-bound, and four shorter waves finish sooner than one long one. Each
+// wave still forms the whole head's per-position vectors.
+template <bool I8, int DT, int P, int NS>
+hipError_t launch_dec(const DecodeArgs& a, hipStream_t st) {
+  constexpr int RPI = kWave / (NS / (I8 ? 16 : 4));  // rows per wave pass
+  constexpr int ITER = (P + RPI - 1) / RPI;          // passes of one wave per head
+  if constexpr (ITER % 4 == 0) {
+    const int64_t ncu = cu_count();
+    if (a.units * 4 <= 16 * (ncu > 0 ? ncu : 256)) return launch_dec_s<I8, DT, P, NS, 4>(a, st);
+  }
+  return launch_dec_s<I8, DT, P, NS, 1>(a, st);
 }
 
 template <int DT, int P>
 hipError_t dispatch_n(bool int8, int N, const DecodeArgs& a, hipStream_t st) {
   switch (N) {
-    case 16: return launch_dec<DT, P, 16>(int8, a, st);
-    case 32: return launch_dec<DT, P, 32>(int8, a, st);
-    case 64: return launch_dec<DT, P, 64>(int8, a, st);
-    case 128: return launch_dec<DT, P, 128>(int8, a, st);
+    case 16: return int8 ? launch_dec<true, DT, P, 16>(a, st) : launch_dec<false, DT, P, 16>(a, st);
+    case 32: return int8 ? launch_dec<true, DT, P, 32>(a, st) : launch_dec<false, DT, P, 32>(a, st);
+    case 64: return int8 ? launch_dec<true, DT, P, 64>(a, st) : launch_dec<false, DT, P, 64>(a, st);
+    case 128: return int8 ? launch_dec<true, DT, P, 128>(a, st) : launch_dec<false, DT, P, 128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1175,17 +1175,6 @@ hipError_t launch_one(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 // One workgroup per CU at a time: B*H heads run in ceil(B*H / CUs) rounds. When
 // the last round is at most half full, its heads are split in two p halves so
@@ -1239,6 +1228,18 @@ hipError_t launch_main(const FusedArgs& fa, hipStream_t st) {
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 bool fused_supported(const Dims& d, int dtype, bool int8) {
   if (!int8) {

@@ -60,6 +60,9 @@ hipError_t launch_amax_xs(const Dims& d, int dtype, const void* X, const float* 
                           float* amax_X, hipStream_t st);
 hipError_t launch_amax_states(const Dims& d, const float* states, float* amax_S, hipStream_t st);
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count();
+
 // Single-token decode step (seqlen 1), state [B,H,P,N] updated in place.
 hipError_t launch_decode_step(const Dims& d, int dtype, bool int8, const void* X, const void* dt,
                               const float* A, const void* B, const void* C, const float* D,

@@ -217,3 +217,47 @@ def test_decode_empty_batch_is_a_noop(gpu_lib):
     L.ssd_decode_step(sh, L.SSD_PATH_INT8, z, z, A, z, z, A, sc, st, z)
     torch.cuda.synchronize()
     assert int(st.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("path", ["int8", "float"])
+def test_decode_steps_replayed_from_a_graph(gpu_lib, path):
+    """Three decode steps captured in one HIP graph and replayed twice, with
+    eager work between the replays, leave the states three and six eager
+    steps leave (bitwise: the same kernels on the same inputs)."""
+    import torch
+    L = gpu_lib
+    c, L0 = _case("f16_ragged")
+    w = c.w
+    i8 = path == "int8"
+    p = L.SSD_PATH_INT8 if i8 else L.SSD_PATH_FLOAT
+    h_dev = torch.empty((w.batch, w.nheads, w.headdim, w.dstate),
+                        dtype=torch.int8 if i8 else torch.float32, device="cuda")
+    A, D, sc = _prefill(L, torch, c, L0, p, h_dev)
+    sh = H.shape_of(L, w, seqlen=1)
+    t = L0
+    x = H.to_dev(_step(c.ev["x"], t), w.dtype)
+    dt = H.to_dev(_step(c.ev["dt"], t), w.dtype)
+    B = H.to_dev(_step(c.ev["B"], t), w.dtype)
+    C = H.to_dev(_step(c.ev["C"], t), w.dtype)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    ref = h_dev.clone()
+    st = h_dev.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside the capture
+        L.ssd_decode_step(sh, p, x, dt, A, B, C, D, sc, st.clone(), y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            L.ssd_decode_step(sh, p, x, dt, A, B, C, D, sc, st, y)
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            L.ssd_decode_step(sh, p, x, dt, A, B, C, D, sc, ref, y)
+        torch.cuda.synchronize()
+        assert torch.equal(st, ref), rep
+        _ = (ref.float() * 2).sum().item()  # eager work between the replays
