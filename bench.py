@@ -161,7 +161,8 @@ def bench_decode(torch, np, L, synth, w, consts, scales, steps, warmup) -> dict:
             out[f"{path_name}_b{batch}"] = {
                 "us_per_step": us, "eager_us_per_step": eager_us, "tokens_per_s": batch / (us * 1e-6),
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes}}
+                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": nbytes,
+                             "traffic": measured_traffic(f"decode_b{batch}", path_name)}}
             del st
         del h8, dev, y
         torch.cuda.empty_cache()
@@ -237,6 +238,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paths", default="int8,float")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode step (prints its JSON object)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the SSD layer runs on a single MI355X here "
@@ -262,6 +265,11 @@ def main() -> int:
     cal_dev = [{k: torch.from_numpy(v).cuda() for k, v in s.items()} for s in cal]
     scales = L.calibrate(lambda s: L.make_shape(1, w.seqlen, w.nheads, w.headdim, w.dstate,
                                                 w.ngroups, w.chunk, w.dtype), cal_dev, A)
+    if args.decode_only:
+        copy_bandwidth(torch)  # the 1 GiB copy that counter runs scale against
+        dec = bench_decode(torch, np, L, synth, w, consts, scales, args.steps, args.warmup)
+        print(json.dumps({"decode": dec, "kernel_source_hash": kernel_source_hash()}), flush=True)
+        return 0
     y = torch.empty_like(dev["x"])
     tokens = w.batch * w.seqlen
     copy_gbs = copy_bandwidth(torch)
