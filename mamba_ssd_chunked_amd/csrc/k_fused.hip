@@ -284,7 +284,7 @@ __device__ __forceinline__ v2i lds_tr8(const int8_t* p) {
 // Writes the prefetched chunk into LDS: x transposed, Q(X_scaled) =
 // sat(RHAZ(fl32(fl32(lut * x) * inv_X))) transposed (the quantiser of "Key
 // design 1") and the per-position vectors.
-template <int DT, int LC, int NS, int PW>
+template <int DT, int LC, int NS, int PW, bool TAPS>
 __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC, NS>& sm, int64_t b, int h, int k,
                                                int tid, int c8base, const Prefetch<LC, NS, PW>& pf) {
   typedef typename Store<DT>::T T;
@@ -343,7 +343,7 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
       qd4[e] = q8x4(v[0], v[1], v[2], v[3]);
       *(uint32_t*)(qxb + e * LC + 16 * (qc ^ e)) = qd4[e];
     }
-    if (a.tap_qxs) {
+    if (TAPS && a.tap_qxs) {
       const Dims& d = a.d;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -374,7 +374,9 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
 // PW = 2: it owns p tiles 2 ph, 2 ph + 1 of a head; two such workgroups cover
 // the head, each recomputing the head's CB tiles. Used for the last, partial
 // round of heads so that it spreads over every CU.
-template <int DT, int LC, int NS, int PW>
+// TAPS: the instantiation that can write the debug taps (the others carry no
+// tap code, which keeps their scalar registers free).
+template <int DT, int LC, int NS, int PW, bool TAPS>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS, PW> PF;
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     PF pf;
     dma_qb<LC, NS, PW>(a, s_qB, b, g_h, 0, w, lo);
     prefetch_load<DT, LC, NS, PW>(a, b, h, 0, tid0, 2 * pt_base, lo, pf);
-    prefetch_store<DT, LC, NS, PW>(a, sm, b, h, 0, tid0, 2 * pt_base, pf);
+    prefetch_store<DT, LC, NS, PW, TAPS>(a, sm, b, h, 0, tid0, 2 * pt_base, pf);
     qd_word = pf.qd;
   }
 
@@ -530,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 #pragma unroll
       for (int j = 0; j < PTW; ++j) {
         const int p = 16 * (pt0 + j) + l16;
-        if (a.tap_s32) {
+        if (TAPS && a.tap_s32) {
           const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
           *(int4*)(a.tap_s32 + so) = make_int4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         }
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     __syncthreads();  // chunk k's tiles and H8l are no longer read
     // stage the next chunk's x tile, then start its Q(B) rows (straight into the
     // now free LDS buffer) and Q(C) rows; they land while StatePassing runs
-    prefetch_store<DT, LC, NS, PW>(a, sm, b, h, kn, tid, 2 * pt_base, pf);
+    prefetch_store<DT, LC, NS, PW, TAPS>(a, sm, b, h, kn, tid, 2 * pt_base, pf);
     dma_qb<LC, NS, PW>(a, s_qB, b, g_h, kn, w, lo);
     load_qc2(kn, lane, qc2);
 
@@ -717,8 +719,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       }
       *(uint32_t*)&H8l[b_off<NS>(p, 16 * nt_own + 4 * lg)] = H8[j];
       const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
-      if (a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = S8[j];
-      if (a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
+      if (TAPS && a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = S8[j];
+      if (TAPS && a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
     qd_word = pf.qd;
   }
@@ -1171,7 +1173,12 @@ size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
 template <int DT, int LC, int NS, int PW>
 hipError_t launch_one(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
-  hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, PW>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+  if (fa.tap_qxs || fa.tap_s32 || fa.tap_s8 || fa.tap_passed)
+    hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, PW, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       st, fa);
+  else
+    hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, PW, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       st, fa);
   return hipGetLastError();
 }
 
