@@ -28,6 +28,7 @@
 // and one factor per output row instead of an exponential per element.
 // Off-diagonal tiles accumulate unscaled and are multiplied by u_s once; the
 // diagonal tile uses exp(a_s - a_s') directly.
+#include "ssd_cumsum.hpp"
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -80,20 +81,21 @@ __device__ __forceinline__ FragF<DT> frag16(const u16* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Prologue: Q(B), Q(C) with padded rows (t >= L -> 0), once per group.
-// grid (c * l/64, B*G), 256 threads; one 64-row x N tile per block.
+// Prologue: Q(B), Q(C) with padded rows (t >= L -> 0), once per group. One
+// block of 256 threads quantises one 64-row x N tile: tile (bx, by) with bx over
+// c * l / 64 row blocks and by over B * G.
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restrict__ B,
-                                                     const void* __restrict__ C,
-                                                     const float* __restrict__ inv_B,
-                                                     const float* __restrict__ inv_C,
-                                                     int8_t* __restrict__ qB,
-                                                     int8_t* __restrict__ qC) {
+__device__ __forceinline__ void prologue_bc_block(const Dims& d, const void* __restrict__ B,
+                                                  const void* __restrict__ C,
+                                                  const float* __restrict__ inv_B,
+                                                  const float* __restrict__ inv_C,
+                                                  int8_t* __restrict__ qB,
+                                                  int8_t* __restrict__ qC, int bx, int64_t by) {
   constexpr int RB = 64;  // rows per block
   const int nsb = d.l / RB;
-  const int k = blockIdx.x / nsb, sb = blockIdx.x % nsb;
-  const int64_t bg = blockIdx.y;
+  const int k = bx / nsb, sb = bx % nsb;
+  const int64_t bg = by;
   const int64_t b = bg / d.G;
   const int g = (int)(bg % d.G);
   const int N = d.N, l = d.l;
@@ -120,6 +122,44 @@ __global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restr
     const int64_t dst = ((b * Lp + t) * d.G + g) * (int64_t)N + n0;
     *(uint2*)(qB + dst) = make_uint2(pack4(qb[0], qb[1], qb[2], qb[3]), pack4(qb[4], qb[5], qb[6], qb[7]));
     *(uint2*)(qC + dst) = make_uint2(pack4(qc[0], qc[1], qc[2], qc[3]), pack4(qc[4], qc[5], qc[6], qc[7]));
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restrict__ B,
+                                                     const void* __restrict__ C,
+                                                     const float* __restrict__ inv_B,
+                                                     const float* __restrict__ inv_C,
+                                                     int8_t* __restrict__ qB,
+                                                     int8_t* __restrict__ qC) {
+  prologue_bc_block<DT>(d, B, C, inv_B, inv_C, qB, qC, blockIdx.x, blockIdx.y);
+}
+
+// The INT8 path's preparation in one launch: blocks [0, ncs) run ChunkCumsum
+// (dAcs, LUT_state, Q(Decay)), the rest the B/C prologue. Both parts are short
+// and latency-bound, so running them side by side hides one behind the other.
+template <int DT>
+__global__ __launch_bounds__(256) void k_prep_i8(Dims d, const void* __restrict__ dt,
+                                                 const float* __restrict__ A,
+                                                 float* __restrict__ dAcs, float* __restrict__ lut,
+                                                 uint8_t* __restrict__ qdecay,
+                                                 const void* __restrict__ B,
+                                                 const void* __restrict__ C,
+                                                 const float* __restrict__ inv_B,
+                                                 const float* __restrict__ inv_C,
+                                                 int8_t* __restrict__ qB, int8_t* __restrict__ qC,
+                                                 int ncs) {
+  const int bi = blockIdx.x;
+  if (bi < ncs) {
+    // ChunkCumsum block (k, b, head block) from the linear index
+    const int k = bi % d.c;
+    const int rest = bi / d.c;
+    const int64_t b = rest % d.B;
+    chunk_cumsum_block<DT>(dt, A, dAcs, lut, qdecay, d, k, b, (int)(rest / d.B));
+  } else {
+    const int pi = bi - ncs;
+    const int nbx = d.c * (d.l / 64);
+    prologue_bc_block<DT>(d, B, C, inv_B, inv_C, qB, qC, pi % nbx, pi / nbx);
   }
 }
 
@@ -1310,15 +1350,31 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
   w += al(cs);
   uint8_t* qd = (uint8_t*)w;
 
-  const dim3 pgrid((unsigned)(d.c * (d.l / 64)), (unsigned)(d.B * d.G));
-  if (dtype == DT_F16)
-    hipLaunchKernelGGL(k_prologue_bc<DT_F16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC);
-  else
-    hipLaunchKernelGGL(k_prologue_bc<DT_BF16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, qd, st);
-  if (e != hipSuccess) return e;
+  // ChunkCumsum and the B/C prologue in one launch when the block count allows
+  const int64_t ncs = (int64_t)d.c * d.B * ((d.H + kCsHeads - 1) / kCsHeads);
+  const int64_t npro = (int64_t)d.c * (d.l / 64) * d.B * d.G;
+  hipError_t e;
+  if (ncs + npro < ((int64_t)1 << 24) && d.B <= 65535) {
+    const dim3 grid((unsigned)(ncs + npro));
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(k_prep_i8<DT_F16>, grid, dim3(256), 0, st, d, dt, A, dAcs, lut, qd, B, C,
+                         sc.inv_B, sc.inv_C, qB, qC, (int)ncs);
+    else
+      hipLaunchKernelGGL(k_prep_i8<DT_BF16>, grid, dim3(256), 0, st, d, dt, A, dAcs, lut, qd, B, C,
+                         sc.inv_B, sc.inv_C, qB, qC, (int)ncs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const dim3 pgrid((unsigned)(d.c * (d.l / 64)), (unsigned)(d.B * d.G));
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(k_prologue_bc<DT_F16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC);
+    else
+      hipLaunchKernelGGL(k_prologue_bc<DT_BF16>, pgrid, dim3(256), 0, st, d, B, C, sc.inv_B, sc.inv_C, qB, qC);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, qd, st);
+    if (e != hipSuccess) return e;
+  }
 
   const FusedArgs fa{d, X, dt, qB, qC, dAcs, lut, qd, D, sc, Y, (const int8_t*)initial_state,
                      (int8_t*)final_state, tap_qxs, tap_s32, tap_s8, tap_passed, 0, 0};

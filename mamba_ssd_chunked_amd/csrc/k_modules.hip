@@ -5,6 +5,7 @@
 // Duality" (paper notes page, ICLR 2026), "Overall framework" and "Key
 // designs 1-3"; the float path is the plain chunked algebra of the selective
 // state-space recurrence.
+#include "ssd_cumsum.hpp"
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -45,63 +46,15 @@ __global__ __launch_bounds__(256) void k_quantize_bc(const void* __restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// ChunkCumsum. One block per (chunk k, batch b, 16-head group). dt is staged in
-// LDS; one thread per head then forms the float64 prefix sums in sequence order
-// (the only serial part), and all threads evaluate the float64 exponentials and
-// write dAcs / LUT_state with coalesced stores. Padded positions past L carry
-// dt = 0, which leaves the running sum unchanged.
+// ChunkCumsum (block body in ssd_cumsum.hpp): grid (c, B, ceil(H / kCsHeads)).
 // ---------------------------------------------------------------------------
-constexpr int kCsHeads = 4;
-
 template <int DT>
 __global__ __launch_bounds__(256) void k_chunk_cumsum(const void* __restrict__ dt,
                                                       const float* __restrict__ A,
                                                       float* __restrict__ dAcs,
                                                       float* __restrict__ lut,
                                                       uint8_t* __restrict__ qdecay, Dims d) {
-  __shared__ float sdt[kCsHeads][256 + 1];
-  __shared__ double sa[kCsHeads][256 + 1];
-  const int k = blockIdx.x;
-  const int64_t b = blockIdx.y;
-  const int h0 = blockIdx.z * kCsHeads;
-  const int nh = min(kCsHeads, d.H - h0);
-  const int l = d.l;
-  const int64_t t0 = (int64_t)k * l;
-  const int nvalid = (int)min((int64_t)l, d.L - t0);
-  for (int idx = threadIdx.x; idx < kCsHeads * l; idx += 256) {
-    const int j = idx % kCsHeads, s = idx / kCsHeads;
-    float v = 0.f;
-    if (j < nh && s < nvalid) v = ld_f<DT>(dt, (b * d.L + t0 + s) * d.H + h0 + j);
-    sdt[j][s] = v;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < nh) {
-    const int j = threadIdx.x;
-    const double Ah = (double)A[h0 + j];
-    double a = 0.0;
-    // sequence order is kept; the LDS reads of each block of 16 steps are issued
-    // together so only the float64 additions form the dependent chain
-    for (int s0 = 0; s0 < l; s0 += 16) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = sdt[j][s0 + u];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        a += (double)v[u] * Ah;  // the product is exact in float64
-        sa[j][s0 + u] = a;
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * l; idx += 256) {
-    const int j = idx / l, s = idx % l;
-    const double a = sa[j][s], alast = sa[j][l - 1];
-    const int64_t o = ((b * d.H + h0 + j) * d.c + k) * (int64_t)l + s;
-    dAcs[o] = (float)a;
-    if (lut) lut[o] = (float)((double)sdt[j][s] * exp(alast - a));
-    if (qdecay && s == 0)
-      qdecay[(b * d.H + h0 + j) * d.c + k] = (uint8_t)fmin(round(exp(alast) * 128.0), 128.0);
-  }
+  chunk_cumsum_block<DT>(dt, A, dAcs, lut, qdecay, d, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------
