@@ -54,6 +54,18 @@ same way on the GPU side):
       position (LUT_state = dt, Q(Decay) from exp(dt A)), updating the
       persistent int8 state with Eq. 6; its output reads the state before the
       step (ChunkScan1) plus the position's own diagonal term (ChunkScan2).
+  R15 the Table 5 row "+ Q(X) only": X alone is quantised, once per (h,p) at
+      SSD entry with a static step s_Xq = amax|x| / q_max from the calibration
+      sequences; every read of X uses Q(X) s_Xq and the rest is the float path
+      (the state stays floating point: without the reconstruction LUT (.) X
+      is not an int8 tensor).
+  R16 the Table 5 row "+ reconstruction + B,C quantisation": B and C are
+      quantised once (as in the full method) and ChunkState runs on INT8
+      through the reconstruction; the state is dequantised (S32 s_X s_B) and
+      passed in floating point; ChunkScan1 runs on INT8 on the passed state
+      quantised with s_S; ChunkBMM and ChunkScan2 stay floating point on the
+      unquantised B and C. The full method (the last row) adds the persistent
+      INT8 state (Eq. 6) and the INT8 ChunkBMM.
 
 Where exactness is claimed, float64 matmuls are used on integer-valued
 operands whose partial sums stay below 2^53, so they are exact in any order.
@@ -466,6 +478,103 @@ def forward_int8(x, dt, A, B, C, D, scales: dict, chunk: int, h_init=None) -> di
     assert H % G == 0
     return {"qB": qB, "qC": qC, "cumsum": cs, "qxs": qxs, "s32": s32, "s8": s8,
             "passed": passed, "cb": cb, "y": y}
+
+
+# ---------------------------------------------------------------------------
+# Table 5 ablation modes ([SSDi8] experiments, Table 5 of the notes page):
+# the rows between the float baseline and the full method (R15, R16)
+# ---------------------------------------------------------------------------
+
+def calibrate_x(seqs) -> np.ndarray:
+    """amax of |x| per (h,p) over calibration sequences: the static scale of
+    Q(X) in the "Q(X) only" mode (R15). Each seq: float64 x [b,L,H,P]."""
+    amax = None
+    for sq in seqs:
+        ax = np.abs(np.asarray(sq["x"], np.float64)).max(axis=(0, 1))
+        amax = ax if amax is None else np.maximum(amax, ax)
+    return amax
+
+
+def forward_qx(x, dt, A, B, C, D, inv_Xq, s_Xq, chunk: int, bits: int = 8) -> dict:
+    """Table 5 row "+ Q(X) only" (R15). X is quantised once per (h,p) with a
+    static step s_Xq: Q(X) = sat(RHAZ(fl32(fl32(x) inv_Xq))); every later step
+    is the floating-point chunked computation on x_hat = Q(X) s_Xq (without
+    the reconstruction, LUT_state (.) X is no longer an int8 tensor, so the
+    state cannot be kept in INT8). inv_Xq, s_Xq [H,P]."""
+    qx = quantize(x, np.asarray(inv_Xq, np.float64)[None, None], bits)
+    xh = qx.astype(np.float64) * np.asarray(s_Xq, np.float64)[None, None]
+    y, hl = chunked(xh, dt, A, B, C, D, chunk)[:2]
+    return {"qx": qx, "x_hat": xh, "y": y, "final": hl}
+
+
+def forward_recon(x, dt, A, B, C, D, scales: dict, chunk: int) -> dict:
+    """Table 5 row "+ reconstruction + B,C quantisation" (R16).
+
+    ChunkState runs on INT8 through the reconstruction, as in the full method:
+    S32 = Q(X_scaled)^T Q(B) (Key design 1). The state is not kept in INT8: it
+    is dequantised, S_k = S32 s_X[h,p] s_B[g], and passed in floating point,
+    H_k = exp(a_{k,l-1}) H_{k-1} + S_k. ChunkScan1 runs on INT8, on the passed
+    state quantised per (h,p) with the state step s_S,
+    Q(H_{k-1}) = sat(RHAZ(H_{k-1} / s_S)), and Q(C):
+    Y_off = exp(a_s) s_C s_S (Q(C) . Q(H_{k-1})). ChunkBMM and ChunkScan2 stay in
+    floating point on the unquantised B and C (their quantisation comes with
+    the full method): Y_diag = sum_{s'<=s} (C_s . B_s') exp(a_s - a_s') dt_s' x_s'.
+    Y = Y_off + Y_diag + D x. Float64 throughout, apart from the quantisers.
+    """
+    bits = int(scales.get("bits", 8))
+    qm = qmax_of(bits)
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    b, L, H, P = x.shape
+    G = B.shape[2]
+    g = head_group(H, G)
+    qB = quantize(B, np.asarray(scales["inv_B"], np.float64)[None, None, :, None], bits)
+    qC = quantize(C, np.asarray(scales["inv_C"], np.float64)[None, None, :, None], bits)
+    cs = chunk_cumsum(dt, A, chunk, bits)
+    qxs = quantize_xs(x, cs["lut"], scales["inv_X"], chunk, bits)
+    s32 = chunk_state_int(qxs, qB, chunk)                                   # [b,c,H,P,N]
+    sxb = np.asarray(scales["s_X"], np.float64) * np.asarray(scales["s_B"], np.float64)[g][:, None]
+    S = s32.astype(np.float64) * sxb[None, None, :, :, None]
+    l = chunk
+    c = -(-L // l)
+    passed = np.empty_like(S)
+    h = np.zeros((b, H, P, N := B.shape[3]))
+    for k in range(c):
+        h = cs["decay"][:, :, k][:, :, None, None] * h + S[:, k]
+        passed[:, k] = h
+    s_S = np.asarray(scales["s_S"], np.float64)                               # [H,P]
+    s_C = np.asarray(scales["s_C"], np.float64)[g]                            # [H]
+    a = cs["a"]
+    xp = _pad_chunks(x, c * l).reshape(b, c, l, H, P)
+    dtp = _pad_chunks(dt, c * l).reshape(b, c, l, H)
+    Bp = _pad_chunks(np.asarray(B, np.float64), c * l).reshape(b, c, l, G, N)
+    Cp = _pad_chunks(np.asarray(C, np.float64), c * l).reshape(b, c, l, G, N)
+    qcp = _pad_chunks(qC.astype(np.float64), c * l).reshape(b, c, l, G, N)
+    D = np.asarray(D, np.float64)
+    tri = np.tril(np.ones((l, l), dtype=bool))
+    y = np.empty((b, c, l, H, P))
+    qpassed = np.empty(passed.shape, np.int64)
+    for k in range(c):
+        ak = a[:, :, k, :]                                                    # [b,H,l]
+        xs = xp[:, k].transpose(0, 2, 1, 3)                                   # [b,H,l,P]
+        if k > 0:
+            qh = saturate(rhaz(passed[:, k - 1] / s_S[None, :, :, None]), qm)  # [b,H,P,N]
+            qpassed[:, k - 1] = qh
+            qcs = qcp[:, k][:, :, g].transpose(0, 2, 1, 3)                    # [b,H,l,N]
+            acc1 = np.matmul(qcs, qh.astype(np.float64).transpose(0, 1, 3, 2))   # exact
+            y_off = acc1 * (np.exp(ak)[..., None] * (s_C[:, None] * s_S)[None, :, None, :])
+        else:
+            y_off = 0.0
+        Bs = Bp[:, k][:, :, g].transpose(0, 2, 1, 3)                          # [b,H,l,N]
+        Cs = Cp[:, k][:, :, g].transpose(0, 2, 1, 3)
+        cb = np.matmul(Cs, Bs.transpose(0, 1, 3, 2))
+        seg = ak[:, :, :, None] - ak[:, :, None, :]
+        Lmat = np.where(tri, np.exp(np.where(tri, seg, 0.0)), 0.0)
+        y_diag = np.matmul(cb * Lmat * dtp[:, k].transpose(0, 2, 1)[:, :, None, :], xs)
+        y[:, k] = (y_off + y_diag + D[None, :, None, None] * xs).transpose(0, 2, 1, 3)
+    qpassed[:, c - 1] = saturate(rhaz(passed[:, c - 1] / s_S[None, :, :, None]), qm)
+    return {"qB": qB, "qC": qC, "cumsum": cs, "qxs": qxs, "s32": s32, "S": S,
+            "passed": passed, "qpassed": qpassed, "y": y.reshape(b, c * l, H, P)[:, :L]}
 
 
 def rel_max_err(y, ref) -> float:

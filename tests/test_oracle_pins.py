@@ -405,3 +405,73 @@ def test_float_decode_steps_equal_the_recurrence():
         y, h = O.decode_step_float(tok["x"], tok["dt"], c.consts["A"], tok["B"], tok["C"], c.consts["D"], h)
         assert np.allclose(y, yr[:, t], rtol=1e-12, atol=1e-12 * np.abs(yr).max())
     assert np.allclose(h, hr, rtol=1e-12, atol=1e-12 * np.abs(hr).max())
+
+
+# Table 5 ablation modes (R15, R16).
+def test_qx_only_is_exact_on_the_quantiser_grid():
+    """x drawn on the grid of its own Q(X) step (powers of two, so inv_Xq is
+    exact): Q(X) returns those integers and the mode reduces to the float64
+    recurrence; off the grid the result moves by at most the rounding."""
+    rng = np.random.default_rng(7)
+    b, L, H, P, N, G = 2, 96, 3, 4, 8, 1
+    x, dt, A, B, C, D = _rand_inputs(rng, b, L, H, P, N, G)
+    s = 2.0 ** rng.integers(-6, -2, size=(H, P))
+    q = rng.integers(-127, 128, size=x.shape)
+    xg = q * s[None, None]
+    r = O.forward_qx(xg, dt, A, B, C, D, 1.0 / s, s, chunk=32)
+    assert np.array_equal(r["qx"], q)
+    y, _ = O.recurrence(xg, dt, A, B, C, D)
+    assert O.rel_max_err(r["y"], y) < 1e-12
+    # the step is applied where X is read: doubling the step with the same
+    # integers doubles every X-linear part of y (all of it, as y is linear in x)
+    r2 = O.forward_qx(2 * xg, dt, A, B, C, D, 0.5 / s, 2 * s, chunk=32)
+    assert np.array_equal(r2["qx"], q)
+    assert np.allclose(r2["y"], 2 * r["y"], rtol=1e-12, atol=1e-12)
+    # saturation: values beyond 127 steps clip to +-127
+    r3 = O.forward_qx(1000 * s[None, None] * np.sign(q + 0.5), dt, A, B, C, D, 1.0 / s, s, 32)
+    assert np.abs(r3["qx"]).max() == 127
+
+
+@pytest.mark.parametrize("wid,seqlen", [(0, None), (1, 512)])
+def test_recon_mode_high_bit_convergence(wid, seqlen):
+    """"+ reconstruction + B,C quantisation" converges to the float64
+    definition as the bit width grows (scales calibrated on the inputs
+    themselves, so nothing saturates); a misplaced s_X, s_B, s_S or s_C would
+    leave an O(1) error at every width."""
+    w = synth.WORKLOADS[wid]
+    if seqlen is not None:
+        w = w.replace(seqlen=seqlen, nheads=8)
+    c = synth.layer_constants(w)
+    ev = synth.as_f64(synth.evaluation_batch(w, c, batch=1), w.dtype)
+    y, _ = O.recurrence(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"])
+    am = O.calibrate([ev], c["A"], w.ngroups, w.chunk)
+    errs = {}
+    for bits in (8, 12, 16, 20):
+        sc = O.scale_pack(am["B"], am["C"], am["Xs"], am["S"], w.nheads, bits=bits)
+        r = O.forward_recon(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"], sc, w.chunk)
+        errs[bits] = O.rel_max_err(r["y"], y)
+    assert errs[20] <= 1e-3
+    assert errs[8] > 4 * errs[12] > 16 * errs[16]
+    # the dequantised local states approach the float64 chunk states
+    _, S, Hs = O.chunk_states(ev["x"], ev["dt"], c["A"], ev["B"], w.chunk)
+    sc = O.scale_pack(am["B"], am["C"], am["Xs"], am["S"], w.nheads, bits=20)
+    r = O.forward_recon(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"], sc, w.chunk)
+    assert np.abs(r["S"] - S).max() <= 1e-4 * np.abs(S).max()
+    assert np.abs(r["passed"] - Hs).max() <= 1e-4 * np.abs(Hs).max()
+
+
+def test_recon_mode_shares_the_int8_chunk_state():
+    """The recon mode's ChunkState integers are those of the full method (the
+    same reconstruction), and its first chunk's output, which has no passed
+    state, differs from the float64 definition only through ChunkScan2's
+    floating-point B and C (none here) and the D skip (exact)."""
+    w, c, ev = _w0_inputs()
+    cal = [synth.as_f64(s, w.dtype) for s in synth.calibration_sequences(w, c)]
+    am = O.calibrate(cal, c["A"], w.ngroups, w.chunk)
+    sc = O.scale_pack(am["B"], am["C"], am["Xs"], am["S"], w.nheads)
+    r = O.forward_recon(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"], sc, w.chunk)
+    r8 = O.forward_int8(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"], sc, w.chunk)
+    assert np.array_equal(r["s32"], r8["s32"]) and np.array_equal(r["qxs"], r8["qxs"])
+    y, _ = O.recurrence(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"])
+    l = w.chunk
+    assert O.rel_max_err(r["y"][:, :l], y[:, :l]) < 1e-12
