@@ -169,6 +169,90 @@ def bench_decode(torch, np, L, synth, w, consts, scales, steps, warmup) -> dict:
     return out
 
 
+# Table 5 of the SSDi8 notes page: SSD latency (ms) of Mamba-2 2.7B at W4A8 for
+# the float SSD, "+ Q(X) only", "+ reconstruction + B,C quantisation" and the
+# full method (persistent INT8 state + INT8 ChunkBMM). Another machine's
+# numbers: their ratios are the comparison, not the values.
+PAGES_TABLE5_MS = (8.63, 8.58, 8.05, 6.53)
+
+
+def bench_ablation(torch, np, L, synth, w, consts, dev, A, D, scales, cal_dev, steps, warmup) -> dict:
+    """The Table 5 ladder on this GPU: every row run through the module
+    kernels (one launch per module, states and CB through HBM, as the pages'
+    modules do), and the two rows the fused kernels cover through ssd_forward."""
+    sh = L.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+    # step of Q(X) by the library's pack rule, from amax |x| on the calibration sequences
+    amx = torch.stack([s["x"].abs().amax(dim=(0, 1)).float() for s in cal_dev]).amax(0)
+    G, HP = w.ngroups, w.nheads * w.headdim
+    am = np.concatenate([np.ones(2 * G, np.float32), amx.cpu().numpy().reshape(-1),
+                         np.ones(HP, np.float32)])
+    px = L.ssd_scales_from_amax(G, w.nheads, w.headdim, am)
+    sc_host = {k: v for k, v in scales.host.items()}
+    sc_host.update({"s_Xq": px["s_X"], "inv_Xq": px["inv_X"]})
+    sc_all = L.ScalePack(sc_host)
+    y = torch.empty_like(dev["x"])
+    c = sh.nchunks
+    cs = (w.batch, w.nheads, c, w.chunk)
+    dAcs = torch.empty(cs, dtype=torch.float32, device="cuda")
+    lut = torch.empty_like(dAcs)
+    qd = torch.empty(cs[:3], dtype=torch.uint8, device="cuda")
+    st_shape = (w.batch, c, w.nheads, w.headdim, w.dstate)
+    st8 = torch.empty(st_shape, dtype=torch.int8, device="cuda")
+    st32 = torch.empty(st_shape, dtype=torch.float32, device="cuda")
+    cb = torch.empty((w.batch, c, w.ngroups, w.chunk, w.chunk), dtype=torch.float32, device="cuda")
+    qB = torch.empty(dev["B"].shape, dtype=torch.int8, device="cuda")
+    qC = torch.empty_like(qB)
+
+    def modules_float():
+        L.ssd_chunk_cumsum(sh, dev["dt"], A, dAcs, lut)
+        L.ssd_chunk_state(sh, L.SSD_PATH_FLOAT, dev["x"], lut, dev["B"], None, st32)
+        L.ssd_state_passing(sh, L.SSD_PATH_FLOAT, st32, dAcs)
+        L.ssd_chunk_bmm(sh, L.SSD_PATH_FLOAT, dev["C"], dev["B"], cb)
+        L.ssd_chunk_scan(sh, L.SSD_PATH_FLOAT, dev["x"], dev["dt"], dAcs, dev["C"], cb, st32, D, None, y)
+
+    def modules_int8():
+        L.ssd_quantize_bc(sh, dev["B"], dev["C"], scales, qB, qC)
+        L.ssd_chunk_cumsum(sh, dev["dt"], A, dAcs, lut, qd)
+        L.ssd_chunk_state(sh, L.SSD_PATH_INT8, dev["x"], lut, qB, scales, st8)
+        L.ssd_state_passing(sh, L.SSD_PATH_INT8, st8, dAcs, qd)
+        L.ssd_chunk_bmm(sh, L.SSD_PATH_INT8, qC, qB, cb)
+        L.ssd_chunk_scan(sh, L.SSD_PATH_INT8, dev["x"], dev["dt"], dAcs, qC, cb, st8, D, scales, y)
+
+    wss = {p: torch.empty(max(1, L.ssd_workspace_bytes(sh, p)), dtype=torch.uint8, device="cuda")
+           for p in (L.SSD_PATH_ABL_QX, L.SSD_PATH_ABL_RECON, L.SSD_PATH_FLOAT, L.SSD_PATH_INT8)}
+
+    def forward(p, sc):
+        return lambda: L.ssd_forward(sh, p, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, sc, y,
+                                     workspace=wss[p])
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    rows = [
+        {"row": "SSD all floating point (fp16)", "module_ms": timed(modules_float),
+         "fused_ms": timed(forward(L.SSD_PATH_FLOAT, None))},
+        {"row": "+ Q(X) only", "module_ms": timed(forward(L.SSD_PATH_ABL_QX, sc_all))},
+        {"row": "+ reconstruction + B,C quantisation", "module_ms": timed(forward(L.SSD_PATH_ABL_RECON, sc_all))},
+        {"row": "+ persistent INT8 state + INT8 ChunkBMM (the full method)", "module_ms": timed(modules_int8),
+         "fused_ms": timed(forward(L.SSD_PATH_INT8, scales))},
+    ]
+    base = rows[0]["module_ms"]
+    for r, pg in zip(rows, PAGES_TABLE5_MS):
+        r["module_speedup_vs_float_modules"] = base / r["module_ms"]
+        r["pages_ms"] = pg
+        r["pages_speedup"] = PAGES_TABLE5_MS[0] / pg
+    return {"workload": w.name, "rows": rows}
+
+
 CPU_SEQUENCES = 2   # sequences of the batch the CPU baseline runs (a bounded sample)
 
 
@@ -238,6 +322,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paths", default="int8,float")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step (prints its JSON object)")
     args = ap.parse_args()
@@ -341,6 +426,9 @@ def main() -> int:
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, np, L, synth, w, consts, scales, args.steps, args.warmup)
+    if not args.no_ablation:
+        out["ablation"] = bench_ablation(torch, np, L, synth, w, consts, dev, A, D, scales, cal_dev,
+                                         args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, consts, ev)
     print(json.dumps(out), flush=True)

@@ -65,8 +65,19 @@ enum {
 /* Element type of X, dt, B, C and Y. */
 enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_F16 = 1, SSD_DTYPE_BF16 = 2 };
 
-/* Which path a call computes. */
-enum { SSD_PATH_FLOAT = 0, SSD_PATH_INT8 = 1 };
+/* Which path a call computes. The two ablation rows of the notes page's
+ * Table 5 (experiments: the latency ladder from the float SSD to the full
+ * method) are ssd_forward paths only:
+ *   SSD_PATH_ABL_QX     "+ Q(X) only": X quantised once per (h,p) with its own
+ *                       static step (scales s_Xq, inv_Xq), everything else the
+ *                       float path on Q(X) s_Xq; the state stays fp32.
+ *   SSD_PATH_ABL_RECON  "+ reconstruction + B,C quantisation": Q(B), Q(C) once;
+ *                       ChunkState on INT8 through the reconstruction
+ *                       (S32 = Q(X_scaled) x Q(B)), dequantised with s_X s_B and
+ *                       passed in fp32; ChunkScan1 on INT8 (the passed state
+ *                       quantised with s_S, Q(C)); ChunkBMM and ChunkScan2 in
+ *                       floating point on B and C. */
+enum { SSD_PATH_FLOAT = 0, SSD_PATH_INT8 = 1, SSD_PATH_ABL_QX = 2, SSD_PATH_ABL_RECON = 3 };
 
 /* Problem shape. batch == 0 or seqlen == 0 is a valid empty problem (calls
  * return SSD_OK and enqueue nothing); every other size must be > 0. */
@@ -87,6 +98,10 @@ typedef struct ssd_shape {
  * scales; B/C per group G, X_scaled and the state per (H,P)).
  *   s_B, s_C, inv_B, inv_C   [G]       inv = fp32(1 / s)
  *   inv_X, s_S, M_req        [H * P]   M_req = fp32(s_X * s_B[g(h)] / s_S)
+ * The ablation paths read more (each may be NULL where no path reads it):
+ *   s_X                      [H * P]   X_scaled step (SSD_PATH_ABL_RECON)
+ *   s_Xq, inv_Xq             [H * P]   step of X itself (SSD_PATH_ABL_QX only;
+ *                                      that path reads no other array)
  */
 typedef struct ssd_scales {
   const float* s_B;
@@ -96,6 +111,9 @@ typedef struct ssd_scales {
   const float* inv_X;
   const float* s_S;
   const float* M_req;
+  const float* s_X;
+  const float* s_Xq;
+  const float* inv_Xq;
 } ssd_scales;
 
 /* Optional debug outputs of the INT8 path (any member may be NULL). */
@@ -174,6 +192,9 @@ int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* 
 
 /* The whole SSD forward in one call ("Overall framework": all modules).
  * B, C, X, dt in shape->dtype; Y in shape->dtype. INT8 needs scales.
+ * path may also be one of the two ablation rows (SSD_PATH_ABL_QX,
+ * SSD_PATH_ABL_RECON: module kernels, fp32 final_state, no initial_state and
+ * no taps; an initial_state returns SSD_E_UNSUPPORTED).
  * initial_state (may be NULL): the state before the first position, int8 in
  * the state scale (INT8) or fp32 (FLOAT) [B,H,P,N]; passing a previous call's
  * final_state continues that sequence (exactly, when the previous call's

@@ -34,6 +34,8 @@ SSD_DTYPE_F16 = 1
 SSD_DTYPE_BF16 = 2
 SSD_PATH_FLOAT = 0
 SSD_PATH_INT8 = 1
+SSD_PATH_ABL_QX = 2
+SSD_PATH_ABL_RECON = 3
 
 DTYPE_CODE = {torch.float32: SSD_DTYPE_F32, torch.float16: SSD_DTYPE_F16,
               torch.bfloat16: SSD_DTYPE_BF16}
@@ -54,7 +56,7 @@ class SsdShape(ctypes.Structure):
 
 class SsdScales(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("s_B", "s_C", "inv_B", "inv_C", "inv_X", "s_S", "M_req")]
+                ("s_B", "s_C", "inv_B", "inv_C", "inv_X", "s_S", "M_req", "s_X", "s_Xq", "inv_Xq")]
 
 
 class SsdTaps(ctypes.Structure):
@@ -147,29 +149,32 @@ def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype) ->
 
 
 class ScalePack:
-    """Device copy of the static INT8 scale pack, each array 256-byte aligned.
+    """Device copy of the static scale pack, each array 256-byte aligned.
 
     ``arrays`` holds float32 numpy arrays s_B, s_C, inv_B, inv_C ([G]) and
-    s_X, inv_X, s_S, M_req ([H, P] or [H*P]).
+    s_X, inv_X, s_S, M_req ([H, P] or [H*P]); optionally s_Xq, inv_Xq ([H, P],
+    the step of X itself, read only by the "Q(X) only" ablation path).
     """
 
     ORDER = ("s_B", "s_C", "inv_B", "inv_C", "s_X", "inv_X", "s_S", "M_req")
+    OPTIONAL = ("s_Xq", "inv_Xq")
 
     def __init__(self, arrays: dict, device="cuda"):
-        flat = [np.ascontiguousarray(arrays[k], dtype=np.float32).reshape(-1) for k in self.ORDER]
+        names = [k for k in self.ORDER if k in arrays] + [k for k in self.OPTIONAL if k in arrays]
+        flat = [np.ascontiguousarray(arrays[k], dtype=np.float32).reshape(-1) for k in names]
         offs, cur = [], 0
         for a in flat:
             offs.append(cur)
             cur += -(-a.size // 64) * 64
-        host = np.zeros(cur, dtype=np.float32)
+        host = np.zeros(max(cur, 64), dtype=np.float32)
         for o, a in zip(offs, flat):
             host[o:o + a.size] = a
-        self.host = {k: a for k, a in zip(self.ORDER, flat)}
+        self.host = {k: a for k, a in zip(names, flat)}
         self.tensor = torch.from_numpy(host).to(device)
         base = self.tensor.data_ptr()
-        ptr = {k: base + 4 * o for k, o in zip(self.ORDER, offs)}
-        self.struct = SsdScales(ptr["s_B"], ptr["s_C"], ptr["inv_B"], ptr["inv_C"],
-                                ptr["inv_X"], ptr["s_S"], ptr["M_req"])
+        ptr = {k: base + 4 * o for k, o in zip(names, offs)}
+        self.struct = SsdScales(*[ptr.get(k) for k in ("s_B", "s_C", "inv_B", "inv_C", "inv_X",
+                                                       "s_S", "M_req", "s_X", "s_Xq", "inv_Xq")])
 
 
 def _scales(sc):

@@ -46,6 +46,28 @@ __global__ __launch_bounds__(256) void k_quantize_bc(const void* __restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
+// Q(X) of the Table 5 "Q(X) only" row: x quantised once per (h, p) with its own
+// static step, sat127(RHAZ(fl32(x * inv_Xq[h,p]))). Each thread converts 8
+// consecutive elements (one head, 8 consecutive p).
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void k_quantize_x(const void* __restrict__ X,
+                                                    const float* __restrict__ inv_Xq,
+                                                    int8_t* __restrict__ qx, int64_t nvec, int HP) {
+  for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = v * 8;
+    const int hp0 = (int)(e0 % HP);
+    float xv[8];
+    ld8_f<DT>(X, e0, xv);
+    int q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = q_sat(xv[j] * inv_Xq[hp0 + j], 127.f);
+    *(uint2*)(qx + e0) = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // ChunkCumsum (block body in ssd_cumsum.hpp): grid (c, B, ceil(H / kCsHeads)).
 // ---------------------------------------------------------------------------
 template <int DT>
@@ -65,15 +87,22 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const void* __restrict__ d
 // ---------------------------------------------------------------------------
 constexpr int kStK = 64;  // s per staged block
 
-template <int DT, bool INT8>
+// MODE (ssd_launch.hpp): kModeFloat, kModeInt8 (S8 requantised, "Key design 2"),
+// kModeQx (X read as int8 Q(X) times its step sx[h,p]; float otherwise) and
+// kModeRecon (S32 on INT8 as in kModeInt8, dequantised to fp32 with
+// sx[h,p] * sb[g] instead of requantised).
+template <int DT, int MODE>
 __global__ __launch_bounds__(256) void k_chunk_state(Dims d, const void* __restrict__ X,
                                                      const float* __restrict__ lut,
                                                      const void* __restrict__ Bq,
                                                      const float* __restrict__ inv_X,
                                                      const float* __restrict__ M_req,
+                                                     const float* __restrict__ sx,
+                                                     const float* __restrict__ sb,
                                                      void* __restrict__ states,
                                                      int8_t* __restrict__ tap_qxs,
                                                      int32_t* __restrict__ tap_s32) {
+  constexpr bool INT8 = MODE == kModeInt8 || MODE == kModeRecon;
   typedef typename Store<DT>::T T;
   constexpr int PAD = INT8 ? 16 : (16 / (int)sizeof(T));
   typedef typename std::conditional<INT8, int8_t, T>::type E;
@@ -103,7 +132,15 @@ __global__ __launch_bounds__(256) void k_chunk_state(Dims d, const void* __restr
       const int64_t t = (int64_t)k * d.l + s0 + s;
       float xv[8];
       if (t < d.L) {
-        ld8_f<DT>(X, ((b * d.L + t) * H + h) * (int64_t)P + p0, xv);
+        const int64_t xo = ((b * d.L + t) * H + h) * (int64_t)P + p0;
+        if constexpr (MODE == kModeQx) {
+          const uint2 q = *(const uint2*)((const int8_t*)X + xo);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xv[j] = (float)byte_s(j < 4 ? q.x : q.y, j % 4) * sx[h * P + p0 + j];
+        } else {
+          ld8_f<DT>(X, xo, xv);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) xv[j] = 0.f;
@@ -196,10 +233,12 @@ __global__ __launch_bounds__(256) void k_chunk_state(Dims d, const void* __restr
       for (int r = 0; r < 4; ++r) {
         const int p = pt * 16 + 4 * (lane >> 4) + r, n = nt * 16 + (lane & 15);
         const int64_t off = (((b * d.c + k) * H + h) * (int64_t)P + p) * N + n;
-        if constexpr (INT8) {
+        if constexpr (MODE == kModeInt8) {
           const int v = acc[j][r];
           if (tap_s32) tap_s32[off] = v;
           ((int8_t*)states)[off] = (int8_t)q_sat((float)v * M_req[h * P + p], 127.f);
+        } else if constexpr (MODE == kModeRecon) {
+          ((float*)states)[off] = (float)acc[j][r] * (sx[h * P + p] * sb[g]);
         } else {
           ((float*)states)[off] = acc[j][r];
         }
@@ -348,7 +387,12 @@ __global__ __launch_bounds__(256) void k_chunk_bmm(Dims d, const void* __restric
 // row tiles w, w+4, w+8, w+12 (balanced under the causal mask) and all P/16
 // column tiles. x is staged transposed in LDS in the compute type.
 // ---------------------------------------------------------------------------
-template <int DT, bool INT8>
+// MODE: kModeFloat, kModeInt8 (Scan1 on the int8 passed states and Q(C), Scan2
+// on the int32 CB with s_C s_B folded into its weights), kModeQx (float, X read
+// as int8 Q(X) times its step sx[h,p]) and kModeRecon (Scan1 on INT8: the fp32
+// passed states are quantised with the state step s_S as they are read and
+// contracted with Q(C); Scan2 on the fp32 CB of the unquantised B and C).
+template <int DT, int MODE>
 __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restrict__ X,
                                                     const void* __restrict__ dt,
                                                     const float* __restrict__ dAcs,
@@ -360,7 +404,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
                                                     const float* __restrict__ s_C,
                                                     const float* __restrict__ s_B,
                                                     const float* __restrict__ s_S,
+                                                    const float* __restrict__ sx,
                                                     void* __restrict__ Y) {
+  constexpr bool INT8 = MODE == kModeInt8;            // int32 CB with folded scales
+  constexpr bool SCAN1_I8 = MODE == kModeInt8 || MODE == kModeRecon;
   typedef typename Store<DT>::T T;
   constexpr int PAD = 16 / (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) T sxT[64][256 + PAD];
@@ -379,7 +426,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
     const int s = item / (P / 8), p0 = (item % (P / 8)) * 8;
     float xv[8];
     if (t0 + s < d.L) {
-      ld8_f<DT>(X, ((b * d.L + t0 + s) * H + h) * (int64_t)P + p0, xv);
+      const int64_t xo = ((b * d.L + t0 + s) * H + h) * (int64_t)P + p0;
+      if constexpr (MODE == kModeQx) {
+        const uint2 q = *(const uint2*)((const int8_t*)X + xo);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = (float)byte_s(j < 4 ? q.x : q.y, j % 4) * sx[h * P + p0 + j];
+      } else {
+        ld8_f<DT>(X, xo, xv);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) xv[j] = 0.f;
@@ -439,7 +493,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
     if (has_prev) {
       const int64_t st0 = (k > 0 ? ((b * d.c + (k - 1)) * H + h) : (b * H + h)) * (int64_t)P * N;
       const int64_t ts = t0 + s;
-      if constexpr (INT8) {
+      if constexpr (SCAN1_I8) {
         v4i acc1[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc1[pt] = v4i{0, 0, 0, 0};
@@ -451,8 +505,21 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
           for (int pt = 0; pt < 4; ++pt) {
             if (pt < PT) {
               v4i hb = {0, 0, 0, 0};
-              if (n < N)
-                hb = *(const v4i*)((const int8_t*)sprev + st0 + (int64_t)(pt * 16 + (lane & 15)) * N + n);
+              const int pr = pt * 16 + (lane & 15);
+              if (n < N) {
+                if constexpr (MODE == kModeRecon) {
+                  // Q(H) = sat(RHAZ(H / s_S[h,p])) of the fp32 passed state
+                  const float* hp = (const float*)sprev + st0 + (int64_t)pr * N + n;
+                  const float sS = s_S[h * P + pr];
+                  int q[16];
+#pragma unroll
+                  for (int e = 0; e < 16; ++e) q[e] = q_sat(hp[e] / sS, 127.f);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) hb[e] = (int)pack4(q[4 * e], q[4 * e + 1], q[4 * e + 2], q[4 * e + 3]);
+                } else {
+                  hb = *(const v4i*)((const int8_t*)sprev + st0 + (int64_t)pr * N + n);
+                }
+              }
               acc1[pt] = mma_i8(a, hb, acc1[pt]);
             }
           }
@@ -495,7 +562,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Dims d, const void* __restri
           float y = acc[pt][r] + Dh * xv;
           if (has_prev) {
             float f = expf(sdA[sr]);
-            if (INT8) f *= s_C[g] * s_S[h * P + p];
+            if (SCAN1_I8) f *= s_C[g] * s_S[h * P + p];
             y += yoff[pt][r] * f;
           }
           const int64_t t = t0 + sr;
@@ -529,6 +596,17 @@ hipError_t launch_quantize_bc(const Dims& d, int dtype, const void* B, const voi
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_x(const Dims& d, int dtype, const void* X, const float* inv_Xq,
+                             int8_t* qx, hipStream_t st) {
+  const int64_t nvec = d.B * d.L * d.H * (int64_t)d.P / 8;
+  const int64_t want = (nvec + 255) / 256;
+  const unsigned grid = (unsigned)(want < 8192 ? (want > 0 ? want : 1) : 8192);
+#define L_(DT_) hipLaunchKernelGGL(k_quantize_x<DT_>, dim3(grid), dim3(256), 0, st, X, inv_Xq, qx, nvec, d.H * d.P)
+  SSD_DISPATCH_DT(dtype, L_)
+#undef L_
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_cumsum(const Dims& d, int dtype, const void* dt, const float* A,
                                float* dAcs, float* lut, uint8_t* qdecay, hipStream_t st) {
   const dim3 grid(d.c, (unsigned)d.B, (d.H + kCsHeads - 1) / kCsHeads);
@@ -538,20 +616,36 @@ hipError_t launch_chunk_cumsum(const Dims& d, int dtype, const void* dt, const f
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_state(const Dims& d, int dtype, bool int8, const void* X,
+hipError_t launch_chunk_state(const Dims& d, int dtype, int mode, const void* X,
                               const float* lut, const void* Bq, const float* inv_X,
-                              const float* M_req, void* states, int8_t* tap_qxs,
-                              int32_t* tap_s32, hipStream_t st) {
+                              const float* M_req, const float* sx, const float* sb, void* states,
+                              int8_t* tap_qxs, int32_t* tap_s32, hipStream_t st) {
   const dim3 grid(d.H, d.c, (unsigned)d.B);
-  if (int8) {
-#define L_(DT_) hipLaunchKernelGGL((k_chunk_state<DT_, true>), grid, dim3(256), 0, st, d, X, lut, Bq, inv_X, M_req, states, tap_qxs, tap_s32)
-    SSD_DISPATCH_DT(dtype, L_)
-#undef L_
-  } else {
-#define L_(DT_) hipLaunchKernelGGL((k_chunk_state<DT_, false>), grid, dim3(256), 0, st, d, X, lut, Bq, inv_X, M_req, states, tap_qxs, tap_s32)
-    SSD_DISPATCH_DT(dtype, L_)
-#undef L_
+#define L_(DT_) hipLaunchKernelGGL((k_chunk_state<DT_, M_>), grid, dim3(256), 0, st, d, X, lut, Bq, inv_X, M_req, sx, sb, states, tap_qxs, tap_s32)
+  switch (mode) {
+    case kModeFloat: {
+      constexpr int M_ = kModeFloat;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    case kModeInt8: {
+      constexpr int M_ = kModeInt8;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    case kModeQx: {
+      constexpr int M_ = kModeQx;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    case kModeRecon: {
+      constexpr int M_ = kModeRecon;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    default: return hipErrorInvalidValue;
   }
+#undef L_
   return hipGetLastError();
 }
 
@@ -583,21 +677,37 @@ hipError_t launch_chunk_bmm(const Dims& d, int dtype, bool int8, const void* Cq,
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_scan(const Dims& d, int dtype, bool int8, const void* X, const void* dt,
+hipError_t launch_chunk_scan(const Dims& d, int dtype, int mode, const void* X, const void* dt,
                              const float* dAcs, const void* Cq, const void* CB,
                              const void* states, const void* init, const float* D,
-                             const float* s_C, const float* s_B, const float* s_S, void* Y,
-                             hipStream_t st) {
+                             const float* s_C, const float* s_B, const float* s_S, const float* sx,
+                             void* Y, hipStream_t st) {
   const dim3 grid(d.H, d.c, (unsigned)d.B);
-  if (int8) {
-#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, true>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, init, D, s_C, s_B, s_S, Y)
-    SSD_DISPATCH_DT(dtype, L_)
-#undef L_
-  } else {
-#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, false>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, init, D, s_C, s_B, s_S, Y)
-    SSD_DISPATCH_DT(dtype, L_)
-#undef L_
+#define L_(DT_) hipLaunchKernelGGL((k_chunk_scan<DT_, M_>), grid, dim3(256), 0, st, d, X, dt, dAcs, Cq, CB, states, init, D, s_C, s_B, s_S, sx, Y)
+  switch (mode) {
+    case kModeFloat: {
+      constexpr int M_ = kModeFloat;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    case kModeInt8: {
+      constexpr int M_ = kModeInt8;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    case kModeQx: {
+      constexpr int M_ = kModeQx;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    case kModeRecon: {
+      constexpr int M_ = kModeRecon;
+      SSD_DISPATCH_DT(dtype, L_)
+      break;
+    }
+    default: return hipErrorInvalidValue;
   }
+#undef L_
   return hipGetLastError();
 }
 

@@ -68,8 +68,14 @@ int check_shape(const ssd_shape* s, Dims* d, bool* empty) {
   return SSD_OK;
 }
 
+// The module calls and the decode step compute the float and INT8 paths.
 int check_path(int path) {
   return (path == SSD_PATH_FLOAT || path == SSD_PATH_INT8) ? SSD_OK : SSD_E_UNSUPPORTED;
+}
+
+// ssd_forward also runs the two Table 5 ablation rows.
+int check_forward_path(int path) {
+  return (path >= SSD_PATH_FLOAT && path <= SSD_PATH_ABL_RECON) ? SSD_OK : SSD_E_UNSUPPORTED;
 }
 
 // Each required pointer must be non-NULL and 16-byte aligned.
@@ -87,14 +93,25 @@ int check_opt(std::initializer_list<const void*> opt) {
   return SSD_OK;
 }
 
-// Scale arrays are read element-wise: non-NULL and 4-byte aligned.
-int check_scales(const ssd_scales* sc) {
+// Scale arrays are read element-wise: non-NULL and 4-byte aligned. Which
+// arrays a path reads: INT8 the first seven; the "Q(X) only" row s_Xq and
+// inv_Xq; the "reconstruction + B,C" row the first seven and s_X.
+int check_scales(const ssd_scales* sc, int path = SSD_PATH_INT8) {
   if (!sc) return SSD_E_NULL;
-  const void* req[] = {sc->s_B, sc->s_C, sc->inv_B, sc->inv_C, sc->inv_X, sc->s_S, sc->M_req};
-  for (const void* p : req)
-    if (!p) return SSD_E_NULL;
-  for (const void* p : req)
-    if (reinterpret_cast<uintptr_t>(p) & 3u) return SSD_E_ALIGN;
+  const void* req[8];
+  int n = 0;
+  if (path == SSD_PATH_ABL_QX) {
+    req[n++] = sc->s_Xq;
+    req[n++] = sc->inv_Xq;
+  } else {
+    const void* base[] = {sc->s_B, sc->s_C, sc->inv_B, sc->inv_C, sc->inv_X, sc->s_S, sc->M_req};
+    for (const void* p : base) req[n++] = p;
+    if (path == SSD_PATH_ABL_RECON) req[n++] = sc->s_X;
+  }
+  for (int i = 0; i < n; ++i)
+    if (!req[i]) return SSD_E_NULL;
+  for (int i = 0; i < n; ++i)
+    if (reinterpret_cast<uintptr_t>(req[i]) & 3u) return SSD_E_ALIGN;
   return SSD_OK;
 }
 
@@ -110,6 +127,9 @@ ssd::ScalePtrs scale_ptrs(const ssd_scales* sc) {
     p.inv_X = sc->inv_X;
     p.s_S = sc->s_S;
     p.M_req = sc->M_req;
+    p.s_X = sc->s_X;
+    p.s_Xq = sc->s_Xq;
+    p.inv_Xq = sc->inv_Xq;
   }
   return p;
 }
@@ -130,14 +150,69 @@ Sizes sizes_of(const Dims& d) {
 }
 
 // Workspace of the module-by-module composition of ssd_forward.
-size_t modular_ws_bytes(const Dims& d, bool int8) {
+size_t modular_ws_bytes(const Dims& d, int path) {
   const Sizes z = sizes_of(d);
   size_t n = 2 * align_up(z.cs) + align_up(z.cb);
-  if (int8)
-    n += 2 * align_up(z.qbc) + align_up(z.qd) + align_up(z.st_i8);
-  else
-    n += align_up(z.st_f32);
+  switch (path) {
+    case SSD_PATH_INT8: n += 2 * align_up(z.qbc) + align_up(z.qd) + align_up(z.st_i8); break;
+    case SSD_PATH_ABL_QX: n += align_up((size_t)d.B * d.L * d.H * d.P) + align_up(z.st_f32); break;
+    case SSD_PATH_ABL_RECON: n += 2 * align_up(z.qbc) + align_up(z.st_f32); break;
+    default: n += align_up(z.st_f32); break;
+  }
   return n;
+}
+
+// The two Table 5 ablation rows ("SSDi8" notes page, experiments, Table 5),
+// composed from the module kernels:
+//   "Q(X) only"                 Q(X) once per (h,p); float modules on Q(X) s_Xq;
+//   "reconstruction + B,C"      Q(B), Q(C); ChunkState on INT8 (S32), dequantised
+//                               to fp32 with s_X s_B; float StatePassing; float
+//                               ChunkBMM on B, C; ChunkScan with an INT8 Scan1
+//                               (passed states quantised with s_S) and a float Scan2.
+int forward_ablation(const Dims& d, int dtype, int path, const void* X, const void* dt,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const ssd::ScalePtrs& sp, void* Y, void* final_state, void* workspace,
+                     hipStream_t st) {
+  const Sizes z = sizes_of(d);
+  char* w = (char*)workspace;
+  float* dAcs = (float*)w;
+  w += align_up(z.cs);
+  float* lut = (float*)w;
+  w += align_up(z.cs);
+  float* CB = (float*)w;
+  w += align_up(z.cb);
+  if (path == SSD_PATH_ABL_QX) {
+    int8_t* qx = (int8_t*)w;
+    w += align_up((size_t)d.B * d.L * d.H * d.P);
+    float* states = (float*)w;
+    if (ssd::launch_quantize_x(d, dtype, X, sp.inv_Xq, qx, st)) return SSD_E_HIP;
+    if (ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st)) return SSD_E_HIP;
+    if (ssd::launch_chunk_state(d, dtype, ssd::kModeQx, qx, lut, B, nullptr, nullptr, sp.s_Xq, nullptr,
+                                states, nullptr, nullptr, st))
+      return SSD_E_HIP;
+    if (ssd::launch_state_passing(d, false, states, dAcs, nullptr, nullptr, final_state, st)) return SSD_E_HIP;
+    if (ssd::launch_chunk_bmm(d, dtype, false, C, B, CB, st)) return SSD_E_HIP;
+    if (ssd::launch_chunk_scan(d, dtype, ssd::kModeQx, qx, dt, dAcs, C, CB, states, nullptr, D, nullptr,
+                               nullptr, nullptr, sp.s_Xq, Y, st))
+      return SSD_E_HIP;
+    return SSD_OK;
+  }
+  int8_t* qB = (int8_t*)w;
+  w += align_up(z.qbc);
+  int8_t* qC = (int8_t*)w;
+  w += align_up(z.qbc);
+  float* states = (float*)w;
+  if (ssd::launch_quantize_bc(d, dtype, B, C, sp.inv_B, sp.inv_C, qB, qC, st)) return SSD_E_HIP;
+  if (ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st)) return SSD_E_HIP;
+  if (ssd::launch_chunk_state(d, dtype, ssd::kModeRecon, X, lut, qB, sp.inv_X, nullptr, sp.s_X, sp.s_B,
+                              states, nullptr, nullptr, st))
+    return SSD_E_HIP;
+  if (ssd::launch_state_passing(d, false, states, dAcs, nullptr, nullptr, final_state, st)) return SSD_E_HIP;
+  if (ssd::launch_chunk_bmm(d, dtype, false, C, B, CB, st)) return SSD_E_HIP;
+  if (ssd::launch_chunk_scan(d, dtype, ssd::kModeRecon, X, dt, dAcs, qC, CB, states, nullptr, D, sp.s_C,
+                             sp.s_B, sp.s_S, nullptr, Y, st))
+    return SSD_E_HIP;
+  return SSD_OK;
 }
 
 }  // namespace
@@ -199,10 +274,10 @@ int ssd_chunk_state(const ssd_shape* shape, int path, const void* X, const float
   int32_t* ts = (i8 && taps) ? taps->s32 : nullptr;
   if ((rc = check_opt({tq, ts}))) return rc;
   if (empty) return SSD_OK;
-  return hip_status(ssd::launch_chunk_state(d, shape->dtype, i8, X, lut, Bq,
-                                            i8 ? scales->inv_X : nullptr,
-                                            i8 ? scales->M_req : nullptr, states, tq, ts,
-                                            (hipStream_t)stream));
+  return hip_status(ssd::launch_chunk_state(d, shape->dtype, i8 ? ssd::kModeInt8 : ssd::kModeFloat,
+                                            X, lut, Bq, i8 ? scales->inv_X : nullptr,
+                                            i8 ? scales->M_req : nullptr, nullptr, nullptr, states,
+                                            tq, ts, (hipStream_t)stream));
 }
 
 int ssd_state_passing(const ssd_shape* shape, int path, void* states, const float* dAcs,
@@ -248,21 +323,23 @@ int ssd_chunk_scan(const ssd_shape* shape, int path, const void* X, const void* 
   if ((rc = check_opt({initial_state}))) return rc;
   if (i8 && (rc = check_scales(scales))) return rc;
   if (empty) return SSD_OK;
-  return hip_status(ssd::launch_chunk_scan(d, shape->dtype, i8, X, dt, dAcs, Cq, CB, states,
-                                           initial_state, D,
+  return hip_status(ssd::launch_chunk_scan(d, shape->dtype, i8 ? ssd::kModeInt8 : ssd::kModeFloat,
+                                           X, dt, dAcs, Cq, CB, states, initial_state, D,
                                            i8 ? scales->s_C : nullptr,
                                            i8 ? scales->s_B : nullptr,
-                                           i8 ? scales->s_S : nullptr, Y, (hipStream_t)stream));
+                                           i8 ? scales->s_S : nullptr, nullptr, Y,
+                                           (hipStream_t)stream));
 }
 
 size_t ssd_workspace_bytes(const ssd_shape* shape, int path) {
   Dims d;
   bool empty;
-  if (check_shape(shape, &d, &empty) != SSD_OK || check_path(path) != SSD_OK) return 0;
+  if (check_shape(shape, &d, &empty) != SSD_OK || check_forward_path(path) != SSD_OK) return 0;
   const bool i8 = path == SSD_PATH_INT8;
   if (empty) return 0;
-  if (ssd::fused_supported(d, shape->dtype, i8)) return ssd::fused_workspace_bytes(d, i8);
-  return modular_ws_bytes(d, i8);
+  if (path <= SSD_PATH_INT8 && ssd::fused_supported(d, shape->dtype, i8))
+    return ssd::fused_workspace_bytes(d, i8);
+  return modular_ws_bytes(d, path);
 }
 
 int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt, const float* A,
@@ -273,10 +350,12 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
   bool empty;
   int rc = check_shape(shape, &d, &empty);
   if (rc) return rc;
-  if ((rc = check_path(path))) return rc;
+  if ((rc = check_forward_path(path))) return rc;
   const bool i8 = path == SSD_PATH_INT8;
+  const bool abl = path == SSD_PATH_ABL_QX || path == SSD_PATH_ABL_RECON;
   if ((rc = check_ptrs({X, dt, A, B, C, D, Y}))) return rc;
-  if (i8 && (rc = check_scales(scales))) return rc;
+  if (path != SSD_PATH_FLOAT && (rc = check_scales(scales, path))) return rc;
+  if (abl && initial_state) return SSD_E_UNSUPPORTED;
   int8_t* tq = (i8 && taps) ? taps->q_xs : nullptr;
   int32_t* ts = (i8 && taps) ? taps->s32 : nullptr;
   int8_t* t8 = (i8 && taps) ? taps->s8_local : nullptr;
@@ -288,6 +367,8 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
   hipStream_t st = (hipStream_t)stream;
   const int dtype = shape->dtype;
   const ssd::ScalePtrs sp = scale_ptrs(scales);
+
+  if (abl) return forward_ablation(d, dtype, path, X, dt, A, B, C, D, sp, Y, final_state, workspace, st);
 
   if (ssd::fused_supported(d, dtype, i8)) {
     hipError_t e = ssd::launch_forward_fused(d, dtype, i8, X, dt, A, B, C, D, sp, Y, initial_state,
@@ -315,27 +396,28 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
     int8_t* states = (int8_t*)w;
     if ((e = ssd::launch_quantize_bc(d, dtype, B, C, sp.inv_B, sp.inv_C, qB, qC, st))) return SSD_E_HIP;
     if ((e = ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, qd, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_chunk_state(d, dtype, true, X, lut, qB, sp.inv_X, sp.M_req, states, tq, ts, st)))
+    if ((e = ssd::launch_chunk_state(d, dtype, ssd::kModeInt8, X, lut, qB, sp.inv_X, sp.M_req, nullptr,
+                                     nullptr, states, tq, ts, st)))
       return SSD_E_HIP;
     if (t8 && (e = hipMemcpyAsync(t8, states, z.st_i8, hipMemcpyDeviceToDevice, st))) return SSD_E_HIP;
     if ((e = ssd::launch_state_passing(d, true, states, dAcs, qd, initial_state, final_state, st)))
       return SSD_E_HIP;
     if (tp && (e = hipMemcpyAsync(tp, states, z.st_i8, hipMemcpyDeviceToDevice, st))) return SSD_E_HIP;
     if ((e = ssd::launch_chunk_bmm(d, dtype, true, qC, qB, CB, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_chunk_scan(d, dtype, true, X, dt, dAcs, qC, CB, states, initial_state, D,
-                                    sp.s_C, sp.s_B, sp.s_S, Y, st)))
+    if ((e = ssd::launch_chunk_scan(d, dtype, ssd::kModeInt8, X, dt, dAcs, qC, CB, states, initial_state,
+                                    D, sp.s_C, sp.s_B, sp.s_S, nullptr, Y, st)))
       return SSD_E_HIP;
   } else {
     float* states = (float*)w;
     if ((e = ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_chunk_state(d, dtype, false, X, lut, B, nullptr, nullptr, states, nullptr,
-                                     nullptr, st)))
+    if ((e = ssd::launch_chunk_state(d, dtype, ssd::kModeFloat, X, lut, B, nullptr, nullptr, nullptr,
+                                     nullptr, states, nullptr, nullptr, st)))
       return SSD_E_HIP;
     if ((e = ssd::launch_state_passing(d, false, states, dAcs, nullptr, initial_state, final_state, st)))
       return SSD_E_HIP;
     if ((e = ssd::launch_chunk_bmm(d, dtype, false, C, B, CB, st))) return SSD_E_HIP;
-    if ((e = ssd::launch_chunk_scan(d, dtype, false, X, dt, dAcs, C, CB, states, initial_state, D,
-                                    nullptr, nullptr, nullptr, Y, st)))
+    if ((e = ssd::launch_chunk_scan(d, dtype, ssd::kModeFloat, X, dt, dAcs, C, CB, states, initial_state,
+                                    D, nullptr, nullptr, nullptr, nullptr, Y, st)))
       return SSD_E_HIP;
   }
   return SSD_OK;
@@ -396,8 +478,8 @@ int ssd_calibrate_amax(const ssd_shape* shape, const void* X, const void* dt, co
   if (ssd::launch_amax_bc(d, dtype, B, C, amB, amC, st)) return SSD_E_HIP;
   if (ssd::launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st)) return SSD_E_HIP;
   if (ssd::launch_amax_xs(d, dtype, X, lut, amX, st)) return SSD_E_HIP;
-  if (ssd::launch_chunk_state(d, dtype, false, X, lut, B, nullptr, nullptr, states, nullptr,
-                              nullptr, st))
+  if (ssd::launch_chunk_state(d, dtype, ssd::kModeFloat, X, lut, B, nullptr, nullptr, nullptr, nullptr,
+                              states, nullptr, nullptr, st))
     return SSD_E_HIP;
   if (ssd::launch_amax_states(d, states, amS, st)) return SSD_E_HIP;
   if (ssd::launch_state_passing(d, false, states, dAcs, nullptr, nullptr, nullptr, st)) return SSD_E_HIP;

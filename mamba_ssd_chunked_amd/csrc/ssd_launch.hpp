@@ -20,27 +20,35 @@ struct ScalePtrs {
   const float* inv_X;
   const float* s_S;
   const float* M_req;
+  const float* s_X;
+  const float* s_Xq;
+  const float* inv_Xq;
 };
+
+// Module-kernel modes; the values equal the C ABI's SSD_PATH_* codes.
+enum { kModeFloat = 0, kModeInt8 = 1, kModeQx = 2, kModeRecon = 3 };
 
 hipError_t launch_quantize_bc(const Dims& d, int dtype, const void* B, const void* C,
                               const float* inv_B, const float* inv_C, int8_t* qB, int8_t* qC,
                               hipStream_t st);
 hipError_t launch_chunk_cumsum(const Dims& d, int dtype, const void* dt, const float* A,
                                float* dAcs, float* lut, uint8_t* qdecay, hipStream_t st);
-hipError_t launch_chunk_state(const Dims& d, int dtype, bool int8, const void* X,
+hipError_t launch_quantize_x(const Dims& d, int dtype, const void* X, const float* inv_Xq,
+                             int8_t* qx, hipStream_t st);
+hipError_t launch_chunk_state(const Dims& d, int dtype, int mode, const void* X,
                               const float* lut, const void* Bq, const float* inv_X,
-                              const float* M_req, void* states, int8_t* tap_qxs,
-                              int32_t* tap_s32, hipStream_t st);
+                              const float* M_req, const float* sx, const float* sb, void* states,
+                              int8_t* tap_qxs, int32_t* tap_s32, hipStream_t st);
 hipError_t launch_state_passing(const Dims& d, bool int8, void* states, const float* dAcs,
                                 const uint8_t* qdecay, const void* init, void* final_state,
                                 hipStream_t st);
 hipError_t launch_chunk_bmm(const Dims& d, int dtype, bool int8, const void* Cq,
                             const void* Bq, void* CB, hipStream_t st);
-hipError_t launch_chunk_scan(const Dims& d, int dtype, bool int8, const void* X, const void* dt,
+hipError_t launch_chunk_scan(const Dims& d, int dtype, int mode, const void* X, const void* dt,
                              const float* dAcs, const void* Cq, const void* CB,
                              const void* states, const void* init, const float* D,
-                             const float* s_C, const float* s_B, const float* s_S, void* Y,
-                             hipStream_t st);
+                             const float* s_C, const float* s_B, const float* s_S, const float* sx,
+                             void* Y, hipStream_t st);
 
 // Fused forward (defined in k_fused.hip). Returns hipErrorNotSupported when the
 // fused kernels do not cover the shape; the caller then composes the modules.

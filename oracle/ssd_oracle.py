@@ -495,6 +495,15 @@ def calibrate_x(seqs) -> np.ndarray:
     return amax
 
 
+def scale_pack_x(amax_X, bits: int = 8) -> dict:
+    """Step and inverse step of Q(X) (R15) by the pack rule of R1:
+    s_Xq = fp32(amax / q_max) (1 when amax is 0 or not finite), inv_Xq = fp32(1 / s_Xq)."""
+    a = np.asarray(amax_X, np.float64)
+    ok = (a > 0) & np.isfinite(a)
+    s = np.where(ok, a / float(qmax_of(bits)), 1.0).astype(np.float32)
+    return {"s_Xq": s, "inv_Xq": (1.0 / s.astype(np.float64)).astype(np.float32)}
+
+
 def forward_qx(x, dt, A, B, C, D, inv_Xq, s_Xq, chunk: int, bits: int = 8) -> dict:
     """Table 5 row "+ Q(X) only" (R15). X is quantised once per (h,p) with a
     static step s_Xq: Q(X) = sat(RHAZ(fl32(fl32(x) inv_Xq))); every later step

@@ -187,3 +187,23 @@ def test_decode_step_validates():
     assert dec(shape(seqlen=1, dstate=256)) == L.SSD_E_UNSUPPORTED
     # empty batch: nothing to do
     assert dec(shape(seqlen=1, batch=0)) == L.SSD_OK
+
+
+def test_ablation_paths_validate():
+    b = ctypes.byref
+    sh = shape()
+    for path in (L.SSD_PATH_ABL_QX, L.SSD_PATH_ABL_RECON):
+        assert L.LIB.ssd_workspace_bytes(b(sh), path) > 0
+        # scales are required
+        assert fwd(sh, path=path, scales=None) == L.SSD_E_NULL
+        # no initial state on the ablation rows
+        full = L.SsdScales(*([A16] * 10))
+        assert fwd(sh, path=path, scales=b(full), init=A16) == L.SSD_E_UNSUPPORTED
+    # "Q(X) only" reads only s_Xq and inv_Xq; the recon row also needs s_X
+    qx_only = L.SsdScales(*([None] * 8 + [A16, A16]))
+    assert fwd(sh, path=L.SSD_PATH_ABL_QX, scales=b(qx_only), ws=None, wsb=0) == L.SSD_E_WORKSPACE
+    no_sx = L.SsdScales(*([A16] * 7 + [None, A16, A16]))
+    assert fwd(sh, path=L.SSD_PATH_ABL_RECON, scales=b(no_sx)) == L.SSD_E_NULL
+    # the module calls and the decode step run the float and INT8 paths only
+    assert L.LIB.ssd_chunk_state(b(sh), 2, A16, A16, A16, None, A16, None, None) == L.SSD_E_UNSUPPORTED
+    assert fwd(sh, path=4) == L.SSD_E_UNSUPPORTED

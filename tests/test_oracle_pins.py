@@ -475,3 +475,13 @@ def test_recon_mode_shares_the_int8_chunk_state():
     y, _ = O.recurrence(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"])
     l = w.chunk
     assert O.rel_max_err(r["y"][:, :l], y[:, :l]) < 1e-12
+
+
+def test_qx_scale_pack_follows_the_pack_rule():
+    """Q(X)'s step uses the same rule as every other scale (R1): compare with the
+    X_scaled entry of scale_pack on the same maxima, including zero and
+    non-finite maxima."""
+    a = np.array([[3.0, 0.0], [np.inf, 1e-30]])
+    px = O.scale_pack_x(a)
+    ref = O.scale_pack(np.ones(1), np.ones(1), a, np.ones((2, 2)), nheads=2)
+    assert np.array_equal(px["s_Xq"], ref["s_X"]) and np.array_equal(px["inv_Xq"], ref["inv_X"])
