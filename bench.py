@@ -253,6 +253,36 @@ def bench_ablation(torch, np, L, synth, w, consts, dev, A, D, scales, cal_dev, s
     return {"workload": w.name, "rows": rows}
 
 
+def bench_epilogue(torch, np, L, synth, w, y, y_ref, steps, warmup) -> dict:
+    """ssd_epilogue (RMSNorm with the 0.15 mean correction) on the layer's
+    output: Y read once and the result written once per call."""
+    sh = L.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+    c = torch.empty((w.nheads, w.headdim), dtype=torch.float32, device="cuda")
+    L.ssd_mean_correction(sh, y_ref, y, c)
+    wt = torch.from_numpy(synth.norm_weight(w)).cuda()
+    out = torch.empty_like(y)
+
+    def step():
+        L.ssd_epilogue(sh, y, c, L.MEAN_CORRECTION_ALPHA, wt, 1e-5, out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    esz = {"fp32": 4, "fp16": 2, "bf16": 2}[w.dtype]
+    nbytes = 2 * w.batch * w.seqlen * w.nheads * w.headdim * esz
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": us, "tokens_per_s": w.batch * w.seqlen / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
+
+
 CPU_SEQUENCES = 2   # sequences of the batch the CPU baseline runs (a bounded sample)
 
 
@@ -323,6 +353,7 @@ def main() -> int:
     ap.add_argument("--paths", default="int8,float")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step (prints its JSON object)")
     args = ap.parse_args()
@@ -426,6 +457,12 @@ def main() -> int:
     }
     if not args.no_decode:
         out["decode"] = bench_decode(torch, np, L, synth, w, consts, scales, args.steps, args.warmup)
+    if not args.no_epilogue and "int8" in results:
+        y8 = torch.empty_like(dev["x"])
+        yf = torch.empty_like(dev["x"])
+        L.ssd_forward(sh, L.SSD_PATH_INT8, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, scales, y8)
+        L.ssd_forward(sh, L.SSD_PATH_FLOAT, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, None, yf)
+        out["epilogue"] = bench_epilogue(torch, np, L, synth, w, y8, yf, args.steps, args.warmup)
     if not args.no_ablation:
         out["ablation"] = bench_ablation(torch, np, L, synth, w, consts, dev, A, D, scales, cal_dev,
                                          args.steps, args.warmup)

@@ -231,6 +231,28 @@ int ssd_decode_step(const ssd_shape* shape, int path, const void* X, const void*
                     const float* A, const void* B, const void* C, const float* D,
                     const ssd_scales* scales, void* state, void* Y, void* stream);
 
+/* SSD epilogue: the steps right after the SSD ("Overall framework": the SSD
+ * output goes through RMSNorm before Out Proj; "Key design 4": the per-channel
+ * mean correction, with the coefficient 0.15 of "Training strategy").
+ * For every position r of Y [B, L, H*P] (shape->dtype):
+ *   u = Y[r, :] + alpha * corr            (corr [H*P] fp32, may be NULL: u = Y[r, :])
+ *   out[r, :] = u / sqrt(mean(u^2) + eps) * weight   (weight [H*P] fp32)
+ * computed in fp32, out in shape->dtype (may alias Y). The pages apply the
+ * correction at Out Proj, whose trained weights are not part of this library;
+ * here it corrects the SSD output's own channels. eps >= 0 and a finite
+ * alpha are required (SSD_E_SHAPE otherwise); B * L <= 2^24. */
+int ssd_epilogue(const ssd_shape* shape, const void* Y, const float* corr, float alpha,
+                 const float* weight, float eps, void* out, void* stream);
+
+/* The mean correction's closed form ("Key design 4": the least-squares
+ * correction of a quantised output is the per-channel mean of its error):
+ * c[ch] = mean over all B * L positions of (Y_ref - Y_q)[., ch], for
+ * Y_ref, Y_q [B, L, H*P] in shape->dtype (e.g. the float path's and the
+ * INT8 path's outputs on calibration sequences); c [H*P] fp32. Summed in
+ * float64 in a fixed order. An empty shape returns SSD_E_SHAPE. */
+int ssd_mean_correction(const ssd_shape* shape, const void* Y_ref, const void* Y_q, float* c,
+                        void* stream);
+
 /* Workspace bytes ssd_forward needs (0 for an invalid shape). Host only. */
 size_t ssd_workspace_bytes(const ssd_shape* shape, int path);
 

@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
                         ctypes.c_size_t, ctypes.POINTER(SsdTaps), P],
         "ssd_decode_step": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P,
                             P],
+        "ssd_epilogue": [SP, P, P, ctypes.c_float, P, ctypes.c_float, P, P],
+        "ssd_mean_correction": [SP, P, P, P, P],
         "ssd_calibrate_amax": [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P],
         "ssd_scales_from_amax": [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P],
     }
@@ -110,6 +112,7 @@ LIB = _load()
 
 EXPORTED = ("ssd_quantize_bc", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
             "ssd_chunk_bmm", "ssd_chunk_scan", "ssd_forward", "ssd_decode_step",
+            "ssd_epilogue", "ssd_mean_correction",
             "ssd_workspace_bytes",
             "ssd_calibrate_amax", "ssd_calibrate_workspace_bytes", "ssd_scales_from_amax",
             "ssd_status_string")
@@ -260,6 +263,23 @@ def ssd_decode_step(shape, path, X, dt, A, B, C, D, scales, state, Y, stream=Non
     _check("ssd_decode_step", LIB.ssd_decode_step(ctypes.byref(shape), path, _p(X), _p(dt), _p(A),
                                                   _p(B), _p(C), _p(D), _scales(scales),
                                                   _p(state), _p(Y), _stream(stream)))
+
+
+# "Key design 4": the mean correction's coefficient fixed by "Training strategy"
+MEAN_CORRECTION_ALPHA = 0.15
+
+
+def ssd_epilogue(shape, Y, corr, alpha, weight, eps, out, stream=None):
+    """RMSNorm over the H*P channels of every position of Y, after adding
+    alpha * corr (corr may be None)."""
+    _check("ssd_epilogue", LIB.ssd_epilogue(ctypes.byref(shape), _p(Y), _p(corr), float(alpha),
+                                            _p(weight), float(eps), _p(out), _stream(stream)))
+
+
+def ssd_mean_correction(shape, Y_ref, Y_q, c, stream=None):
+    """c = per-channel mean of Y_ref - Y_q over all positions."""
+    _check("ssd_mean_correction", LIB.ssd_mean_correction(ctypes.byref(shape), _p(Y_ref), _p(Y_q),
+                                                          _p(c), _stream(stream)))
 
 
 def ssd_calibrate_workspace_bytes(shape) -> int:

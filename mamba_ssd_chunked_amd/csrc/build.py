@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libssd.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
-HIP_SOURCES = ["k_modules.hip", "k_fused.hip", "k_calib.hip", "k_decode.hip"]
+HIP_SOURCES = ["k_modules.hip", "k_fused.hip", "k_calib.hip", "k_decode.hip", "k_epilogue.hip"]
 CPP_SOURCES = ["ssd_api.cpp"]
 
 ARCH = "gfx950"

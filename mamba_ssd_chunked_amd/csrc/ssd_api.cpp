@@ -442,6 +442,33 @@ int ssd_decode_step(const ssd_shape* shape, int path, const void* X, const void*
                                             scale_ptrs(scales), state, Y, (hipStream_t)stream));
 }
 
+int ssd_epilogue(const ssd_shape* shape, const void* Y, const float* corr, float alpha,
+                 const float* weight, float eps, void* out, void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_ptrs({Y, weight, out}))) return rc;
+  if ((rc = check_opt({corr}))) return rc;
+  if (!(eps >= 0.0f) || !std::isfinite(alpha)) return SSD_E_SHAPE;
+  // one workgroup per position: keep the grid's thread count below 2^32
+  if (d.B * d.L > (int64_t)1 << 24) return SSD_E_SHAPE;
+  if (empty) return SSD_OK;
+  return hip_status(ssd::launch_epilogue(d, shape->dtype, Y, corr, alpha, weight, eps, out,
+                                         (hipStream_t)stream));
+}
+
+int ssd_mean_correction(const ssd_shape* shape, const void* Y_ref, const void* Y_q, float* c,
+                        void* stream) {
+  Dims d;
+  bool empty;
+  int rc = check_shape(shape, &d, &empty);
+  if (rc) return rc;
+  if ((rc = check_ptrs({Y_ref, Y_q, c}))) return rc;
+  if (empty) return SSD_E_SHAPE;  // the mean of no positions is undefined
+  return hip_status(ssd::launch_mean_correction(d, shape->dtype, Y_ref, Y_q, c, (hipStream_t)stream));
+}
+
 size_t ssd_calibrate_workspace_bytes(const ssd_shape* shape) {
   Dims d;
   bool empty;

@@ -76,4 +76,10 @@ hipError_t launch_decode_step(const Dims& d, int dtype, bool int8, const void* X
                               const float* A, const void* B, const void* C, const float* D,
                               const ScalePtrs& sc, void* state, void* Y, hipStream_t st);
 
+// SSD epilogue: RMSNorm with the optional mean correction (k_epilogue.hip).
+hipError_t launch_epilogue(const Dims& d, int dtype, const void* Y, const float* corr, float alpha,
+                           const float* weight, float eps, void* out, hipStream_t st);
+hipError_t launch_mean_correction(const Dims& d, int dtype, const void* Yr, const void* Yq, float* c,
+                                  hipStream_t st);
+
 }  // namespace ssd

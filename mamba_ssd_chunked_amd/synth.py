@@ -172,6 +172,12 @@ def int8_state(w: Workload, batch: int, seed: int | None = None) -> np.ndarray:
     return rng.integers(-127, 128, size=(batch, w.nheads, w.headdim, w.dstate), dtype=np.int8)
 
 
+def norm_weight(w: Workload, seed: int | None = None) -> np.ndarray:
+    """RMSNorm weight [H, P] for the epilogue, 1 + 0.1 N(0, 1) (seeded; role 5)."""
+    rng = np.random.Generator(np.random.PCG64(1000 * w.wid + 5 if seed is None else seed))
+    return (1.0 + 0.1 * rng.standard_normal((w.nheads, w.headdim))).astype(np.float32)
+
+
 def as_f64(seq: dict, dtype: str) -> dict:
     """Widen every stored tensor of a sequence dict to float64 (exact)."""
     return {k: to_f64(v, dtype) for k, v in seq.items()}

@@ -66,6 +66,14 @@ same way on the GPU side):
       quantised with s_S; ChunkBMM and ChunkScan2 stay floating point on the
       unquantised B and C. The full method (the last row) adds the persistent
       INT8 state (Eq. 6) and the INT8 ChunkBMM.
+  R17 the RMSNorm after the SSD ("Overall framework") normalises the H*P
+      channels of each position, out = u / sqrt(mean(u^2) + eps) * weight,
+      with no gate (the pages name none) and eps given by the caller.
+  R18 the mean correction (Key design 4) is the per-channel mean of the
+      quantised output's error over the calibration positions, added with the
+      coefficient 0.15 ("Training strategy"). The pages correct the Out Proj
+      output; without its trained weights it is applied here to the SSD
+      output's own channels (H*P), before the RMSNorm.
 
 Where exactness is claimed, float64 matmuls are used on integer-valued
 operands whose partial sums stay below 2^53, so they are exact in any order.
@@ -584,6 +592,32 @@ def forward_recon(x, dt, A, B, C, D, scales: dict, chunk: int) -> dict:
     qpassed[:, c - 1] = saturate(rhaz(passed[:, c - 1] / s_S[None, :, :, None]), qm)
     return {"qB": qB, "qC": qC, "cumsum": cs, "qxs": qxs, "s32": s32, "S": S,
             "passed": passed, "qpassed": qpassed, "y": y.reshape(b, c * l, H, P)[:, :L]}
+
+
+# ---------------------------------------------------------------------------
+# The steps right after the SSD (R17, R18)
+# ---------------------------------------------------------------------------
+
+MEAN_CORRECTION_ALPHA = 0.15   # [SSDi8] "Training strategy": the correction coefficient
+
+
+def mean_correction(y_ref, y_q):
+    """[SSDi8] Key design 4: the c minimising ||Y - (Y' + c)||_F^2 over all
+    positions is the per-channel mean of the error, c*_ch = mean_i (Y - Y')_{i,ch}.
+    y_ref, y_q [b,L,H,P] float64. Returns c [H,P]."""
+    e = np.asarray(y_ref, np.float64) - np.asarray(y_q, np.float64)
+    return e.reshape(-1, *e.shape[2:]).mean(axis=0)
+
+
+def epilogue(y, corr, alpha, weight, eps):
+    """RMSNorm over the H*P channels of each position after the mean correction
+    (R17, R18): u = y + alpha c; out = u / sqrt(mean(u^2) + eps) * weight.
+    y [b,L,H,P]; corr, weight [H,P] (corr may be None). Float64."""
+    u = np.asarray(y, np.float64)
+    if corr is not None:
+        u = u + alpha * np.asarray(corr, np.float64)[None, None]
+    ms = np.mean(u * u, axis=(2, 3), keepdims=True)
+    return u / np.sqrt(ms + eps) * np.asarray(weight, np.float64)[None, None]
 
 
 def rel_max_err(y, ref) -> float:

@@ -207,3 +207,15 @@ def test_ablation_paths_validate():
     # the module calls and the decode step run the float and INT8 paths only
     assert L.LIB.ssd_chunk_state(b(sh), 2, A16, A16, A16, None, A16, None, None) == L.SSD_E_UNSUPPORTED
     assert fwd(sh, path=4) == L.SSD_E_UNSUPPORTED
+
+
+def test_epilogue_calls_validate():
+    b = ctypes.byref
+    sh = shape()
+    assert L.LIB.ssd_epilogue(b(sh), None, None, 0.15, A16, 1e-5, A16, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_epilogue(b(sh), A16, MIS, 0.15, A16, 1e-5, A16, None) == L.SSD_E_ALIGN
+    assert L.LIB.ssd_epilogue(b(sh), A16, None, 0.15, A16, -1.0, A16, None) == L.SSD_E_SHAPE
+    assert L.LIB.ssd_epilogue(b(sh), A16, None, float("nan"), A16, 1e-5, A16, None) == L.SSD_E_SHAPE
+    assert L.LIB.ssd_epilogue(b(shape(batch=0)), A16, None, 0.15, A16, 1e-5, A16, None) == L.SSD_OK
+    assert L.LIB.ssd_mean_correction(b(sh), A16, None, A16, None) == L.SSD_E_NULL
+    assert L.LIB.ssd_mean_correction(b(shape(seqlen=0)), A16, A16, A16, None) == L.SSD_E_SHAPE

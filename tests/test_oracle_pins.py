@@ -485,3 +485,41 @@ def test_qx_scale_pack_follows_the_pack_rule():
     px = O.scale_pack_x(a)
     ref = O.scale_pack(np.ones(1), np.ones(1), a, np.ones((2, 2)), nheads=2)
     assert np.array_equal(px["s_Xq"], ref["s_X"]) and np.array_equal(px["inv_Xq"], ref["inv_X"])
+
+
+# The steps after the SSD (R17, R18).
+def test_mean_correction_is_the_least_squares_optimum():
+    """The closed form of Key design 4: no other per-channel offset lowers
+    ||Y - (Y' + c)||^2 (checked along random directions and per channel), and
+    the corrected error has zero mean in every channel."""
+    rng = np.random.default_rng(11)
+    y = rng.standard_normal((2, 50, 3, 4)) * 3
+    yq = y + rng.standard_normal(y.shape) * 0.1 + rng.standard_normal((3, 4))[None, None] * 0.05
+    c = O.mean_correction(y, yq)
+    E = lambda cc: float(np.sum((y - (yq + cc[None, None])) ** 2))  # noqa: E731
+    e0 = E(c)
+    for _ in range(20):
+        d = rng.standard_normal(c.shape) * 1e-3
+        assert E(c + d) > e0 and E(c - d) > e0
+    assert np.abs((y - (yq + c[None, None])).mean(axis=(0, 1))).max() < 1e-12
+
+
+def test_epilogue_rmsnorm_properties():
+    """RMSNorm: with unit weight and eps = 0 each position has RMS exactly 1;
+    it is invariant to scaling a position; the weight multiplies channelwise;
+    the correction enters before the norm; eps damps small rows."""
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((2, 7, 3, 8))
+    one = np.ones((3, 8))
+    o = O.epilogue(y, None, 0.0, one, 0.0)
+    assert np.allclose(np.sqrt(np.mean(o * o, axis=(2, 3))), 1.0, atol=1e-14)
+    k = rng.uniform(0.5, 4.0, size=(2, 7, 1, 1))
+    assert np.allclose(O.epilogue(y * k, None, 0.0, one, 0.0), o, atol=1e-13)
+    wgt = rng.standard_normal((3, 8))
+    assert np.allclose(O.epilogue(y, None, 0.0, wgt, 0.0), o * wgt[None, None], atol=1e-14)
+    corr = rng.standard_normal((3, 8))
+    assert np.allclose(O.epilogue(y, corr, 0.15, one, 0.0),
+                       O.epilogue(y + 0.15 * corr[None, None], None, 0.0, one, 0.0), atol=1e-14)
+    tiny = 1e-4 * y
+    assert np.sqrt(np.mean(O.epilogue(tiny, None, 0.0, one, 1e-5) ** 2)) < 0.1
+    assert O.MEAN_CORRECTION_ALPHA == 0.15
