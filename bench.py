@@ -283,7 +283,7 @@ def bench_epilogue(torch, np, L, synth, w, y, y_ref, steps, warmup) -> dict:
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes}}
 
 
-CPU_SEQUENCES = 2   # sequences of the batch the CPU baseline runs (a bounded sample)
+CPU_SEQUENCES = 4   # sequences of the batch the CPU baseline runs (a bounded sample)
 
 
 def cpu_baseline(w, consts, ev) -> dict:

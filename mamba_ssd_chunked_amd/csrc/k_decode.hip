@@ -73,41 +73,6 @@ __device__ __forceinline__ uint32_t perm_pack4(int a, int b, int c, int d) {
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Packed 16-bit helpers of the Eq. 6 update (two state elements per lane op).
-typedef short v2s __attribute__((ext_vector_type(2)));
-
-// Two int8 codes from float values prepared by q8_pre, as int16 halves of one
-// dword: the second conversion writes its low 16 bits into the high half.
-__device__ __forceinline__ v2s cvt_pair(float c0, float c1) {
-  uint32_t d = (uint32_t)(int)c0;
-  asm("v_cvt_i32_f32_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
-      : "+v"(d) : "v"(c1));
-  return __builtin_bit_cast(v2s, d);
-}
-
-// Two signed bytes of w (picked by the permute selector into bits 15:8 and
-// 31:24) as sign-extended int16 halves.
-__device__ __forceinline__ v2s unpack_pair(uint32_t w, uint32_t sel) {
-  return __builtin_bit_cast(v2s, __builtin_amdgcn_perm(w, w, sel)) >> (short)8;
-}
-
-// RSH7(qd h) = (qd h + 64 + [qd h < 0 ? -1 : 0]) >> 7 per half. qd >= 0, so the
-// sign of h stands for the sign of the product (a zero product rounds to 0
-// either way); |qd h| <= 128 * 127 fits int16.
-__device__ __forceinline__ v2s rsh7_pair(v2s qd, v2s h) {
-  return (v2s)(qd * h + (short)64 + (h >> (short)15)) >> (short)7;
-}
-
-__device__ __forceinline__ v2s sat127_pair(v2s v) {
-  return __builtin_elementwise_min(__builtin_elementwise_max(v, (v2s){-127, -127}), (v2s){127, 127});
-}
-
-// Low bytes of the four int16 halves of (lo, hi) as one dword.
-__device__ __forceinline__ uint32_t pack_pairs(v2s lo, v2s hi) {
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
-                               0x06040200u);
-}
-
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // LDS of one wave: the per-position vectors of its head.

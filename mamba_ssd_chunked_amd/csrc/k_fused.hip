@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     const int kn = min(k + 1, d.c - 1);
 
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
-    uint32_t S8[PTW];
+    v2s S8a[PTW], S8b[PTW];  // local state codes n = 4 lg + {0, 1} and {2, 3} of each dword
     {
       v4i acc[PTW];
 #pragma unroll
@@ -576,10 +576,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
           const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
           *(int4*)(a.tap_s32 + so) = make_int4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         }
-        // requantise in registers (Key design 2)
+        // requantise in registers (Key design 2); the codes stay as int16 pairs
+        // for the packed Eq. 6 update
         const float mreq = SSl[2 * kP + p];
-        S8[j] = pack4(q8((float)acc[j][0] * mreq), q8((float)acc[j][1] * mreq),
-                      q8((float)acc[j][2] * mreq), q8((float)acc[j][3] * mreq));
+        S8a[j] = cvt_pair(q8_pre((float)acc[j][0] * mreq), q8_pre((float)acc[j][1] * mreq));
+        S8b[j] = cvt_pair(q8_pre((float)acc[j][2] * mreq), q8_pre((float)acc[j][3] * mreq));
       }
     }
 
@@ -746,20 +747,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     load_qc2(kn, lane, qc2);
 
     // ---- StatePassing (Eq. 6) in registers; publish H8 for the next ChunkScan1 ----
+    const v2s qd2 = {(short)qd, (short)qd};
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       const int p = 16 * (pt0 + j) + l16;
       if (k == 0 && !has_init) {
-        H8[j] = S8[j];
+        H8[j] = pack_pairs(S8a[j], S8b[j]);
       } else {
-        int o[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = sat127(byte_s(S8[j], r) + rsh7_fast(qd * byte_s(H8[j], r)));
-        H8[j] = pack4(o[0], o[1], o[2], o[3]);
+        // two elements per lane op: RSH7 of the int16 products, add, saturate
+        const v2s r01 = rsh7_pair(qd2, unpack_pair(H8[j], 0x010c000cu));
+        const v2s r23 = rsh7_pair(qd2, unpack_pair(H8[j], 0x030c020cu));
+        H8[j] = pack_pairs(sat127_pair(S8a[j] + r01), sat127_pair(S8b[j] + r23));
       }
       *(uint32_t*)&H8l[b_off<NS>(p, 16 * nt_own + 4 * lg)] = H8[j];
       const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kP + p) * NS + 16 * nt_own + 4 * lg;
-      if (TAPS && a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = S8[j];
+      if (TAPS && a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = pack_pairs(S8a[j], S8b[j]);
       if (TAPS && a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
     qd_word = pf.qd;
