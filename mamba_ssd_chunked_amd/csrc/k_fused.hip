@@ -282,11 +282,11 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
   const uint32_t lim = (uint32_t)min((int64_t)LC - 1, d.L - 1 - t0);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    pf.x[r] = *(const uint4*)(xk + (min(lo.q4 + r, lim) * (uint32_t)rowB + lo.xc));
+    pf.x[r] = *(const uint4*)(xk + (__umul24(min(lo.q4 + r, lim), rowB) + lo.xc));
   if constexpr (sizeof(T) == 4)
     pf.vd = *(const uint32_t*)(dtk + min(lo.sv, lim) * (uint32_t)(d.H * sizeof(T)));
   else
-    pf.vd = *(const u16*)(dtk + min(lo.sv, lim) * (uint32_t)(d.H * sizeof(T)));
+    pf.vd = *(const u16*)(dtk + __umul24(min(lo.sv, lim), (uint32_t)(d.H * sizeof(T))));
   pf.lut = *(const float4*)((const char*)(a.lut + cs0) + lo.lut);
   pf.va = *(const float*)((const char*)(a.dAcs + cs0) + 4 * lo.sv);
   const int64_t qi = (b * d.H + h) * d.c + k;
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
-      const int8_t* src = qcb + (uint32_t)((16 * i + l16) * d.G * NS + 16 * lg);
+      const int8_t* src = qcb + (__umul24(16 * i + l16, d.G * NS) + 16 * lg);
 #pragma unroll
       for (int kn = 0; kn < KN; ++kn) qc[rr][kn] = *(const v4i*)(src + 64 * kn);
     }
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       }
       // epilogue: lane holds s = s_row and p = 16 pt + 4 lg + r
       const int64_t t = t0 + s_row;
-      char* yrow = (char*)ybase + (uint32_t)(((int)t * H * kP + 4 * lg) * (int)sizeof(T));
+      char* yrow = (char*)ybase + (__umul24((uint32_t)t, H * kP * (int)sizeof(T)) + 4 * lg * (int)sizeof(T));
 #pragma unroll
       for (int jp = 0; jp < PW; ++jp) {
         const int pt = pt_base + jp;
@@ -912,12 +912,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     const int q = it / C8N, c8 = c8b + it % C8N;
     const T* xk = Xb + (int64_t)t0 * rowX + 8 * c8;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pf.x[r] = *(const uint4*)(xk + (uint32_t)(min(4 * q + r, lim) * rowX));
+    for (int r = 0; r < 4; ++r) pf.x[r] = *(const uint4*)(xk + __umul24(min(4 * q + r, lim), rowX));
     const int64_t cs0 = ((b * H + h) * d.c + kc) * (int64_t)LC;
     pf.lut = *(const float4*)(a.lut + cs0 + 4 * q);
     const int sv = tid % LC;
     pf.va = a.dAcs[cs0 + sv];
-    pf.vd = ((const u16*)a.dt)[((b * d.L + t0) * H + h) + (uint32_t)(min(sv, lim) * H)];
+    pf.vd = ((const u16*)a.dt)[((b * d.L + t0) * H + h) + __umul24(min(sv, lim), H)];
   };
   const auto stage_store = [&](int kc, int tid, const Pf& pf) {
     const int t0 = kc * LC;
@@ -976,7 +976,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       const int byte = 1024 * gi + 16 * lane;
       const int r = byte / (2 * NS), pc = (byte % (2 * NS)) / 16;
       const int c = pc ^ (r & msk);
-      __builtin_amdgcn_global_load_lds((const void*)(src0 + (uint32_t)(min(r, lim) * rowB + 8 * c)),
+      __builtin_amdgcn_global_load_lds((const void*)(src0 + (__umul24(min(r, lim), rowB) + 8 * c)),
                                        (__attribute__((address_space(3))) void*)((char*)s_B + 1024 * gi), 16, 0, 0);
     }
   };
@@ -989,7 +989,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
-      const T* src = c0 + (uint32_t)(min(16 * i + l16, lim) * rowB + 8 * lg);
+      const T* src = c0 + (__umul24(min(16 * i + l16, lim), rowB) + 8 * lg);
 #pragma unroll
       for (int kn = 0; kn < KNF; ++kn) cf[rr][kn] = *(const uint4*)(src + 32 * kn);
     }
@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
           acc[jp] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, i >> 1, lg)]), wf, acc[jp]);
       }
       const int64_t t = t0 + s_row;
-      char* yrow = (char*)ybase + (uint32_t)(((int)t * H * kP + 4 * lg) * 2);
+      char* yrow = (char*)ybase + (__umul24((uint32_t)t, H * kP * 2) + 4 * lg * 2);
 #pragma unroll
       for (int jp = 0; jp < PW; ++jp) {
         const int pt = pt_base + jp;
@@ -1291,6 +1291,9 @@ int cu_count() {
 }
 
 bool fused_supported(const Dims& d, int dtype, bool int8) {
+  // row strides (bytes) and the position index enter 24-bit multiplies
+  if ((int64_t)d.H * d.P * 4 >= (1 << 24) || (int64_t)d.G * d.N * 4 >= (1 << 24)) return false;
+  if (d.L >= (1 << 24)) return false;
   if (!int8) {
     if (dtype != DT_F16 || d.P != kP) return false;
     if (d.N != 64 && d.N != 128) return false;
