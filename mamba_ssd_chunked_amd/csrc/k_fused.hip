@@ -780,13 +780,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 }
 
 // ===========================================================================
-// Fused float forward (fp16 inputs). The same per-head walk over the chunks as
-// the INT8 kernel, with every contraction on fp16 MFMA (fp32 accumulation):
+// Fused float forward (fp16 or bf16 inputs). The same per-head walk over the
+// chunks as the INT8 kernel, with every contraction on MFMA in the input's
+// 16-bit type (fp32 accumulation):
 //   ChunkState   S^T[n,p] = sum_s B^T[n,s] (LUT x)^T[s,p]  (B^T by transposing
-//                LDS reads of the B rows, LUT x rounded once to fp16);
+//                LDS reads of the B rows, LUT x rounded to the 16-bit type);
 //   StatePassing H_k = exp(a_{k,l-1}) H_{k-1} + S_k, in fp32 registers;
-//   ChunkScan1   Y_off = exp(a_s) sum_n C[s,n] H_{k-1}[p,n] (H as fp16 in LDS);
-//   ChunkBMM/Scan2 as in the INT8 kernel, CB from fp16 B and C rows.
+//   ChunkScan1   Y_off = exp(a_s) sum_n C[s,n] H_{k-1}[p,n] (H as 16-bit in LDS);
+//   ChunkBMM/Scan2 as in the INT8 kernel, CB from the B and C rows.
+// bf16 keeps 8 significant bits, so with bf16 inputs the computed operands (LUT
+// B in ChunkState, the Scan2 weights and the state copy ChunkScan1 reads) are
+// carried as hi + lo pairs (two MFMAs, about 16 significant bits); B, C and x
+// are exact inputs.
 // ===========================================================================
 
 // fp16 tiles [rows][W] (element offsets); 16-byte chunks XOR-swizzled with the
@@ -811,10 +816,21 @@ __device__ __forceinline__ v8s v8s_join(v4s lo, v4s hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ FragF<DT_F16> frag_u4(const uint4& v) {
-  FragF<DT_F16> f;
-  f.v = __builtin_bit_cast(v8h, v);
+template <int DT>
+__device__ __forceinline__ FragF<DT> frag_u4(const uint4& v) {
+  FragF<DT> f;
+  f.v = __builtin_bit_cast(decltype(f.v), v);
   return f;
+}
+
+// 16-bit storage bits of a float, and its rounding residual (for hi + lo pairs)
+template <int DT>
+__device__ __forceinline__ uint32_t bits16(float v) {
+  return (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(v));
+}
+template <int DT>
+__device__ __forceinline__ float resid16(float v) {
+  return v - Store<DT>::to_f(Store<DT>::from_f(v));
 }
 
 struct FusedFArgs {
@@ -835,10 +851,11 @@ struct FusedFArgs {
 
 // PW = 4: a whole head per workgroup; PW = 2: p tiles 2 ph, 2 ph + 1 of a head
 // (the partial last round, as in the INT8 kernel).
-template <int LC, int NS, int PW>
+template <int DT, int LC, int NS, int PW>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
-  typedef _Float16 T;
-  typedef FragF<DT_F16> F;
+  typedef typename Store<DT>::T T;
+  typedef FragF<DT> F;
+  constexpr bool SPLIT = DT == DT_BF16;  // hi + lo pairs for LUT x and the weights
   constexpr int RT = LC / 16;            // row tiles of the chunk
   constexpr int NT = NS / 16;            // n tiles of the state
   constexpr int PTW = PW * NT / kWaves;  // p tiles per wave in ChunkState / StatePassing
@@ -849,13 +866,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   static_assert(XI <= kThreads, "tile split");
 
   __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];  // x^T (xT_pair layout)
-  __shared__ __attribute__((aligned(16))) u16 s_xs[kP * LC];  // fp16(LUT x)^T [p][s] (h_off<LC>)
+  // 16-bit (LUT x)^T [p][s] (h_off<LC>); with bf16 the LUT goes on the B side
+  __shared__ __attribute__((aligned(16))) u16 s_xs[SPLIT ? 8 : kP * LC];
   __shared__ __attribute__((aligned(16))) u16 s_B[LC * NS];   // B rows [s][n] (h_off<NS>)
-  __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];   // fp16 passed state [p][n] (h_off<NS>)
-  __shared__ __attribute__((aligned(16))) float s_vec[2 * LC];  // a*log2(e), dt
+  __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];   // 16-bit passed state [p][n] (h_off<NS>)
+  __shared__ __attribute__((aligned(16))) u16 s_H_lo[SPLIT ? kP * NS : 8];  // its residual (bf16)
+  __shared__ __attribute__((aligned(16))) float s_vec[(SPLIT ? 3 : 2) * LC];  // a*log2(e), dt (, LUT)
   __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
   const float* vA2 = s_vec;
   const float* vDt = s_vec + LC;
+  const float* vLut = s_vec + 2 * LC;  // bf16 only
 
   const Dims& d = a.d;
   int64_t slot;
@@ -903,6 +923,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     uint4 x[4];
     float4 lut;
     float va;
+    float vl;  // LUT of position tid % LC (bf16 only)
     uint32_t vd;
   };
   const auto stage_load = [&](int kc, int tid, Pf& pf) {
@@ -917,6 +938,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     pf.lut = *(const float4*)(a.lut + cs0 + 4 * q);
     const int sv = tid % LC;
     pf.va = a.dAcs[cs0 + sv];
+    if constexpr (SPLIT) pf.vl = a.lut[cs0 + sv];
     pf.vd = ((const u16*)a.dt)[((b * d.L + t0) * H + h) + __umul24(min(sv, lim), H)];
   };
   const auto stage_store = [&](int kc, int tid, const Pf& pf) {
@@ -939,28 +961,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
         *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) =
             make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u), __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
       }
-      // fp16(fl32(LUT x)) for 4 rows of each p
-      const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
+      // fl32(LUT x) in the 16-bit type for 4 rows of each p (fp16 only)
+      if constexpr (!SPLIT) {
+        const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v[4];
+        for (int e = 0; e < 8; ++e) {
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t dw = (e >> 1) == 0 ? xr[r].x : (e >> 1) == 1 ? xr[r].y : (e >> 1) == 2 ? xr[r].z : xr[r].w;
-          const uint32_t hv = (e & 1) ? (dw >> 16) : (dw & 0xffffu);
-          v[r] = __builtin_fmaf(lutv[r], (float)__builtin_bit_cast(_Float16, (u16)hv), 0.0f);
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t dw = (e >> 1) == 0 ? xr[r].x : (e >> 1) == 1 ? xr[r].y : (e >> 1) == 2 ? xr[r].z : xr[r].w;
+            const uint32_t hv = (e & 1) ? (dw >> 16) : (dw & 0xffffu);
+            v[r] = __builtin_fmaf(lutv[r], Store<DT>::to_f(__builtin_bit_cast(T, (u16)hv)), 0.0f);
+          }
+          *(uint2*)&s_xs[h_off<LC>(8 * c8 + e, 4 * q)] =
+              make_uint2(bits16<DT>(v[0]) | (bits16<DT>(v[1]) << 16), bits16<DT>(v[2]) | (bits16<DT>(v[3]) << 16));
         }
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)v[0]) |
-                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v[1]) << 16);
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)v[2]) |
-                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v[3]) << 16);
-        *(uint2*)&s_xs[h_off<LC>(8 * c8 + e, 4 * q)] = make_uint2(lo, hi);
       }
     }
     if (tid < LC) {
       s_vec[tid] = pf.va * kLog2e;
-      const float dtv = (float)__builtin_bit_cast(_Float16, (u16)pf.vd);
+      const float dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)pf.vd));
       s_vec[LC + tid] = (t0 + tid < (int)d.L) ? dtv : 0.f;
+      if constexpr (SPLIT) s_vec[2 * LC + tid] = pf.vl;
     }
   };
   // B rows of chunk kc straight into LDS (1 KB per copy; lane L fills bytes
@@ -1008,12 +1030,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       Hs[j][1] = v.y;
       Hs[j][2] = v.z;
       Hs[j][3] = v.w;
-      if (has_init) {  // fp16 copy for chunk 0's ChunkScan1
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)v.x) |
-                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v.y) << 16);
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)v.z) |
-                            ((uint32_t)__builtin_bit_cast(u16, (_Float16)v.w) << 16);
-        *(uint2*)&s_H[h_off<NS>(p, 16 * nt_own + 4 * lg)] = make_uint2(lo, hi);
+      if (has_init) {  // 16-bit copy (bf16: hi + lo) for chunk 0's ChunkScan1
+        const int ho = h_off<NS>(p, 16 * nt_own + 4 * lg);
+        *(uint2*)&s_H[ho] =
+            make_uint2(bits16<DT>(v.x) | (bits16<DT>(v.y) << 16), bits16<DT>(v.z) | (bits16<DT>(v.w) << 16));
+        if constexpr (SPLIT)
+          *(uint2*)&s_H_lo[ho] = make_uint2(bits16<DT>(resid16<DT>(v.x)) | (bits16<DT>(resid16<DT>(v.y)) << 16),
+                                            bits16<DT>(resid16<DT>(v.z)) | (bits16<DT>(resid16<DT>(v.w)) << 16));
       }
     }
   }
@@ -1043,17 +1066,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     for (int j = 0; j < PTW; ++j) sacc[j] = v4f{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KSF; ++ks) {
-      // A: B^T rows n = 16 nt_own + l16, K = s0 .. s0 + 7 (two reads of 4 rows)
-      const int s0 = 32 * ks + 8 * lg;
       const int cn = 16 * nt_own + 4 * (l16 & 3);
-      const v4s lo = lds_tr16(s_B + h_off<NS>(s0 + (l16 >> 2), cn));
-      const v4s hi = lds_tr16(s_B + h_off<NS>(s0 + 4 + (l16 >> 2), cn));
-      F fa;
-      fa.v = __builtin_bit_cast(v8h, v8s_join(lo, hi));
+      if constexpr (!SPLIT) {
+        // A: B^T rows n = 16 nt_own + l16, K = s0 .. s0 + 7 (two reads of 4 rows)
+        const int s0 = 32 * ks + 8 * lg;
+        const v4s lo = lds_tr16(s_B + h_off<NS>(s0 + (l16 >> 2), cn));
+        const v4s hi = lds_tr16(s_B + h_off<NS>(s0 + 4 + (l16 >> 2), cn));
+        F fa;
+        fa.v = __builtin_bit_cast(decltype(fa.v), v8s_join(lo, hi));
 #pragma unroll
-      for (int j = 0; j < PTW; ++j) {
-        const F fb = frag16<DT_F16>(&s_xs[h_off<LC>(16 * (pt0 + j) + l16, s0)]);
-        sacc[j] = F::mma(fa, fb, sacc[j]);
+        for (int j = 0; j < PTW; ++j) {
+          const F fb = frag16<DT>(&s_xs[h_off<LC>(16 * (pt0 + j) + l16, s0)]);
+          sacc[j] = F::mma(fa, fb, sacc[j]);
+        }
+      } else {
+        // bf16: S^T = (B LUT)^T x, with B LUT formed here as hi + lo and x read
+        // exactly from x^T. K order of x^T's operand: s = 32 ks + 4 lg + (0..3)
+        // and 32 ks + 16 + 4 lg + (0..3); the two transposing reads follow it.
+        const int sA = 32 * ks + 4 * lg, sB = sA + 16;
+        const v4s lo = lds_tr16(s_B + h_off<NS>(sA + (l16 >> 2), cn));
+        const v4s hi = lds_tr16(s_B + h_off<NS>(sB + (l16 >> 2), cn));
+        const float4 la = *(const float4*)&vLut[sA];
+        const float4 lb = *(const float4*)&vLut[sB];
+        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        F fh, fl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const short bs = e < 4 ? lo[e] : hi[e - 4];
+          const float v = Store<DT>::to_f(__builtin_bit_cast(T, (u16)bs)) * lv[e];
+          fh.set(e, v);
+          fl.set(e, resid16<DT>(v));
+        }
+#pragma unroll
+        for (int j = 0; j < PTW; ++j) {
+          const F fb = frag16<DT>(&s_xT[xT_pair<LC>(16 * (pt0 + j) + l16, ks, lg)]);
+          sacc[j] = F::mma(fh, fb, sacc[j]);
+          sacc[j] = F::mma(fl, fb, sacc[j]);
+        }
       }
     }
 #pragma unroll
@@ -1073,7 +1122,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       const int s_row = 16 * i + l16;
       F cr[KNF];
 #pragma unroll
-      for (int kn = 0; kn < KNF; ++kn) cr[kn] = frag_u4(rr ? cf2[1][kn] : cf2[0][kn]);
+      for (int kn = 0; kn < KNF; ++kn) cr[kn] = frag_u4<DT>(rr ? cf2[1][kn] : cf2[0][kn]);
       // V_i[s'] = exp(a_{16i} - a_s') dt_s' for s' < 16 i
       const float a_ref = vA2[16 * i];
       for (int sp = lane; sp < 16 * i; sp += kWave) Vw[sp] = fast_exp2(a_ref - vA2[sp]) * vDt[sp];
@@ -1089,24 +1138,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
         v4f cbA = v4f{0, 0, 0, 0}, cbB = v4f{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < KNF; ++kn)
-          cbA = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * jA + l16, 32 * kn + 8 * lg)]), cr[kn], cbA);
+          cbA = F::mma(frag16<DT>(&s_B[h_off<NS>(16 * jA + l16, 32 * kn + 8 * lg)]), cr[kn], cbA);
 #pragma unroll
         for (int kn = 0; kn < KNF; ++kn)
-          cbB = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * jB + l16, 32 * kn + 8 * lg)]), cr[kn], cbB);
+          cbB = F::mma(frag16<DT>(&s_B[h_off<NS>(16 * jB + l16, 32 * kn + 8 * lg)]), cr[kn], cbB);
         const float4 vA = *(const float4*)&Vw[16 * jA + 4 * lg];
         const float4 vB = *(const float4*)&Vw[16 * jB + 4 * lg];
-        F wf;
-        wf.set(0, cbA[0] * vA.x);
-        wf.set(1, cbA[1] * vA.y);
-        wf.set(2, cbA[2] * vA.z);
-        wf.set(3, cbA[3] * vA.w);
-        wf.set(4, cbB[0] * vB.x);
-        wf.set(5, cbB[1] * vB.y);
-        wf.set(6, cbB[2] * vB.z);
-        wf.set(7, cbB[3] * vB.w);
+        const float wv[8] = {cbA[0] * vA.x, cbA[1] * vA.y, cbA[2] * vA.z, cbA[3] * vA.w,
+                             cbB[0] * vB.x, cbB[1] * vB.y, cbB[2] * vB.z, cbB[3] * vB.w};
+        F wf, wl;
 #pragma unroll
-        for (int jp = 0; jp < PW; ++jp)
-          acc[jp] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, jA >> 1, lg)]), wf, acc[jp]);
+        for (int e = 0; e < 8; ++e) {
+          wf.set(e, wv[e]);
+          if constexpr (SPLIT) wl.set(e, resid16<DT>(wv[e]));
+        }
+#pragma unroll
+        for (int jp = 0; jp < PW; ++jp) {
+          const F xf = frag16<DT>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, jA >> 1, lg)]);
+          acc[jp] = F::mma(xf, wf, acc[jp]);
+          if constexpr (SPLIT) acc[jp] = F::mma(xf, wl, acc[jp]);
+        }
       }
       const float a_s = vA2[s_row];
       const float us = fast_exp2(a_s - a_ref);
@@ -1120,8 +1171,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
           const int pt = pt_base + jp;
           v4f acc1 = v4f{0, 0, 0, 0};
 #pragma unroll
-          for (int kn = 0; kn < KNF; ++kn)
-            acc1 = F::mma(frag16<DT_F16>(&s_H[h_off<NS>(16 * pt + l16, 32 * kn + 8 * lg)]), cr[kn], acc1);
+          for (int kn = 0; kn < KNF; ++kn) {
+            const int ho = h_off<NS>(16 * pt + l16, 32 * kn + 8 * lg);
+            acc1 = F::mma(frag16<DT>(&s_H[ho]), cr[kn], acc1);
+            if constexpr (SPLIT) acc1 = F::mma(frag16<DT>(&s_H_lo[ho]), cr[kn], acc1);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[jp][r] = fmaf(acc1[r], eo, acc[jp][r]);
         }
@@ -1132,11 +1186,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
         v4f cbD = v4f{0, 0, 0, 0}, cbL = v4f{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < KNF; ++kn)
-          cbD = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * i + l16, 32 * kn + 8 * lg)]), cr[kn], cbD);
+          cbD = F::mma(frag16<DT>(&s_B[h_off<NS>(16 * i + l16, 32 * kn + 8 * lg)]), cr[kn], cbD);
         if (hd) {
 #pragma unroll
           for (int kn = 0; kn < KNF; ++kn)
-            cbL = F::mma(frag16<DT_F16>(&s_B[h_off<NS>(16 * jL + l16, 32 * kn + 8 * lg)]), cr[kn], cbL);
+            cbL = F::mma(frag16<DT>(&s_B[h_off<NS>(16 * jL + l16, 32 * kn + 8 * lg)]), cr[kn], cbL);
         }
         const float4 ad = *(const float4*)&vA2[16 * i + 4 * lg];
         const float4 dd = *(const float4*)&vDt[16 * i + 4 * lg];
@@ -1154,28 +1208,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
           wd[r] = wv;
           wl[r] = cbL[r] * vLv[r];
         }
-        F wf;
+        F wf, wlo;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          wf.set(r, hd ? wl[r] : wd[r]);
-          wf.set(r + 4, hd ? wd[r] : 0.f);
+          const float v0 = hd ? wl[r] : wd[r], v1 = hd ? wd[r] : 0.f;
+          wf.set(r, v0);
+          wf.set(r + 4, v1);
+          if constexpr (SPLIT) {
+            wlo.set(r, resid16<DT>(v0));
+            wlo.set(r + 4, resid16<DT>(v1));
+          }
         }
 #pragma unroll
-        for (int jp = 0; jp < PW; ++jp)
-          acc[jp] = F::mma(frag16<DT_F16>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, i >> 1, lg)]), wf, acc[jp]);
+        for (int jp = 0; jp < PW; ++jp) {
+          const F xf = frag16<DT>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, i >> 1, lg)]);
+          acc[jp] = F::mma(xf, wf, acc[jp]);
+          if constexpr (SPLIT) acc[jp] = F::mma(xf, wlo, acc[jp]);
+        }
       }
       const int64_t t = t0 + s_row;
       char* yrow = (char*)ybase + (__umul24((uint32_t)t, H * kP * 2) + 4 * lg * 2);
 #pragma unroll
       for (int jp = 0; jp < PW; ++jp) {
         const int pt = pt_base + jp;
-        if (t < d.L) {
-          const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][0]) |
-                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][1]) << 16);
-          const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][2]) |
-                              ((uint32_t)__builtin_bit_cast(u16, (_Float16)acc[jp][3]) << 16);
-          *(uint2*)(yrow + 32 * pt) = make_uint2(lo, hi);
-        }
+        if (t < d.L)
+          *(uint2*)(yrow + 32 * pt) = make_uint2(bits16<DT>(acc[jp][0]) | (bits16<DT>(acc[jp][1]) << 16),
+                                                 bits16<DT>(acc[jp][2]) | (bits16<DT>(acc[jp][3]) << 16));
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -1184,18 +1242,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     dma_B(kn1, lane);
     load_C(kn1, lane, cf2);
 
-    // ---- StatePassing in fp32 registers; fp16 copy for the next ChunkScan1 ----
+    // ---- StatePassing in fp32 registers; 16-bit copy for the next ChunkScan1 ----
     const float decay = fast_exp2(alast2);
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Hs[j][r] = (k == 0 && !has_init) ? sacc[j][r] : fmaf(decay, Hs[j][r], sacc[j][r]);
       const int p = 16 * (pt0 + j) + l16;
-      const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][0]) |
-                          ((uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][1]) << 16);
-      const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][2]) |
-                          ((uint32_t)__builtin_bit_cast(u16, (_Float16)Hs[j][3]) << 16);
-      *(uint2*)&s_H[h_off<NS>(p, 16 * nt_own + 4 * lg)] = make_uint2(lo, hi);
+      const int ho = h_off<NS>(p, 16 * nt_own + 4 * lg);
+      *(uint2*)&s_H[ho] = make_uint2(bits16<DT>(Hs[j][0]) | (bits16<DT>(Hs[j][1]) << 16),
+                                     bits16<DT>(Hs[j][2]) | (bits16<DT>(Hs[j][3]) << 16));
+      if constexpr (SPLIT)
+        *(uint2*)&s_H_lo[ho] =
+            make_uint2(bits16<DT>(resid16<DT>(Hs[j][0])) | (bits16<DT>(resid16<DT>(Hs[j][1])) << 16),
+                       bits16<DT>(resid16<DT>(Hs[j][2])) | (bits16<DT>(resid16<DT>(Hs[j][3])) << 16));
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1254,11 +1314,11 @@ hipError_t launch_split(Args fa, hipStream_t st) {
   return hipSuccess;
 }
 
-template <int LC, int NS>
+template <int DT, int LC, int NS>
 struct FloatLaunch {
   template <int PW>
   static hipError_t launch(const FusedFArgs& fa, int64_t blocks, hipStream_t st) {
-    hipLaunchKernelGGL((k_fused_f16<LC, NS, PW>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+    hipLaunchKernelGGL((k_fused_f16<DT, LC, NS, PW>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
     return hipGetLastError();
   }
 };
@@ -1295,7 +1355,7 @@ bool fused_supported(const Dims& d, int dtype, bool int8) {
   if ((int64_t)d.H * d.P * 4 >= (1 << 24) || (int64_t)d.G * d.N * 4 >= (1 << 24)) return false;
   if (d.L >= (1 << 24)) return false;
   if (!int8) {
-    if (dtype != DT_F16 || d.P != kP) return false;
+    if ((dtype != DT_F16 && dtype != DT_BF16) || d.P != kP) return false;
     if (d.N != 64 && d.N != 128) return false;
     if (d.l != 128 && d.l != 256) return false;
     if (d.B * d.H > (int64_t)1 << 30) return false;
@@ -1336,10 +1396,16 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
     if (e != hipSuccess) return e;
     const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (const float*)initial_state,
                         (float*)final_state, 0, 0};
-    if (d.l == 256 && d.N == 128) return launch_split<FloatLaunch<256, 128>>(fa, st);
-    if (d.l == 256) return launch_split<FloatLaunch<256, 64>>(fa, st);
-    if (d.N == 128) return launch_split<FloatLaunch<128, 128>>(fa, st);
-    return launch_split<FloatLaunch<128, 64>>(fa, st);
+    if (dtype == DT_F16) {
+      if (d.l == 256 && d.N == 128) return launch_split<FloatLaunch<DT_F16, 256, 128>>(fa, st);
+      if (d.l == 256) return launch_split<FloatLaunch<DT_F16, 256, 64>>(fa, st);
+      if (d.N == 128) return launch_split<FloatLaunch<DT_F16, 128, 128>>(fa, st);
+      return launch_split<FloatLaunch<DT_F16, 128, 64>>(fa, st);
+    }
+    if (d.l == 256 && d.N == 128) return launch_split<FloatLaunch<DT_BF16, 256, 128>>(fa, st);
+    if (d.l == 256) return launch_split<FloatLaunch<DT_BF16, 256, 64>>(fa, st);
+    if (d.N == 128) return launch_split<FloatLaunch<DT_BF16, 128, 128>>(fa, st);
+    return launch_split<FloatLaunch<DT_BF16, 128, 64>>(fa, st);
   }
   const size_t Lp = (size_t)d.c * d.l;
   const size_t qbc = (size_t)d.B * Lp * d.G * d.N;
