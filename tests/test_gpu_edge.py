@@ -1,0 +1,94 @@
+"""Edge cases of ssd_forward on the GPU against the oracle: degenerate decays,
+the shortest sequences around a chunk boundary, and the empty problem.
+
+Degenerate decays: heads with A = 0 (every decay is 1: Q(Decay) = 128, so Eq. 6
+is the saturating prefix sum of the local states) and heads with A = -1e4
+(every decay underflows to 0: Q(Decay) = 0, the passed state is the local one
+and the output memoryless), beside ordinary heads. INT8 integers bit for bit,
+outputs within the paths' tolerances (2e-2 float against float64, 5e-2 INT8
+against the INT8 method).
+"""
+import numpy as np
+import pytest
+
+from mamba_ssd_chunked_amd import synth
+from oracle import ssd_oracle as O
+from tests import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_both(L, torch, w, consts, ev):
+    e = synth.as_f64(ev, w.dtype)
+    cal = [synth.as_f64(s, w.dtype) for s in synth.calibration_sequences(w, consts, seqlen=max(w.seqlen, 64))]
+    am = O.calibrate(cal, consts["A"], w.ngroups, w.chunk)
+    sc = O.scale_pack(am["B"], am["C"], am["Xs"], am["S"], w.nheads)
+    r8 = O.forward_int8(e["x"], e["dt"], consts["A"], e["B"], e["C"], consts["D"], sc, w.chunk)
+    yf = O.chunked(e["x"], e["dt"], consts["A"], e["B"], e["C"], consts["D"], w.chunk)[0]
+    d = {k: H.to_dev(v, w.dtype) for k, v in ev.items()}
+    A = torch.from_numpy(consts["A"]).cuda()
+    D = torch.from_numpy(consts["D"]).cuda()
+    sh = H.shape_of(L, w)
+    y8 = torch.empty_like(d["x"])
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
+    stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
+    taps = {"passed": torch.empty(stshape, dtype=torch.int8, device="cuda")}
+    L.ssd_forward(sh, L.SSD_PATH_INT8, d["x"], d["dt"], A, d["B"], d["C"], D, L.ScalePack(sc), y8,
+                  final_state=fin, taps=taps)
+    y32 = torch.empty_like(d["x"])
+    L.ssd_forward(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], A, d["B"], d["C"], D, None, y32)
+    torch.cuda.synchronize()
+    return r8, yf, y8, fin, taps, y32
+
+
+@pytest.mark.parametrize("name", ["f16_ragged", "w0", "bf16_n64_l128"])
+def test_degenerate_decays(gpu_lib, name):
+    import torch
+    L = gpu_lib
+    w = H.CASES[name]
+    print(f"degenerate decays {name}", flush=True)
+    consts = synth.layer_constants(w)
+    A = consts["A"].copy()
+    A[0] = 0.0
+    A[-1] = -1e4
+    consts = dict(consts, A=A)
+    ev = synth.evaluation_batch(w, consts)
+    r8, yf, y8, fin, taps, y32 = _run_both(L, torch, w, consts, ev)
+    qd = r8["cumsum"]["qdecay"]
+    assert (qd[:, 0] == 128).all() and (qd[:, -1] == 0).all()
+    assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
+    assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
+    assert H.chan_err(H.f64(y8), r8["y"], w.dtype) <= 5e-2
+    assert H.chan_err(H.f64(y32), yf, w.dtype) <= 2e-2
+
+
+@pytest.mark.parametrize("seqlen", [1, 17, 255, 256, 257])
+def test_short_sequences(gpu_lib, seqlen):
+    """One position, a partial chunk, exactly one chunk, one past it (the
+    fused kernels at chunk 256)."""
+    import torch
+    L = gpu_lib
+    w = H.CASES["f16_ragged"].replace(seqlen=seqlen)
+    print(f"short sequence L={seqlen}", flush=True)
+    consts = synth.layer_constants(w)
+    ev = synth.evaluation_batch(w, consts)
+    r8, yf, y8, fin, taps, y32 = _run_both(L, torch, w, consts, ev)
+    assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
+    assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
+    assert H.chan_err(H.f64(y8), r8["y"], w.dtype) <= 5e-2
+    assert H.chan_err(H.f64(y32), yf, w.dtype) <= 2e-2
+
+
+def test_empty_problem_writes_nothing(gpu_lib):
+    import torch
+    L = gpu_lib
+    w = H.CASES["f16_ragged"]
+    for batch, seqlen in ((0, 640), (2, 0)):
+        sh = L.make_shape(batch, seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+        buf = torch.full((64,), 7.0, dtype=torch.float16, device="cuda")
+        A = torch.zeros(w.nheads, dtype=torch.float32, device="cuda")
+        for path in (L.SSD_PATH_FLOAT, L.SSD_PATH_INT8):
+            sc = L.ScalePack({k: np.ones(1024, np.float32) for k in L.ScalePack.ORDER})
+            L.ssd_forward(sh, path, buf, buf, A, buf, buf, A, sc, buf)
+        torch.cuda.synchronize()
+        assert bool((buf == 7.0).all())
