@@ -330,17 +330,25 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS, PW> PF;
   const int t0 = k * LC;
+  // Every prefetched register passes through an empty asm here, in all lanes:
+  // nothing that uses the values (unpacking, conversion) can then be scheduled
+  // right after the loads, which would make the prefetch wait for memory; and
+  // no lane leaves the staging below with a load still outstanding (a lane that
+  // skipped a branch would carry one, and where the paths merge the compiler
+  // would then wait for every outstanding load, the next chunk's Q(B) copies
+  // and Q(C) rows included).
+  uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
+  float4 lutp = pf.lut;
+  float vap = pf.va;
+  uint32_t vdp = pf.vd;
+  asm volatile("" : "+v"(lutp.x), "+v"(lutp.y), "+v"(lutp.z), "+v"(lutp.w), "+v"(vap), "+v"(vdp));
   if (tid < PF::XI) {
     const int q = tid / PF::C8N, c8 = c8base + tid % PF::C8N;
     // Rows past L (ragged last chunk) hold copies of row L-1 (finite values):
     // their LUT_state is 0, so their Q(X_scaled) is 0, and ChunkScan2 never
     // pairs them with a valid output row (causal mask) and gives them weight 0.
-    // The loaded values pass through an empty asm here, so nothing that uses
-    // them (unpacking, conversion) can be scheduled right after the loads, which
-    // would make the prefetch wait for memory.
-    uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
     const uint32_t* w0 = (const uint32_t*)&xr[0];
     const uint32_t* w1 = (const uint32_t*)&xr[1];
     const uint32_t* w2 = (const uint32_t*)&xr[2];
@@ -359,7 +367,7 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
       *(uint2*)(xTb + (2 * e) * 2 * LC + 16 * (mgc ^ (2 * e))) = make_uint2(lo01, lo23);
       *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) = make_uint2(hi01, hi23);
     }
-    const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
+    const float lutv[4] = {lutp.x, lutp.y, lutp.z, lutp.w};
     const float* ixl = sm.ss + kP + 8 * c8;
     const float4 i0 = *(const float4*)ixl, i1 = *(const float4*)(ixl + 4);
     const float invx8[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
@@ -400,12 +408,12 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
   }
   if (tid < LC) {
     float* vec = sm.vec;
-    vec[tid] = pf.va * kLog2e;
+    vec[tid] = vap * kLog2e;
     float dtv;
     if constexpr (sizeof(T) == 4)
-      dtv = __uint_as_float(pf.vd);
+      dtv = __uint_as_float(vdp);
     else
-      dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)pf.vd));
+      dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)vdp));
     vec[LC + tid] = (t0 + tid < (int)a.d.L) ? dtv : 0.f;
   }
 }
@@ -541,7 +549,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     const int64_t t0 = (int64_t)k * LC;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies and Q(C) rows have landed
     __syncthreads();  // chunk k staged; H8l holds H_{k-1}
-    const int qd = (int)((qd_word >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
     PF pf;
     // The next chunk's loads are issued unconditionally (the last chunk reloads
     // itself): with no branch around them the compiler counts outstanding loads
@@ -742,11 +749,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     __syncthreads();  // chunk k's tiles and H8l are no longer read
     // stage the next chunk's x tile, then start its Q(B) rows (straight into the
     // now free LDS buffer) and Q(C) rows; they land while StatePassing runs
+    asm volatile("" : "+v"(pf.qd));  // landed before the copies below are issued
     prefetch_store<DT, LC, NS, PW, TAPS>(a, sm, b, h, kn, tid, 2 * pt_base, pf);
     dma_qb<LC, NS, PW>(a, s_qB, b, g_h, kn, w, lo);
     load_qc2(kn, lane, qc2);
 
     // ---- StatePassing (Eq. 6) in registers; publish H8 for the next ChunkScan1 ----
+    const int qd = (int)((qd_word >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
     const v2s qd2 = {(short)qd, (short)qd};
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
