@@ -101,23 +101,32 @@ __device__ __forceinline__ void prologue_bc_block(const Dims& d, const void* __r
   const int N = d.N, l = d.l;
   const int64_t Lp = (int64_t)d.c * l;
   const float ib = inv_B[g], ic = inv_C[g];
-  for (int item = threadIdx.x; item < RB * (N / 8); item += 256) {
+  // N <= 128, so a thread has at most 4 items; all their loads are issued before
+  // any is used (rows past L read row L - 1 and are written as zeros)
+  constexpr int kIt = RB * (128 / 8) / 256;
+  float xb[kIt][8], xc[kIt][8];
+#pragma unroll
+  for (int u = 0; u < kIt; ++u) {
+    const int item = (int)threadIdx.x + 256 * u;
+    if (item < RB * (N / 8)) {
+      const int sl = item / (N / 8), n0 = (item % (N / 8)) * 8;
+      const int64_t t = min((int64_t)k * l + RB * sb + sl, d.L - 1);
+      const int64_t src = ((b * d.L + t) * d.G + g) * (int64_t)N + n0;
+      ld8_f<DT>(B, src, xb[u]);
+      ld8_f<DT>(C, src, xc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kIt; ++u) {
+    const int item = (int)threadIdx.x + 256 * u;
+    if (item >= RB * (N / 8)) break;
     const int sl = item / (N / 8), n0 = (item % (N / 8)) * 8;
     const int64_t t = (int64_t)k * l + RB * sb + sl;
     int qb[8], qc[8];
-    if (t < d.L) {
-      float xb[8], xc[8];
-      const int64_t src = ((b * d.L + t) * d.G + g) * (int64_t)N + n0;
-      ld8_f<DT>(B, src, xb);
-      ld8_f<DT>(C, src, xc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qb[j] = q_sat(xb[j] * ib, 127.f);
-        qc[j] = q_sat(xc[j] * ic, 127.f);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qb[j] = qc[j] = 0;
+    for (int j = 0; j < 8; ++j) {
+      qb[j] = t < d.L ? q_sat(xb[u][j] * ib, 127.f) : 0;
+      qc[j] = t < d.L ? q_sat(xc[u][j] * ic, 127.f) : 0;
     }
     const int64_t dst = ((b * Lp + t) * d.G + g) * (int64_t)N + n0;
     *(uint2*)(qB + dst) = make_uint2(pack4(qb[0], qb[1], qb[2], qb[3]), pack4(qb[4], qb[5], qb[6], qb[7]));

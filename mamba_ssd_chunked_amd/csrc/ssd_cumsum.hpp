@@ -30,16 +30,28 @@ __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
   const int l = d.l;
   const int64_t t0 = (int64_t)k * l;
   const int nvalid = (int)min((int64_t)l, d.L - t0);
-  for (int idx = threadIdx.x; idx < kCsHeads * l; idx += 256) {
+  // all of a thread's loads are issued before any is used (chunks are at most
+  // 256 positions, so at most 4 per thread); out-of-range entries read element 0
+  // and are replaced by 0
+  const float Aj = A[h0 + min((int)threadIdx.x, nh - 1)];  // the head of threads 0 .. nh - 1
+  float v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = (int)threadIdx.x + 256 * u;
     const int j = idx % kCsHeads, s = idx / kCsHeads;
-    float v = 0.f;
-    if (j < nh && s < nvalid) v = ld_f<DT>(dt, (b * d.L + t0 + s) * d.H + h0 + j);
-    sdt[j][s] = v;
+    const bool ok = idx < kCsHeads * l && j < nh && s < nvalid;
+    const float x = ld_f<DT>(dt, ok ? (b * d.L + t0 + s) * d.H + h0 + j : 0);
+    v[u] = ok ? x : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = (int)threadIdx.x + 256 * u;
+    if (idx < kCsHeads * l) sdt[idx % kCsHeads][idx / kCsHeads] = v[u];
   }
   __syncthreads();
   if ((int)threadIdx.x < nh) {
     const int j = threadIdx.x;
-    const double Ah = (double)A[h0 + j];
+    const double Ah = (double)Aj;
     double a = 0.0;
     // sequence order is kept; the LDS reads of each block of 16 steps are issued
     // together so only the float64 additions form the dependent chain
