@@ -82,10 +82,10 @@ __device__ __forceinline__ FragF<DT> frag16(const u16* p) {
 
 // ---------------------------------------------------------------------------
 // Prologue: Q(B), Q(C) with padded rows (t >= L -> 0), once per group. One
-// block of 256 threads quantises one 64-row x N tile: tile (bx, by) with bx over
+// block of NT threads quantises one 64-row x N tile: tile (bx, by) with bx over
 // c * l / 64 row blocks and by over B * G.
 // ---------------------------------------------------------------------------
-template <int DT>
+template <int DT, int NT>
 __device__ __forceinline__ void prologue_bc_block(const Dims& d, const void* __restrict__ B,
                                                   const void* __restrict__ C,
                                                   const float* __restrict__ inv_B,
@@ -101,13 +101,13 @@ __device__ __forceinline__ void prologue_bc_block(const Dims& d, const void* __r
   const int N = d.N, l = d.l;
   const int64_t Lp = (int64_t)d.c * l;
   const float ib = inv_B[g], ic = inv_C[g];
-  // N <= 128, so a thread has at most 4 items; all their loads are issued before
-  // any is used (rows past L read row L - 1 and are written as zeros)
-  constexpr int kIt = RB * (128 / 8) / 256;
+  // N <= 128, so a thread has at most RB * 16 / NT items; all their loads are
+  // issued before any is used (rows past L read row L - 1 and are written as zeros)
+  constexpr int kIt = RB * (128 / 8) / NT;
   float xb[kIt][8], xc[kIt][8];
 #pragma unroll
   for (int u = 0; u < kIt; ++u) {
-    const int item = (int)threadIdx.x + 256 * u;
+    const int item = (int)threadIdx.x + NT * u;
     if (item < RB * (N / 8)) {
       const int sl = item / (N / 8), n0 = (item % (N / 8)) * 8;
       const int64_t t = min((int64_t)k * l + RB * sb + sl, d.L - 1);
@@ -118,7 +118,7 @@ __device__ __forceinline__ void prologue_bc_block(const Dims& d, const void* __r
   }
 #pragma unroll
   for (int u = 0; u < kIt; ++u) {
-    const int item = (int)threadIdx.x + 256 * u;
+    const int item = (int)threadIdx.x + NT * u;
     if (item >= RB * (N / 8)) break;
     const int sl = item / (N / 8), n0 = (item % (N / 8)) * 8;
     const int64_t t = (int64_t)k * l + RB * sb + sl;
@@ -141,14 +141,14 @@ __global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restr
                                                      const float* __restrict__ inv_C,
                                                      int8_t* __restrict__ qB,
                                                      int8_t* __restrict__ qC) {
-  prologue_bc_block<DT>(d, B, C, inv_B, inv_C, qB, qC, blockIdx.x, blockIdx.y);
+  prologue_bc_block<DT, 256>(d, B, C, inv_B, inv_C, qB, qC, blockIdx.x, blockIdx.y);
 }
 
 // The INT8 path's preparation in one launch: blocks [0, ncs) run ChunkCumsum
 // (dAcs, LUT_state, Q(Decay)), the rest the B/C prologue. Both parts are short
 // and latency-bound, so running them side by side hides one behind the other.
 template <int DT>
-__global__ __launch_bounds__(256) void k_prep_i8(Dims d, const void* __restrict__ dt,
+__global__ __launch_bounds__(kCsThreads) void k_prep_i8(Dims d, const void* __restrict__ dt,
                                                  const float* __restrict__ A,
                                                  float* __restrict__ dAcs, float* __restrict__ lut,
                                                  uint8_t* __restrict__ qdecay,
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void k_prep_i8(Dims d, const void* __restrict_
   } else {
     const int pi = bi - ncs;
     const int nbx = d.c * (d.l / 64);
-    prologue_bc_block<DT>(d, B, C, inv_B, inv_C, qB, qC, pi % nbx, pi / nbx);
+    prologue_bc_block<DT, kCsThreads>(d, B, C, inv_B, inv_C, qB, qC, pi % nbx, pi / nbx);
   }
 }
 
@@ -1446,10 +1446,10 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
   if (ncs + npro < ((int64_t)1 << 24) && d.B <= 65535) {
     const dim3 grid((unsigned)(ncs + npro));
     if (dtype == DT_F16)
-      hipLaunchKernelGGL(k_prep_i8<DT_F16>, grid, dim3(256), 0, st, d, dt, A, dAcs, lut, qd, B, C,
+      hipLaunchKernelGGL(k_prep_i8<DT_F16>, grid, dim3(kCsThreads), 0, st, d, dt, A, dAcs, lut, qd, B, C,
                          sc.inv_B, sc.inv_C, qB, qC, (int)ncs);
     else
-      hipLaunchKernelGGL(k_prep_i8<DT_BF16>, grid, dim3(256), 0, st, d, dt, A, dAcs, lut, qd, B, C,
+      hipLaunchKernelGGL(k_prep_i8<DT_BF16>, grid, dim3(kCsThreads), 0, st, d, dt, A, dAcs, lut, qd, B, C,
                          sc.inv_B, sc.inv_C, qB, qC, (int)ncs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

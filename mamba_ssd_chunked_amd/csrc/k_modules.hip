@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_quantize_x(const void* __restrict__ X,
 // ChunkCumsum (block body in ssd_cumsum.hpp): grid (c, B, ceil(H / kCsHeads)).
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(256) void k_chunk_cumsum(const void* __restrict__ dt,
+__global__ __launch_bounds__(kCsThreads) void k_chunk_cumsum(const void* __restrict__ dt,
                                                       const float* __restrict__ A,
                                                       float* __restrict__ dAcs,
                                                       float* __restrict__ lut,
@@ -610,7 +610,7 @@ hipError_t launch_quantize_x(const Dims& d, int dtype, const void* X, const floa
 hipError_t launch_chunk_cumsum(const Dims& d, int dtype, const void* dt, const float* A,
                                float* dAcs, float* lut, uint8_t* qdecay, hipStream_t st) {
   const dim3 grid(d.c, (unsigned)d.B, (d.H + kCsHeads - 1) / kCsHeads);
-#define L_(DT_) hipLaunchKernelGGL(k_chunk_cumsum<DT_>, grid, dim3(256), 0, st, dt, A, dAcs, lut, qdecay, d)
+#define L_(DT_) hipLaunchKernelGGL(k_chunk_cumsum<DT_>, grid, dim3(kCsThreads), 0, st, dt, A, dAcs, lut, qdecay, d)
   SSD_DISPATCH_DT(dtype, L_)
 #undef L_
   return hipGetLastError();

@@ -8,13 +8,17 @@
 namespace ssd {
 
 // ---------------------------------------------------------------------------
-// ChunkCumsum. One block per (chunk k, batch b, group of kCsHeads heads). dt is
-// staged in LDS; one thread per head then forms the float64 prefix sums in
-// sequence order (the only serial part), and all threads evaluate the float64
-// exponentials and write dAcs / LUT_state with coalesced stores. Padded
-// positions past L carry dt = 0, which leaves the running sum unchanged.
+// ChunkCumsum. One block of kCsThreads threads per (chunk k, batch b, group of
+// kCsHeads heads). All threads stage dt and the products dt * A (exact in
+// float64) in LDS; one thread per head then forms the float64 prefix sums in
+// sequence order, the only serial part, whose length is set by the latency of
+// the dependent float64 additions. The heads' chains sit in the lanes of one
+// wave, so few such waves share a SIMD. Finally all threads evaluate the
+// float64 exponentials and write dAcs / LUT_state with coalesced stores.
+// Padded positions past L carry dt = 0, which leaves the running sum unchanged.
 // ---------------------------------------------------------------------------
-constexpr int kCsHeads = 4;
+constexpr int kCsHeads = 16;
+constexpr int kCsThreads = 1024;
 
 template <int DT>
 __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
@@ -23,6 +27,7 @@ __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
                                                    float* __restrict__ lut,
                                                    uint8_t* __restrict__ qdecay, const Dims& d,
                                                    int k, int64_t b, int hblk) {
+  constexpr int kPer = kCsHeads * 256 / kCsThreads;  // staged entries per thread (chunks <= 256)
   __shared__ float sdt[kCsHeads][256 + 1];
   __shared__ double sa[kCsHeads][256 + 1];
   const int h0 = hblk * kCsHeads;
@@ -30,44 +35,48 @@ __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
   const int l = d.l;
   const int64_t t0 = (int64_t)k * l;
   const int nvalid = (int)min((int64_t)l, d.L - t0);
-  // all of a thread's loads are issued before any is used (chunks are at most
-  // 256 positions, so at most 4 per thread); out-of-range entries read element 0
-  // and are replaced by 0
-  const float Aj = A[h0 + min((int)threadIdx.x, nh - 1)];  // the head of threads 0 .. nh - 1
-  float v[4];
+  // entry idx = tid + kCsThreads u is (head idx % kCsHeads, position idx /
+  // kCsHeads), so every entry of a thread belongs to the same head. All loads of
+  // a thread are issued before any is used; out-of-range entries read element 0
+  // and are replaced by 0.
+  const int jt = (int)threadIdx.x % kCsHeads;
+  const double Aj = (double)A[h0 + min(jt, nh - 1)];
+  float v[kPer];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = (int)threadIdx.x + 256 * u;
-    const int j = idx % kCsHeads, s = idx / kCsHeads;
-    const bool ok = idx < kCsHeads * l && j < nh && s < nvalid;
-    const float x = ld_f<DT>(dt, ok ? (b * d.L + t0 + s) * d.H + h0 + j : 0);
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = (int)threadIdx.x + kCsThreads * u;
+    const int s = idx / kCsHeads;
+    const bool ok = idx < kCsHeads * l && jt < nh && s < nvalid;
+    const float x = ld_f<DT>(dt, ok ? (b * d.L + t0 + s) * d.H + h0 + jt : 0);
     v[u] = ok ? x : 0.f;
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = (int)threadIdx.x + 256 * u;
-    if (idx < kCsHeads * l) sdt[idx % kCsHeads][idx / kCsHeads] = v[u];
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = (int)threadIdx.x + kCsThreads * u;
+    if (idx < kCsHeads * l) {
+      sdt[jt][idx / kCsHeads] = v[u];
+      sa[jt][idx / kCsHeads] = (double)v[u] * Aj;  // the product is exact in float64
+    }
   }
   __syncthreads();
   if ((int)threadIdx.x < nh) {
     const int j = threadIdx.x;
-    const double Ah = (double)Aj;
     double a = 0.0;
     // sequence order is kept; the LDS reads of each block of 16 steps are issued
     // together so only the float64 additions form the dependent chain
     for (int s0 = 0; s0 < l; s0 += 16) {
-      float v[16];
+      double p[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = sdt[j][s0 + u];
+      for (int u = 0; u < 16; ++u) p[u] = sa[j][s0 + u];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        a += (double)v[u] * Ah;  // the product is exact in float64
+        a += p[u];
         sa[j][s0 + u] = a;
       }
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * l; idx += 256) {
+  for (int idx = threadIdx.x; idx < nh * l; idx += kCsThreads) {
     const int j = idx / l, s = idx % l;
     const double a = sa[j][s], alast = sa[j][l - 1];
     const int64_t o = ((b * d.H + h0 + j) * d.c + k) * (int64_t)l + s;
