@@ -632,10 +632,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       // one accumulator per p tile: off-diagonal tiles are summed unscaled, then
       // multiplied by u_s; ChunkScan1 and the diagonal tile add on top
       v4f acc[PW];
-#pragma unroll
-      for (int jp = 0; jp < PW; ++jp) acc[jp] = v4f{0, 0, 0, 0};
-      // off-diagonal column tiles j < i in full pairs (jA, jA + 1)
-      for (int jA = 0; jA + 1 < i; jA += 2) {
+      // off-diagonal column tiles j < i in full pairs (jA, jA + 1); the first
+      // pair starts the accumulators (zero addend) instead of a separate clear
+      const auto pair = [&](int jA, bool first) {
         const int jB = jA + 1;
         v4i ba[KN], bb[KN];
 #pragma unroll
@@ -664,7 +663,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
         wf.set(6, (float)cbB[2] * vB.z);
         wf.set(7, (float)cbB[3] * vB.w);
 #pragma unroll
-        for (int jp = 0; jp < PW; ++jp) acc[jp] = FragF<DT>::mma(xf[jp], wf, acc[jp]);
+        for (int jp = 0; jp < PW; ++jp) acc[jp] = FragF<DT>::mma(xf[jp], wf, first ? v4f{0, 0, 0, 0} : acc[jp]);
+      };
+      if (i >= 2) {
+        pair(0, true);
+        for (int jA = 2; jA + 1 < i; jA += 2) pair(jA, false);
+      } else {
+#pragma unroll
+        for (int jp = 0; jp < PW; ++jp) acc[jp] = v4f{0, 0, 0, 0};
       }
       // diagonal tile j = i (with D on its diagonal, so the skip term D x rides the
       // MFMA). It shares its MFMA with the other tile of its pair (2m, 2m + 1),
@@ -676,23 +682,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 #pragma unroll
       for (int jp = 0; jp < PW; ++jp) acc[jp] *= us;
       // ChunkScan1 (inter-chunk), transposed: H8 rows x Q(C) rows, scaled by
-      // exp(a_s) s_C s_S[p] and added to the output accumulator
+      // exp(a_s) s_C s_S[p] and added to the output accumulator. All operands
+      // are read first and the MFMAs of the p tiles interleave, so the tiles'
+      // LDS and MFMA latencies overlap instead of adding up.
       if (k > 0 || has_init) {
         const float eo = fast_exp2(a_s) * sC;
+        v4i hb[KN][PW];
+        float4 ssv[PW];
+#pragma unroll
+        for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+          for (int jp = 0; jp < PW; ++jp)
+            hb[kn][jp] = *(const v4i*)&H8l[b_off<NS>(16 * (pt_base + jp) + l16, 64 * kn + 16 * lg)];
+#pragma unroll
+        for (int jp = 0; jp < PW; ++jp) ssv[jp] = *(const float4*)&SSl[16 * (pt_base + jp) + 4 * lg];
+        v4i acc1[PW];
+#pragma unroll
+        for (int jp = 0; jp < PW; ++jp) acc1[jp] = mma_i8(hb[0][jp], qcr[0], v4i{0, 0, 0, 0});
+#pragma unroll
+        for (int kn = 1; kn < KN; ++kn)
+#pragma unroll
+          for (int jp = 0; jp < PW; ++jp) acc1[jp] = mma_i8(hb[kn][jp], qcr[kn], acc1[jp]);
 #pragma unroll
         for (int jp = 0; jp < PW; ++jp) {
-          const int pt = pt_base + jp;
-          v4i acc1 = v4i{0, 0, 0, 0};
-#pragma unroll
-          for (int kn = 0; kn < KN; ++kn) {
-            const v4i hb = *(const v4i*)&H8l[b_off<NS>(16 * pt + l16, 64 * kn + 16 * lg)];
-            acc1 = mma_i8(hb, qcr[kn], acc1);
-          }
-          const float4 ss = *(const float4*)&SSl[16 * pt + 4 * lg];
-          acc[jp][0] = fmaf((float)acc1[0], eo * ss.x, acc[jp][0]);
-          acc[jp][1] = fmaf((float)acc1[1], eo * ss.y, acc[jp][1]);
-          acc[jp][2] = fmaf((float)acc1[2], eo * ss.z, acc[jp][2]);
-          acc[jp][3] = fmaf((float)acc1[3], eo * ss.w, acc[jp][3]);
+          acc[jp][0] = fmaf((float)acc1[jp][0], eo * ssv[jp].x, acc[jp][0]);
+          acc[jp][1] = fmaf((float)acc1[jp][1], eo * ssv[jp].y, acc[jp][1]);
+          acc[jp][2] = fmaf((float)acc1[jp][2], eo * ssv[jp].z, acc[jp][2]);
+          acc[jp][3] = fmaf((float)acc1[jp][3], eo * ssv[jp].w, acc[jp][3]);
         }
       }
       {
@@ -724,9 +740,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int sp = 16 * i + 4 * lg + r;
-          float wv = (sp <= s_row) ? (float)cbD[r] * scBC * fast_exp2(a_s - adv[r]) * ddv[r] : 0.f;
-          if (sp == s_row) wv += Dh;
-          wd[r] = wv;
+          // evaluated in every lane and then selected (no branch); above the
+          // diagonal the exponent is positive and the discarded value may be inf
+          const float wv = (float)cbD[r] * scBC * fast_exp2(a_s - adv[r]) * ddv[r];
+          wd[r] = (sp < s_row) ? wv : (sp == s_row) ? wv + Dh : 0.f;
           wl[r] = (float)cbL[r] * vLv[r];
         }
         FragF<DT> wf;
@@ -745,13 +762,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       for (int jp = 0; jp < PW; ++jp) {
         const int pt = pt_base + jp;
         const float y[4] = {acc[jp][0], acc[jp][1], acc[jp][2], acc[jp][3]};
-        if (t < d.L) {
-          const uint32_t lo = (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[0])) |
-                              ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[1])) << 16);
-          const uint32_t hi = (uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[2])) |
-                              ((uint32_t)__builtin_bit_cast(u16, Store<DT>::from_f(y[3])) << 16);
-          *(uint2*)(yrow + 16 * pt * (int)sizeof(T)) = make_uint2(lo, hi);
-        }
+        if (t < d.L) *(uint2*)(yrow + 16 * pt * (int)sizeof(T)) = make_uint2(pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3]));
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
     }

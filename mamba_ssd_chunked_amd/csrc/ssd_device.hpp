@@ -50,6 +50,22 @@ struct Store<DT_BF16> {
   }
 };
 
+// Two values rounded (to nearest even) to the 16-bit type, packed low/high in
+// one dword (one packed conversion instruction).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit types only");
+  if constexpr (DT == DT_F16) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    const b2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ float ld_f(const void* p, int64_t i) {
   return Store<DT>::to_f(((const typename Store<DT>::T*)p)[i]);
