@@ -568,22 +568,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     v2s S8a[PTW], S8b[PTW];  // local state codes n = 4 lg + {0, 1} and {2, 3} of each dword
     {
       v4i acc[PTW];
-#pragma unroll
-      for (int j = 0; j < PTW; ++j) acc[j] = v4i{0, 0, 0, 0};
       // A operand Q(B)^T[n, s] straight from the Q(B) rows with two transposing
-      // reads: lane (lg, l16) gets n = 16 nt_own + l16 and s = s0 .. s0 + 15
+      // reads: lane (lg, l16) gets n = 16 nt_own + l16 and s = s0 .. s0 + 15.
+      // The operands of step ks + 1 are read while step ks multiplies.
       const int cB = 16 * nt_own + 8 * (l16 & 1);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      v4i qa[2], bq[2][PTW];
+      const auto load_ks = [&](int ks, v4i& a_, v4i (&b_)[PTW]) {
         const int s0 = 64 * ks + 16 * lg;
         const v2i lo = lds_tr8(qBl + b_off<NS>(s0 + (l16 >> 1), cB));
         const v2i hi = lds_tr8(qBl + b_off<NS>(s0 + 8 + (l16 >> 1), cB));
-        const v4i qa = v4i{lo.x, lo.y, hi.x, hi.y};
+        a_ = v4i{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int j = 0; j < PTW; ++j) {
-          const v4i bq = *(const v4i*)&qxl[qx_off<LC>(16 * (pt0 + j) + l16, s0)];
-          acc[j] = mma_i8(qa, bq, acc[j]);
-        }
+        for (int j = 0; j < PTW; ++j) b_[j] = *(const v4i*)&qxl[qx_off<LC>(16 * (pt0 + j) + l16, s0)];
+      };
+      load_ks(0, qa[0], bq[0]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) load_ks(ks + 1, qa[(ks + 1) & 1], bq[(ks + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < PTW; ++j)
+          acc[j] = mma_i8(qa[ks & 1], bq[ks & 1][j], ks == 0 ? v4i{0, 0, 0, 0} : acc[j]);
       }
 #pragma unroll
       for (int j = 0; j < PTW; ++j) {
