@@ -976,11 +976,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   };
   const auto stage_store = [&](int kc, int tid, const Pf& pf) {
     const int t0 = kc * LC;
+    // every prefetched register passes through an empty asm in all lanes (see
+    // prefetch_store of the INT8 kernel)
+    uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
+    float4 lutp = pf.lut;
+    float vap = pf.va, vlp = SPLIT ? pf.vl : 0.f;
+    uint32_t vdp = pf.vd;
+    asm volatile("" : "+v"(lutp.x), "+v"(lutp.y), "+v"(lutp.z), "+v"(lutp.w), "+v"(vap), "+v"(vdp));
+    if constexpr (SPLIT) asm volatile("" : "+v"(vlp));
     if (tid < XI) {
       const int q = tid / C8N, c8 = c8b + tid % C8N;
-      uint4 xr[4] = {pf.x[0], pf.x[1], pf.x[2], pf.x[3]};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(xr[r].x), "+v"(xr[r].y), "+v"(xr[r].z), "+v"(xr[r].w));
       const uint32_t* w0 = (const uint32_t*)&xr[0];
       const uint32_t* w1 = (const uint32_t*)&xr[1];
       const uint32_t* w2 = (const uint32_t*)&xr[2];
@@ -996,7 +1003,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       }
       // fl32(LUT x) in the 16-bit type for 4 rows of each p (fp16 only)
       if constexpr (!SPLIT) {
-        const float lutv[4] = {pf.lut.x, pf.lut.y, pf.lut.z, pf.lut.w};
+        const float lutv[4] = {lutp.x, lutp.y, lutp.z, lutp.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float v[4];
@@ -1006,16 +1013,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
             const uint32_t hv = (e & 1) ? (dw >> 16) : (dw & 0xffffu);
             v[r] = __builtin_fmaf(lutv[r], Store<DT>::to_f(__builtin_bit_cast(T, (u16)hv)), 0.0f);
           }
-          *(uint2*)&s_xs[h_off<LC>(8 * c8 + e, 4 * q)] =
-              make_uint2(bits16<DT>(v[0]) | (bits16<DT>(v[1]) << 16), bits16<DT>(v[2]) | (bits16<DT>(v[3]) << 16));
+          *(uint2*)&s_xs[h_off<LC>(8 * c8 + e, 4 * q)] = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
         }
       }
     }
     if (tid < LC) {
-      s_vec[tid] = pf.va * kLog2e;
-      const float dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)pf.vd));
+      s_vec[tid] = vap * kLog2e;
+      const float dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)vdp));
       s_vec[LC + tid] = (t0 + tid < (int)d.L) ? dtv : 0.f;
-      if constexpr (SPLIT) s_vec[2 * LC + tid] = pf.vl;
+      if constexpr (SPLIT) s_vec[2 * LC + tid] = vlp;
     }
   };
   // B rows of chunk kc straight into LDS (1 KB per copy; lane L fills bytes
@@ -1164,9 +1170,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       v4f acc[PW];
-#pragma unroll
-      for (int jp = 0; jp < PW; ++jp) acc[jp] = v4f{0, 0, 0, 0};
-      for (int jA = 0; jA + 1 < i; jA += 2) {
+      // off-diagonal pairs (jA, jA + 1); the first one starts the accumulators
+      const auto pair = [&](int jA, bool first) {
         const int jB = jA + 1;
         v4f cbA = v4f{0, 0, 0, 0}, cbB = v4f{0, 0, 0, 0};
 #pragma unroll
@@ -1188,30 +1193,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
 #pragma unroll
         for (int jp = 0; jp < PW; ++jp) {
           const F xf = frag16<DT>(&s_xT[xT_pair<LC>(16 * (pt_base + jp) + l16, jA >> 1, lg)]);
-          acc[jp] = F::mma(xf, wf, acc[jp]);
+          acc[jp] = F::mma(xf, wf, first ? v4f{0, 0, 0, 0} : acc[jp]);
           if constexpr (SPLIT) acc[jp] = F::mma(xf, wl, acc[jp]);
         }
+      };
+      if (i >= 2) {
+        pair(0, true);
+        for (int jA = 2; jA + 1 < i; jA += 2) pair(jA, false);
+      } else {
+#pragma unroll
+        for (int jp = 0; jp < PW; ++jp) acc[jp] = v4f{0, 0, 0, 0};
       }
       const float a_s = vA2[s_row];
       const float us = fast_exp2(a_s - a_ref);
 #pragma unroll
       for (int jp = 0; jp < PW; ++jp) acc[jp] *= us;
       // ChunkScan1: exp(a_s) sum_n C[s,n] H_{k-1}[p,n] (H_{-1}: the initial state)
+      // (the p tiles' MFMA chains interleave: each K step reads the operands of
+      // all p tiles first)
       if (k > 0 || has_init) {
         const float eo = fast_exp2(a_s);
+        v4f acc1[PW];
 #pragma unroll
-        for (int jp = 0; jp < PW; ++jp) {
-          const int pt = pt_base + jp;
-          v4f acc1 = v4f{0, 0, 0, 0};
+        for (int kn = 0; kn < KNF; ++kn) {
+          F hf[PW], hl[PW];
 #pragma unroll
-          for (int kn = 0; kn < KNF; ++kn) {
-            const int ho = h_off<NS>(16 * pt + l16, 32 * kn + 8 * lg);
-            acc1 = F::mma(frag16<DT>(&s_H[ho]), cr[kn], acc1);
-            if constexpr (SPLIT) acc1 = F::mma(frag16<DT>(&s_H_lo[ho]), cr[kn], acc1);
+          for (int jp = 0; jp < PW; ++jp) {
+            const int ho = h_off<NS>(16 * (pt_base + jp) + l16, 32 * kn + 8 * lg);
+            hf[jp] = frag16<DT>(&s_H[ho]);
+            if constexpr (SPLIT) hl[jp] = frag16<DT>(&s_H_lo[ho]);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[jp][r] = fmaf(acc1[r], eo, acc[jp][r]);
+          for (int jp = 0; jp < PW; ++jp) {
+            acc1[jp] = F::mma(hf[jp], cr[kn], kn == 0 ? v4f{0, 0, 0, 0} : acc1[jp]);
+            if constexpr (SPLIT) acc1[jp] = F::mma(hl[jp], cr[kn], acc1[jp]);
+          }
         }
+#pragma unroll
+        for (int jp = 0; jp < PW; ++jp)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[jp][r] = fmaf(acc1[jp][r], eo, acc[jp][r]);
       }
       {  // diagonal tile (D on its diagonal), sharing its MFMA with tile i - 1 (odd i)
         const int hd = i & 1;
@@ -1236,9 +1257,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int sp = 16 * i + 4 * lg + r;
-          float wv = (sp <= s_row) ? cbD[r] * fast_exp2(a_s - adv[r]) * ddv[r] : 0.f;
-          if (sp == s_row) wv += Dh;
-          wd[r] = wv;
+          const float wv = cbD[r] * fast_exp2(a_s - adv[r]) * ddv[r];  // selected below (no branch)
+          wd[r] = (sp < s_row) ? wv : (sp == s_row) ? wv + Dh : 0.f;
           wl[r] = cbL[r] * vLv[r];
         }
         F wf, wlo;
@@ -1265,8 +1285,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       for (int jp = 0; jp < PW; ++jp) {
         const int pt = pt_base + jp;
         if (t < d.L)
-          *(uint2*)(yrow + 32 * pt) = make_uint2(bits16<DT>(acc[jp][0]) | (bits16<DT>(acc[jp][1]) << 16),
-                                                 bits16<DT>(acc[jp][2]) | (bits16<DT>(acc[jp][3]) << 16));
+          *(uint2*)(yrow + 32 * pt) = make_uint2(pack2<DT>(acc[jp][0], acc[jp][1]), pack2<DT>(acc[jp][2], acc[jp][3]));
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -1283,12 +1302,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
       for (int r = 0; r < 4; ++r) Hs[j][r] = (k == 0 && !has_init) ? sacc[j][r] : fmaf(decay, Hs[j][r], sacc[j][r]);
       const int p = 16 * (pt0 + j) + l16;
       const int ho = h_off<NS>(p, 16 * nt_own + 4 * lg);
-      *(uint2*)&s_H[ho] = make_uint2(bits16<DT>(Hs[j][0]) | (bits16<DT>(Hs[j][1]) << 16),
-                                     bits16<DT>(Hs[j][2]) | (bits16<DT>(Hs[j][3]) << 16));
+      *(uint2*)&s_H[ho] = make_uint2(pack2<DT>(Hs[j][0], Hs[j][1]), pack2<DT>(Hs[j][2], Hs[j][3]));
       if constexpr (SPLIT)
         *(uint2*)&s_H_lo[ho] =
-            make_uint2(bits16<DT>(resid16<DT>(Hs[j][0])) | (bits16<DT>(resid16<DT>(Hs[j][1])) << 16),
-                       bits16<DT>(resid16<DT>(Hs[j][2])) | (bits16<DT>(resid16<DT>(Hs[j][3])) << 16));
+            make_uint2(pack2<DT>(resid16<DT>(Hs[j][0]), resid16<DT>(Hs[j][1])),
+                       pack2<DT>(resid16<DT>(Hs[j][2]), resid16<DT>(Hs[j][3])));
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
