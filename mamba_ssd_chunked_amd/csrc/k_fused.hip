@@ -1101,24 +1101,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
 
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
     v4f sacc[PTW];
-#pragma unroll
-    for (int j = 0; j < PTW; ++j) sacc[j] = v4f{0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < KSF; ++ks) {
-      const int cn = 16 * nt_own + 4 * (l16 & 3);
-      if constexpr (!SPLIT) {
-        // A: B^T rows n = 16 nt_own + l16, K = s0 .. s0 + 7 (two reads of 4 rows)
+    const int cn = 16 * nt_own + 4 * (l16 & 3);
+    if constexpr (!SPLIT) {
+      // A: B^T rows n = 16 nt_own + l16, K = s0 .. s0 + 7 (two reads of 4 rows);
+      // the operands of step ks + 1 are read while step ks multiplies
+      F fa[2], fb[2][PTW];
+      const auto load_ks = [&](int ks, F& a_, F (&b_)[PTW]) {
         const int s0 = 32 * ks + 8 * lg;
         const v4s lo = lds_tr16(s_B + h_off<NS>(s0 + (l16 >> 2), cn));
         const v4s hi = lds_tr16(s_B + h_off<NS>(s0 + 4 + (l16 >> 2), cn));
-        F fa;
-        fa.v = __builtin_bit_cast(decltype(fa.v), v8s_join(lo, hi));
+        a_.v = __builtin_bit_cast(decltype(a_.v), v8s_join(lo, hi));
 #pragma unroll
-        for (int j = 0; j < PTW; ++j) {
-          const F fb = frag16<DT>(&s_xs[h_off<LC>(16 * (pt0 + j) + l16, s0)]);
-          sacc[j] = F::mma(fa, fb, sacc[j]);
-        }
-      } else {
+        for (int j = 0; j < PTW; ++j) b_[j] = frag16<DT>(&s_xs[h_off<LC>(16 * (pt0 + j) + l16, s0)]);
+      };
+      load_ks(0, fa[0], fb[0]);
+#pragma unroll
+      for (int ks = 0; ks < KSF; ++ks) {
+        if (ks + 1 < KSF) load_ks(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < PTW; ++j)
+          sacc[j] = F::mma(fa[ks & 1], fb[ks & 1][j], ks == 0 ? v4f{0, 0, 0, 0} : sacc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PTW; ++j) sacc[j] = v4f{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KSF; ++ks) {
         // bf16: S^T = (B LUT)^T x, with B LUT formed here as hi + lo and x read
         // exactly from x^T. K order of x^T's operand: s = 32 ks + 4 lg + (0..3)
         // and 32 ks + 16 + 4 lg + (0..3); the two transposing reads follow it.
