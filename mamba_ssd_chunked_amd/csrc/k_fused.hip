@@ -614,6 +614,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       for (int kn = 0; kn < KN; ++kn) asm volatile("" : "+v"(qc2[rr][kn]));
     // next chunk: x and vectors into registers (Q(B) rows follow after the scan)
     prefetch_load<DT, LC, NS, PW>(a, b, h, kn, tid, 2 * pt_base, lo, pf);
+    // Waves w and w + 4 share a SIMD, and at equal priority the older wave w is
+    // issued first, so waves 4..7 used to reach the barrier after the scan about
+    // 10% later. They run their first row tile at a raised priority.
+    if (w >= kWaves / 2) __builtin_amdgcn_s_setprio(1);
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
     // (outputs land as 4 consecutive p per lane for one position s)
@@ -769,7 +773,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
         if (t < d.L) *(uint2*)(yrow + 16 * pt * (int)sizeof(T)) = make_uint2(pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3]));
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
+      if (rr == 0 && w >= kWaves / 2) __builtin_amdgcn_s_setprio(0);
     }
+    __builtin_amdgcn_s_setprio(0);  // (also when a row tile was skipped)
     __syncthreads();  // chunk k's tiles and H8l are no longer read
     // stage the next chunk's x tile, then start its Q(B) rows (straight into the
     // now free LDS buffer) and Q(C) rows; they land while StatePassing runs
