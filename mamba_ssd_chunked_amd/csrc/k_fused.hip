@@ -564,6 +564,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
     // exactly instead of waiting for all of them where the paths merge.
     const int kn = min(k + 1, d.c - 1);
 
+    // The Q(C) rows are complete (they were loaded during the previous chunk's
+    // tail); passing them through an empty asm here keeps the compiler from
+    // placing its own wait for them inside the scan loops, where the in-order
+    // load counter would also wait for every prefetch load.
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int kn = 0; kn < KN; ++kn) asm volatile("" : "+v"(qc2[rr][kn]));
+    // next chunk: x and vectors into registers, issued before ChunkState so the
+    // load issue overlaps its MFMA work (Q(B) rows follow after the scan)
+    prefetch_load<DT, LC, NS, PW>(a, b, h, kn, tid, 2 * pt_base, lo, pf);
+
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
     v2s S8a[PTW], S8b[PTW];  // local state codes n = 4 lg + {0, 1} and {2, 3} of each dword
     {
@@ -604,16 +616,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       }
     }
 
-    // The Q(C) rows are complete (they were loaded during the previous chunk's
-    // tail); passing them through an empty asm here keeps the compiler from
-    // placing its own wait for them inside the scan loops, where the in-order
-    // load counter would also wait for every prefetch load.
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-      for (int kn = 0; kn < KN; ++kn) asm volatile("" : "+v"(qc2[rr][kn]));
-    // next chunk: x and vectors into registers (Q(B) rows follow after the scan)
-    prefetch_load<DT, LC, NS, PW>(a, b, h, kn, tid, 2 * pt_base, lo, pf);
     // Waves w and w + 4 share a SIMD, and at equal priority the older wave w is
     // issued first, so waves 4..7 used to reach the barrier after the scan about
     // 10% later. They run their first row tile at a raised priority.
