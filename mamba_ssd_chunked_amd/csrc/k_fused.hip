@@ -1107,6 +1107,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
     __syncthreads();  // chunk k staged; s_H holds H_{k-1}
     const float alast2 = vA2[LC - 1];  // a_{k,l-1} log2(e): StatePassing decay
 
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int kn = 0; kn < KNF; ++kn)
+        asm volatile("" : "+v"(cf2[rr][kn].x), "+v"(cf2[rr][kn].y), "+v"(cf2[rr][kn].z), "+v"(cf2[rr][kn].w));
+    const int kn1 = min(k + 1, d.c - 1);
+    Pf pf;
+    stage_load(kn1, tid, pf);  // issued before ChunkState (as in the INT8 kernel)
+
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
     v4f sacc[PTW];
     const int cn = 16 * nt_own + 4 * (l16 & 3);
@@ -1160,14 +1169,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
         }
       }
     }
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-      for (int kn = 0; kn < KNF; ++kn)
-        asm volatile("" : "+v"(cf2[rr][kn].x), "+v"(cf2[rr][kn].y), "+v"(cf2[rr][kn].z), "+v"(cf2[rr][kn].w));
-    const int kn1 = min(k + 1, d.c - 1);
-    Pf pf;
-    stage_load(kn1, tid, pf);
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
 #pragma unroll
