@@ -16,14 +16,18 @@ namespace {
 constexpr int kEpThreads = 256;
 constexpr int kEpVec = 8;  // elements per vector access
 
-// One workgroup per position. Each thread keeps up to kMaxV vectors of the row
-// in registers between the sum of squares and the normalised write (rows of up
-// to 256 * kMaxV * 8 = 8192 channels are read once; longer rows re-read the
-// rest, which the cache serves). The row is read and written once, so the
+// One workgroup per kEpRows positions. The weight and alpha * corr vectors a
+// thread needs are loaded once per workgroup and kept in registers for all its
+// rows (they were the larger part of the cache traffic when every position
+// re-read them). Each thread keeps up to kMaxV vectors of every row in
+// registers between the sum of squares and the normalised write: rows of up
+// to 256 * kMaxV * 8 = 6144 channels are read once; longer rows re-read the
+// rest, which the cache serves. The rows are read and written once, so those
 // loads and stores carry the non-temporal hint. out may be Y itself: each
 // element is read before the same thread overwrites it, after the whole row
 // has been summed.
-constexpr int kMaxV = 4;
+constexpr int kEpRows = 2;
+constexpr int kMaxV = 3;
 
 template <int DT>
 __device__ __forceinline__ void ld8_nt(const void* p, int64_t i, float out[8]) {
@@ -57,9 +61,7 @@ __device__ __forceinline__ void st8_nt(void* p, int64_t i, const float o[8]) {
     typedef uint32_t v4u_ __attribute__((ext_vector_type(4)));
     v4u_ w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (uint32_t)__builtin_bit_cast(u16, to_store<DT>(o[2 * j])) |
-             ((uint32_t)__builtin_bit_cast(u16, to_store<DT>(o[2 * j + 1])) << 16);
+    for (int j = 0; j < 4; ++j) w[j] = pack2<DT>(o[2 * j], o[2 * j + 1]);
     __builtin_nontemporal_store(w, (v4u_*)((u16*)p + i));
   }
 }
@@ -70,69 +72,98 @@ __global__ __launch_bounds__(kEpThreads) void k_epilogue(const void* Y,
                                                          float alpha,
                                                          const float* __restrict__ weight,
                                                          float eps, void* out,
-                                                         int Dc) {
-  __shared__ float red[kEpThreads / kWave];
-  const int64_t row = blockIdx.x;
+                                                         int Dc, int64_t rows) {
+  __shared__ float red[kEpRows][kEpThreads / kWave];
+  const int64_t row0 = (int64_t)blockIdx.x * kEpRows;
+  const int nr = (int)min((int64_t)kEpRows, rows - row0);  // rows of this workgroup (uniform)
   const int nv = Dc / kEpVec;
-  const int64_t base = row * (int64_t)Dc;
   // without a correction the weight array stands in for it with a zero
   // coefficient, so every access is an unconditional vector load
   const float* const cp = corr ? corr : weight;
   const float al = corr ? alpha : 0.f;
-  float u[kMaxV][kEpVec];
-  float ss = 0.f;
+  float wv[kMaxV][kEpVec], cv[kMaxV][kEpVec];
 #pragma unroll
   for (int i = 0; i < kMaxV; ++i) {
     const int v = threadIdx.x + i * kEpThreads;
     if (v < nv) {
-      float y[kEpVec], cv[kEpVec];
-      ld8_nt<DT>(Y, base + (int64_t)v * kEpVec, y);
-      ld8_f<DT_F32>(cp, (int64_t)v * kEpVec, cv);
+      ld8_f<DT_F32>(weight, (int64_t)v * kEpVec, wv[i]);
+      ld8_f<DT_F32>(cp, (int64_t)v * kEpVec, cv[i]);
+    }
+  }
+  float u[kEpRows][kMaxV][kEpVec];
+  float ss[kEpRows];
 #pragma unroll
-      for (int j = 0; j < kEpVec; ++j) {
-        u[i][j] = fmaf(al, cv[j], y[j]);
-        ss = fmaf(u[i][j], u[i][j], ss);
+  for (int r = 0; r < kEpRows; ++r) {
+    ss[r] = 0.f;
+    if (r < nr) {
+#pragma unroll
+      for (int i = 0; i < kMaxV; ++i) {
+        const int v = threadIdx.x + i * kEpThreads;
+        if (v < nv) ld8_nt<DT>(Y, (row0 + r) * (int64_t)Dc + (int64_t)v * kEpVec, u[r][i]);
       }
     }
   }
-  for (int v = threadIdx.x + kMaxV * kEpThreads; v < nv; v += kEpThreads) {
-    float y[kEpVec], cv[kEpVec];
-    ld8_f<DT>(Y, base + (int64_t)v * kEpVec, y);
-    ld8_f<DT_F32>(cp, (int64_t)v * kEpVec, cv);
 #pragma unroll
-    for (int j = 0; j < kEpVec; ++j) {
-      const float t = fmaf(al, cv[j], y[j]);
-      ss = fmaf(t, t, ss);
+  for (int r = 0; r < kEpRows; ++r) {
+    if (r < nr) {
+#pragma unroll
+      for (int i = 0; i < kMaxV; ++i) {
+        const int v = threadIdx.x + i * kEpThreads;
+        if (v < nv) {
+#pragma unroll
+          for (int j = 0; j < kEpVec; ++j) {
+            u[r][i][j] = fmaf(al, cv[i][j], u[r][i][j]);
+            ss[r] = fmaf(u[r][i][j], u[r][i][j], ss[r]);
+          }
+        }
+      }
+      for (int v = threadIdx.x + kMaxV * kEpThreads; v < nv; v += kEpThreads) {
+        float y[kEpVec], c8[kEpVec];
+        ld8_f<DT>(Y, (row0 + r) * (int64_t)Dc + (int64_t)v * kEpVec, y);
+        ld8_f<DT_F32>(cp, (int64_t)v * kEpVec, c8);
+#pragma unroll
+        for (int j = 0; j < kEpVec; ++j) {
+          const float t = fmaf(al, c8[j], y[j]);
+          ss[r] = fmaf(t, t, ss[r]);
+        }
+      }
     }
   }
-  // workgroup sum of squares
+  // workgroup sums of squares, all rows at once
 #pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-  if (lane_id() == 0) red[wave_id()] = ss;
+  for (int r = 0; r < kEpRows; ++r) {
+#pragma unroll
+    for (int m = kWave / 2; m >= 1; m >>= 1) ss[r] += __shfl_xor(ss[r], m);
+    if (lane_id() == 0) red[r][wave_id()] = ss[r];
+  }
   __syncthreads();
-  float tot = 0.f;
 #pragma unroll
-  for (int i = 0; i < kEpThreads / kWave; ++i) tot += red[i];
-  const float rs = rsqrtf(tot / (float)Dc + eps);
+  for (int r = 0; r < kEpRows; ++r) {
+    if (r >= nr) break;
+    float tot = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i) {
-    const int v = threadIdx.x + i * kEpThreads;
-    if (v < nv) {
-      float wv8[kEpVec], o[kEpVec];
-      ld8_f<DT_F32>(weight, (int64_t)v * kEpVec, wv8);
+    for (int i = 0; i < kEpThreads / kWave; ++i) tot += red[r][i];
+    const float rs = rsqrtf(tot / (float)Dc + eps);
+    const int64_t base = (row0 + r) * (int64_t)Dc;
 #pragma unroll
-      for (int j = 0; j < kEpVec; ++j) o[j] = u[i][j] * rs * wv8[j];
+    for (int i = 0; i < kMaxV; ++i) {
+      const int v = threadIdx.x + i * kEpThreads;
+      if (v < nv) {
+        float o[kEpVec];
+#pragma unroll
+        for (int j = 0; j < kEpVec; ++j) o[j] = u[r][i][j] * rs * wv[i][j];
+        st8_nt<DT>(out, base + (int64_t)v * kEpVec, o);
+      }
+    }
+    for (int v = threadIdx.x + kMaxV * kEpThreads; v < nv; v += kEpThreads) {
+      float y[kEpVec], c8[kEpVec], w8[kEpVec], o[kEpVec];
+      ld8_f<DT>(Y, base + (int64_t)v * kEpVec, y);
+      ld8_f<DT_F32>(cp, (int64_t)v * kEpVec, c8);
+      ld8_f<DT_F32>(weight, (int64_t)v * kEpVec, w8);
+#pragma unroll
+      for (int j = 0; j < kEpVec; ++j) o[j] = fmaf(al, c8[j], y[j]) * rs * w8[j];
       st8_nt<DT>(out, base + (int64_t)v * kEpVec, o);
     }
-  }
-  for (int v = threadIdx.x + kMaxV * kEpThreads; v < nv; v += kEpThreads) {
-    float y[kEpVec], cv[kEpVec], wv8[kEpVec], o[kEpVec];
-    ld8_f<DT>(Y, base + (int64_t)v * kEpVec, y);
-    ld8_f<DT_F32>(cp, (int64_t)v * kEpVec, cv);
-    ld8_f<DT_F32>(weight, (int64_t)v * kEpVec, wv8);
-#pragma unroll
-    for (int j = 0; j < kEpVec; ++j) o[j] = fmaf(al, cv[j], y[j]) * rs * wv8[j];
-    st8_nt<DT>(out, base + (int64_t)v * kEpVec, o);
   }
 }
 
@@ -169,10 +200,11 @@ hipError_t launch_epilogue(const Dims& d, int dtype, const void* Y, const float*
                            const float* weight, float eps, void* out, hipStream_t st) {
   const int64_t rows = d.B * d.L;
   const int Dc = d.H * d.P;
+  const dim3 grid((unsigned)((rows + kEpRows - 1) / kEpRows));
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL(k_epilogue<DT_F32>, dim3((unsigned)rows), dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc); break;
-    case DT_F16: hipLaunchKernelGGL(k_epilogue<DT_F16>, dim3((unsigned)rows), dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc); break;
-    case DT_BF16: hipLaunchKernelGGL(k_epilogue<DT_BF16>, dim3((unsigned)rows), dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc); break;
+    case DT_F32: hipLaunchKernelGGL(k_epilogue<DT_F32>, grid, dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc, rows); break;
+    case DT_F16: hipLaunchKernelGGL(k_epilogue<DT_F16>, grid, dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc, rows); break;
+    case DT_BF16: hipLaunchKernelGGL(k_epilogue<DT_BF16>, grid, dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc, rows); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -451,7 +451,7 @@ int ssd_epilogue(const ssd_shape* shape, const void* Y, const float* corr, float
   if ((rc = check_ptrs({Y, weight, out}))) return rc;
   if ((rc = check_opt({corr}))) return rc;
   if (!(eps >= 0.0f) || !std::isfinite(alpha)) return SSD_E_SHAPE;
-  // one workgroup per position: keep the grid's thread count below 2^32
+  // a workgroup per four positions: keeps the grid far below 2^32 threads
   if (d.B * d.L > (int64_t)1 << 24) return SSD_E_SHAPE;
   if (empty) return SSD_OK;
   return hip_status(ssd::launch_epilogue(d, shape->dtype, Y, corr, alpha, weight, eps, out,
