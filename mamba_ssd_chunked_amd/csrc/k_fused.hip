@@ -193,8 +193,11 @@ struct FusedArgs {
   int32_t* tap_s32;
   int8_t* tap_s8;
   int8_t* tap_passed;
-  int64_t slot0;  // first (batch, head) slot of this launch
-  int xcd_map;    // 1: slots are laid out so each XCD serves whole (batch, group) units
+  // launch layout: blocks [0, nfull) run whole heads (slots 0 .. nfull - 1), the
+  // rest run p halves of heads nfull .. (two blocks per head)
+  int64_t nfull;
+  int xcd_full;  // 1: the slots of that part are laid out so each XCD serves
+  int xcd_half;  //    whole (batch, group) units
 };
 
 // LDS of one workgroup: separate arrays, so the compiler knows the Q(B) buffer
@@ -434,7 +437,9 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
 // TAPS: the instantiation that can write the debug taps (the others carry no
 // tap code, which keeps their scalar registers free).
 template <int DT, int LC, int NS, int PW, bool TAPS>
-__global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
+__device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t bx, u16* s_xT, int8_t* s_qB,
+                                              int8_t* s_qx, int8_t* s_h8, float* s_vec, float* s_vw,
+                                              float* s_ss) {
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS, PW> PF;
   constexpr int RT = LC / 16;      // row tiles of the chunk
@@ -443,13 +448,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   constexpr int KS = LC / 64;      // ChunkState K steps
   constexpr int KN = NS / 64;      // K steps over N
 
-  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
-  __shared__ __attribute__((aligned(16))) int8_t s_qB[LC * NS];
-  __shared__ __attribute__((aligned(16))) int8_t s_qx[kP * LC];
-  __shared__ __attribute__((aligned(16))) int8_t s_h8[kP * NS];
-  __shared__ __attribute__((aligned(16))) float s_vec[2 * LC];
-  __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
-  __shared__ __attribute__((aligned(16))) float s_ss[3 * kP];
   const Smem<LC, NS> sm{s_xT, s_qB, s_qx, s_h8, s_vec, s_vw, s_ss};
   const u16* xT = s_xT;
   const int8_t* qxl = s_qx;
@@ -463,20 +461,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
   // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8). With
   // xcd_map, slot s runs on XCD s % 8 and every XCD gets whole (batch, group)
   // units, so the int8 Q(B)/Q(C) rows its heads share stay in that XCD's L2.
+  // bx: the block's index within its part of the launch
+  const int64_t slot0 = (PW == 4) ? 0 : a.nfull;
+  const bool xcd_map = (PW == 4) ? a.xcd_full : a.xcd_half;
   int64_t slot;
   int ph = 0;
   if (PW == 4) {
-    slot = a.slot0 + blockIdx.x;
-  } else if (a.xcd_map) {
-    const int64_t j = blockIdx.x / 8;
-    slot = a.slot0 + (blockIdx.x % 8) + 8 * (j >> 1);
+    slot = bx;
+  } else if (xcd_map) {
+    const int64_t j = bx / 8;
+    slot = slot0 + (bx % 8) + 8 * (j >> 1);
     ph = (int)(j & 1);
   } else {
-    slot = a.slot0 + blockIdx.x / 2;
-    ph = blockIdx.x & 1;
+    slot = slot0 + bx / 2;
+    ph = (int)(bx & 1);
   }
   int64_t unit, hl;
-  if (a.xcd_map) {
+  if (xcd_map) {
     const int64_t j = slot / 8;
     unit = (slot % 8) + 8 * (j / d.hpg);
     hl = j % d.hpg;
@@ -818,6 +819,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
       *(uint32_t*)(a.final_state + fo) = H8[j];
     }
   }
+}
+
+// One launch for both parts: whole heads in blocks [0, nfull), then the p
+// halves of the partial last round, which start on each CU as soon as its last
+// whole head is done. The LDS arrays are declared once here, as separate
+// objects (the compiler then knows the Q(B) copy target aliases none of the
+// other arrays).
+template <int DT, int LC, int NS, bool TAPS>
+__global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
+  __shared__ __attribute__((aligned(16))) int8_t s_qB[LC * NS];
+  __shared__ __attribute__((aligned(16))) int8_t s_qx[kP * LC];
+  __shared__ __attribute__((aligned(16))) int8_t s_h8[kP * NS];
+  __shared__ __attribute__((aligned(16))) float s_vec[2 * LC];
+  __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
+  __shared__ __attribute__((aligned(16))) float s_ss[3 * kP];
+  const int64_t bid = blockIdx.x;
+  if (bid < a.nfull)
+    fused_i8_body<DT, LC, NS, 4, TAPS>(a, bid, s_xT, s_qB, s_qx, s_h8, s_vec, s_vw, s_ss);
+  else
+    fused_i8_body<DT, LC, NS, 2, TAPS>(a, bid - a.nfull, s_xT, s_qB, s_qx, s_h8, s_vec, s_vw, s_ss);
 }
 
 // ===========================================================================
@@ -1341,18 +1363,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
 constexpr size_t kAl = 256;
 size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
-template <int DT, int LC, int NS, int PW>
-hipError_t launch_one(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
-  if (fa.tap_qxs || fa.tap_s32 || fa.tap_s8 || fa.tap_passed)
-    hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, PW, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       st, fa);
-  else
-    hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, PW, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       st, fa);
-  return hipGetLastError();
-}
-
-
 // One workgroup per CU at a time: B*H heads run in ceil(B*H / CUs) rounds. When
 // the last round is at most half full, its heads are split in two p halves so
 // the round spreads over all CUs (each half recomputes the head's CB tiles).
@@ -1368,34 +1378,45 @@ hipError_t launch_split(Args fa, hipStream_t st) {
   }
   const int64_t nfull = BH - nhalf;
   const bool unit_map = (d.B * d.G) % 8 == 0;
-  if (nfull > 0) {
-    fa.slot0 = 0;
-    fa.xcd_map = unit_map;
-    const hipError_t e = K::template launch<4>(fa, nfull, st);
-    if (e != hipSuccess) return e;
-  }
-  if (nhalf > 0) {
-    fa.slot0 = nfull;
-    fa.xcd_map = unit_map && nfull % 8 == 0 && nhalf % 8 == 0;
-    return K::template launch<2>(fa, 2 * nhalf, st);
-  }
-  return hipSuccess;
+  return K::launch(fa, nfull, nhalf, unit_map, unit_map && nfull % 8 == 0 && nhalf % 8 == 0, st);
 }
 
 template <int DT, int LC, int NS>
 struct FloatLaunch {
-  template <int PW>
-  static hipError_t launch(const FusedFArgs& fa, int64_t blocks, hipStream_t st) {
-    hipLaunchKernelGGL((k_fused_f16<DT, LC, NS, PW>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
-    return hipGetLastError();
+  static hipError_t launch(FusedFArgs fa, int64_t nfull, int64_t nhalf, bool xcd_full, bool xcd_half,
+                           hipStream_t st) {
+    if (nfull > 0) {
+      fa.slot0 = 0;
+      fa.xcd_map = xcd_full;
+      hipLaunchKernelGGL((k_fused_f16<DT, LC, NS, 4>), dim3((unsigned)nfull), dim3(kThreads), 0, st, fa);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (nhalf > 0) {
+      fa.slot0 = nfull;
+      fa.xcd_map = xcd_half;
+      hipLaunchKernelGGL((k_fused_f16<DT, LC, NS, 2>), dim3((unsigned)(2 * nhalf)), dim3(kThreads), 0, st, fa);
+      return hipGetLastError();
+    }
+    return hipSuccess;
   }
 };
 
+// both parts in one launch (k_fused_i8)
 template <int DT, int LC, int NS>
 struct Int8Launch {
-  template <int PW>
-  static hipError_t launch(const FusedArgs& fa, int64_t blocks, hipStream_t st) {
-    return launch_one<DT, LC, NS, PW>(fa, blocks, st);
+  static hipError_t launch(FusedArgs fa, int64_t nfull, int64_t nhalf, bool xcd_full, bool xcd_half,
+                           hipStream_t st) {
+    fa.nfull = nfull;
+    fa.xcd_full = xcd_full;
+    fa.xcd_half = xcd_half;
+    const int64_t blocks = nfull + 2 * nhalf;
+    if (blocks == 0) return hipSuccess;
+    if (fa.tap_qxs || fa.tap_s32 || fa.tap_s8 || fa.tap_passed)
+      hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+    else
+      hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+    return hipGetLastError();
   }
 };
 
@@ -1516,7 +1537,7 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
   }
 
   const FusedArgs fa{d, X, dt, qB, qC, dAcs, lut, qd, D, sc, Y, (const int8_t*)initial_state,
-                     (int8_t*)final_state, tap_qxs, tap_s32, tap_s8, tap_passed, 0, 0};
+                     (int8_t*)final_state, tap_qxs, tap_s32, tap_s8, tap_passed, 0, 0, 0};
   if (dtype == DT_F16) {
     if (d.l == 256 && d.N == 128) return launch_main<DT_F16, 256, 128>(fa, st);
     if (d.l == 256 && d.N == 64) return launch_main<DT_F16, 256, 64>(fa, st);
