@@ -908,14 +908,28 @@ struct FusedFArgs {
   void* Y;
   const float* init;  // optional initial state [B,H,P,N] fp32
   float* final_state;
-  int64_t slot0;
-  int xcd_map;
+  int64_t nfull;  // launch layout as in FusedArgs
+  int xcd_full;
+  int xcd_half;
+};
+
+// LDS arrays of the float kernel, declared once per kernel (see k_fused_i8)
+template <int DT, int LC, int NS>
+struct FLds {
+  static constexpr bool SPLIT = DT == DT_BF16;
+  u16* xT;    // x^T (xT_pair layout)
+  u16* xs;    // 16-bit (LUT x)^T [p][s] (h_off<LC>); with bf16 the LUT goes on the B side
+  u16* B;     // B rows [s][n] (h_off<NS>)
+  u16* H;     // 16-bit passed state [p][n] (h_off<NS>)
+  u16* H_lo;  // its residual (bf16)
+  float* vec; // a*log2(e), dt (, LUT)
+  float* vw;
 };
 
 // PW = 4: a whole head per workgroup; PW = 2: p tiles 2 ph, 2 ph + 1 of a head
 // (the partial last round, as in the INT8 kernel).
 template <int DT, int LC, int NS, int PW>
-__global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
+__device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_t bx, const FLds<DT, LC, NS>& ls) {
   typedef typename Store<DT>::T T;
   typedef FragF<DT> F;
   constexpr bool SPLIT = DT == DT_BF16;  // hi + lo pairs for LUT x and the weights
@@ -928,35 +942,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   constexpr int XI = (LC / 4) * C8N;     // staging items (4 rows x 8 p each)
   static_assert(XI <= kThreads, "tile split");
 
-  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];  // x^T (xT_pair layout)
-  // 16-bit (LUT x)^T [p][s] (h_off<LC>); with bf16 the LUT goes on the B side
-  __shared__ __attribute__((aligned(16))) u16 s_xs[SPLIT ? 8 : kP * LC];
-  __shared__ __attribute__((aligned(16))) u16 s_B[LC * NS];   // B rows [s][n] (h_off<NS>)
-  __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];   // 16-bit passed state [p][n] (h_off<NS>)
-  __shared__ __attribute__((aligned(16))) u16 s_H_lo[SPLIT ? kP * NS : 8];  // its residual (bf16)
-  __shared__ __attribute__((aligned(16))) float s_vec[(SPLIT ? 3 : 2) * LC];  // a*log2(e), dt (, LUT)
-  __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
+  u16* const s_xT = ls.xT;
+  u16* const s_xs = ls.xs;
+  u16* const s_B = ls.B;
+  u16* const s_H = ls.H;
+  u16* const s_H_lo = ls.H_lo;
+  float* const s_vec = ls.vec;
+  float* const s_vw = ls.vw;
   const float* vA2 = s_vec;
   const float* vDt = s_vec + LC;
   const float* vLut = s_vec + 2 * LC;  // bf16 only
 
   const Dims& d = a.d;
+  // bx: the block's index within its part of the launch
+  const int64_t slot0 = (PW == 4) ? 0 : a.nfull;
+  const bool xcd_map = (PW == 4) ? a.xcd_full : a.xcd_half;
   int64_t slot;
   int ph = 0;
   if (PW == 4) {
-    slot = a.slot0 + blockIdx.x;
-  } else if (a.xcd_map) {
-    const int64_t j = blockIdx.x / 8;
-    slot = a.slot0 + (blockIdx.x % 8) + 8 * (j >> 1);
+    slot = bx;
+  } else if (xcd_map) {
+    const int64_t j = bx / 8;
+    slot = slot0 + (bx % 8) + 8 * (j >> 1);
     ph = (int)(j & 1);
   } else {
-    slot = a.slot0 + blockIdx.x / 2;
-    ph = blockIdx.x & 1;
+    slot = slot0 + bx / 2;
+    ph = (int)(bx & 1);
   }
   const int pt_base = (PW == 4) ? 0 : 2 * ph;
   const int c8b = 2 * pt_base;  // first 8-column group of p
   int64_t unit, hl;
-  if (a.xcd_map) {
+  if (xcd_map) {
     const int64_t j = slot / 8;
     unit = (slot % 8) + 8 * (j / d.hpg);
     hl = j % d.hpg;
@@ -1360,6 +1376,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   }
 }
 
+// whole heads and p halves in one launch (as k_fused_i8)
+template <int DT, int LC, int NS>
+__global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
+  constexpr bool SPLIT = DT == DT_BF16;
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
+  __shared__ __attribute__((aligned(16))) u16 s_xs[SPLIT ? 8 : kP * LC];
+  __shared__ __attribute__((aligned(16))) u16 s_B[LC * NS];
+  __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];
+  __shared__ __attribute__((aligned(16))) u16 s_H_lo[SPLIT ? kP * NS : 8];
+  __shared__ __attribute__((aligned(16))) float s_vec[(SPLIT ? 3 : 2) * LC];
+  __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
+  const FLds<DT, LC, NS> ls{s_xT, s_xs, s_B, s_H, s_H_lo, s_vec, s_vw};
+  const int64_t bid = blockIdx.x;
+  if (bid < a.nfull)
+    fused_f16_body<DT, LC, NS, 4>(a, bid, ls);
+  else
+    fused_f16_body<DT, LC, NS, 2>(a, bid - a.nfull, ls);
+}
+
 constexpr size_t kAl = 256;
 size_t al(size_t v) { return (v + kAl - 1) / kAl * kAl; }
 
@@ -1381,28 +1416,21 @@ hipError_t launch_split(Args fa, hipStream_t st) {
   return K::launch(fa, nfull, nhalf, unit_map, unit_map && nfull % 8 == 0 && nhalf % 8 == 0, st);
 }
 
+// both parts in one launch
 template <int DT, int LC, int NS>
 struct FloatLaunch {
   static hipError_t launch(FusedFArgs fa, int64_t nfull, int64_t nhalf, bool xcd_full, bool xcd_half,
                            hipStream_t st) {
-    if (nfull > 0) {
-      fa.slot0 = 0;
-      fa.xcd_map = xcd_full;
-      hipLaunchKernelGGL((k_fused_f16<DT, LC, NS, 4>), dim3((unsigned)nfull), dim3(kThreads), 0, st, fa);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    if (nhalf > 0) {
-      fa.slot0 = nfull;
-      fa.xcd_map = xcd_half;
-      hipLaunchKernelGGL((k_fused_f16<DT, LC, NS, 2>), dim3((unsigned)(2 * nhalf)), dim3(kThreads), 0, st, fa);
-      return hipGetLastError();
-    }
-    return hipSuccess;
+    fa.nfull = nfull;
+    fa.xcd_full = xcd_full;
+    fa.xcd_half = xcd_half;
+    const int64_t blocks = nfull + 2 * nhalf;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_fused_f16<DT, LC, NS>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+    return hipGetLastError();
   }
 };
 
-// both parts in one launch (k_fused_i8)
 template <int DT, int LC, int NS>
 struct Int8Launch {
   static hipError_t launch(FusedArgs fa, int64_t nfull, int64_t nhalf, bool xcd_full, bool xcd_half,
@@ -1484,7 +1512,7 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
     hipError_t e = launch_chunk_cumsum(d, dtype, dt, A, dAcs, lut, nullptr, st);
     if (e != hipSuccess) return e;
     const FusedFArgs fa{d, X, dt, B, C, dAcs, lut, D, Y, (const float*)initial_state,
-                        (float*)final_state, 0, 0};
+                        (float*)final_state, 0, 0, 0};
     if (dtype == DT_F16) {
       if (d.l == 256 && d.N == 128) return launch_split<FloatLaunch<DT_F16, 256, 128>>(fa, st);
       if (d.l == 256) return launch_split<FloatLaunch<DT_F16, 256, 64>>(fa, st);
