@@ -1,9 +1,9 @@
 // Fused SSD forward on the persistent-INT8 path ("SSDi8" notes page, "Overall
 // framework" and "Key designs 1-3").
 //
-// A prologue launch quantises B and C once per group and a second forms the
-// float64 in-chunk cumulative sums. The main kernel runs one workgroup of eight
-// waves per (batch, head). It walks that head's chunks in order and keeps the
+// A preparation launch quantises B and C once per group and forms the float64
+// in-chunk cumulative sums (two launches when the combined grid would be too
+// large). The main kernel runs one workgroup of eight waves per (batch, head). It walks that head's chunks in order and keeps the
 // INT8 state in registers, so the state never travels through HBM. Per chunk:
 //
 //   Q(Xs)        X_scaled = LUT_state * x quantised once per (s, p) into LDS;
@@ -17,10 +17,11 @@
 //   ChunkScan2   Y_diag = W x, W = CB s_C s_B exp(a_s - a_s') dt_s'  (fp16/bf16 MFMA);
 //   StatePassing H8_k = sat(S8_k + RSH7(Q(Decay_k) H8_{k-1}))  (Eq. 6, in registers).
 //
-// While chunk k computes, chunk k+1's Q(B) rows are copied from memory straight
-// into the second of two LDS buffers, and its x tile and per-position vectors
-// are loaded into registers and written to LDS after the chunk, so HBM latency
-// overlaps the MFMA/VALU work.
+// Chunk k+1's x tile and per-position vectors are loaded into registers before
+// chunk k's ChunkState and written to LDS after its scan; its Q(B) rows are
+// then copied from memory straight into the freed LDS buffer and its Q(C) rows
+// into registers, landing during the staging and StatePassing. HBM latency
+// thus overlaps the MFMA/VALU work.
 //
 // ChunkScan2 factorisation (exact algebra): for a column tile j strictly below
 // row tile i, exp(a_s - a_s') = u_s * V_i[s'] with u_s = exp(a_s - a_{16i}) <= 1
@@ -572,7 +573,7 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-      for (int kn = 0; kn < KN; ++kn) asm volatile("" : "+v"(qc2[rr][kn]));
+      for (int q = 0; q < KN; ++q) asm volatile("" : "+v"(qc2[rr][q]));
     // next chunk: x and vectors into registers, issued before ChunkState so the
     // load issue overlaps its MFMA work (Q(B) rows follow after the scan)
     prefetch_load<DT, LC, NS, PW>(a, b, h, kn, tid, 2 * pt_base, lo, pf);
