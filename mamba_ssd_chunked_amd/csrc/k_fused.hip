@@ -54,10 +54,15 @@ __device__ __forceinline__ int xsw(int p) { return (p ^ (p >> 3)) & 7; }
 // of 32 positions (two 16-position column tiles 2m and 2m + 1): the 4-position
 // runs s = 32m + 16h + 4g + (0..3) sit at 32m + 8g + 4h + (0..3). A lane's
 // ChunkScan2 operand (group g of tiles 2m and 2m + 1) is then one 16-byte
-// chunk, index 4m + g, XOR-swizzled with the row.
+// chunk, index 4m + g. Rows are padded by 16 bytes (kXTPad elements), so 16
+// consecutive rows start in 16 different bank groups, and the two low bits of
+// the chunk index are XORed with bits 4-5 of the row, which spreads the
+// staging's writes to rows 8 apart. For the operand reads, whose 16 rows
+// share bits 4-5, the offset is then linear in m (no per-step swizzle).
+constexpr int kXTPad = 8;
 template <int LC>
 __device__ __forceinline__ int xT_pair(int p, int m, int g) {  // 16-byte chunk start
-  return p * LC + 8 * ((4 * m + g) ^ xsw(p));
+  return p * (LC + kXTPad) + 32 * m + 8 * (g ^ ((p >> 4) & 3));  // = chunk (4m + g) ^ ((p >> 4) & 3)
 }
 template <int LC>
 __device__ __forceinline__ int xT_off(int p, int s) {  // s aligned to 4
@@ -366,10 +371,9 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
     const uint32_t* w1 = (const uint32_t*)&xr[1];
     const uint32_t* w2 = (const uint32_t*)&xr[2];
     const uint32_t* w3 = (const uint32_t*)&xr[3];
-    // x^T: for p = 8 c8 + e' the row swizzle xsw(p) is e' ^ c8, and s = 4q sits in
-    // 16-byte chunk (4 (q >> 3) + (q & 3)) ^ xsw(p), half (q >> 2) & 1 of it
-    char* xTb = (char*)sm.xT + 16 * LC * c8 + 8 * ((q >> 2) & 1);
-    const int mgc = (4 * (q >> 3) + (q & 3)) ^ c8;
+    // x^T: s = 4q sits in 16-byte chunk 4 (q >> 3) + (q & 3), half (q >> 2) & 1;
+    // the rows p = 8 c8 + e' share bits 4-5 (c8 >> 1), so one base serves all 8
+    u16* const xTb = sm.xT + xT_pair<LC>(8 * c8, q >> 3, q & 3) + 4 * ((q >> 2) & 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // dword e of each row holds p = 8 c8 + 2e (low half) and 2e + 1 (high half)
@@ -377,8 +381,8 @@ __device__ __forceinline__ void prefetch_store(const FusedArgs& a, const Smem<LC
       const uint32_t lo23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
       const uint32_t hi01 = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
       const uint32_t hi23 = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
-      *(uint2*)(xTb + (2 * e) * 2 * LC + 16 * (mgc ^ (2 * e))) = make_uint2(lo01, lo23);
-      *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) = make_uint2(hi01, hi23);
+      *(uint2*)(xTb + (2 * e) * (LC + kXTPad)) = make_uint2(lo01, lo23);
+      *(uint2*)(xTb + (2 * e + 1) * (LC + kXTPad)) = make_uint2(hi01, hi23);
     }
     const float lutv[4] = {lutp.x, lutp.y, lutp.z, lutp.w};
     const float* ixl = sm.ss + kP + 8 * c8;
@@ -829,7 +833,7 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
 // other arrays).
 template <int DT, int LC, int NS, bool TAPS>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * (LC + kXTPad)];
   __shared__ __attribute__((aligned(16))) int8_t s_qB[LC * NS];
   __shared__ __attribute__((aligned(16))) int8_t s_qx[kP * LC];
   __shared__ __attribute__((aligned(16))) int8_t s_h8[kP * NS];
@@ -1039,13 +1043,12 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
       const uint32_t* w1 = (const uint32_t*)&xr[1];
       const uint32_t* w2 = (const uint32_t*)&xr[2];
       const uint32_t* w3 = (const uint32_t*)&xr[3];
-      char* xTb = (char*)s_xT + 16 * LC * c8 + 8 * ((q >> 2) & 1);
-      const int mgc = (4 * (q >> 3) + (q & 3)) ^ c8;
+      u16* const xTb = s_xT + xT_pair<LC>(8 * c8, q >> 3, q & 3) + 4 * ((q >> 2) & 1);  // as in the INT8 kernel
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *(uint2*)(xTb + (2 * e) * 2 * LC + 16 * (mgc ^ (2 * e))) =
+        *(uint2*)(xTb + (2 * e) * (LC + kXTPad)) =
             make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u), __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u));
-        *(uint2*)(xTb + (2 * e + 1) * 2 * LC + 16 * (mgc ^ (2 * e + 1))) =
+        *(uint2*)(xTb + (2 * e + 1) * (LC + kXTPad)) =
             make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u), __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
       }
       // fl32(LUT x) in the 16-bit type for 4 rows of each p (fp16 only)
@@ -1381,7 +1384,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
 template <int DT, int LC, int NS>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   constexpr bool SPLIT = DT == DT_BF16;
-  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * (LC + kXTPad)];
   __shared__ __attribute__((aligned(16))) u16 s_xs[SPLIT ? 8 : kP * LC];
   __shared__ __attribute__((aligned(16))) u16 s_B[LC * NS];
   __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];
