@@ -39,6 +39,9 @@ namespace {
 constexpr int kP = 64;        // head dim of the fused kernel
 constexpr int kThreads = 512;  // eight waves
 constexpr int kWaves = kThreads / kWave;
+// The INT8 kernel adds kProdWaves producer waves to the kWaves compute waves.
+constexpr int kProdWaves = 4;
+constexpr int kThreadsI8 = kThreads + kProdWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 2^x with the hardware transcendental (arguments here are <= 0; results that
@@ -453,13 +456,17 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
   constexpr int KS = LC / 64;      // ChunkState K steps
   constexpr int KN = NS / 64;      // K steps over N
 
-  const Smem<LC, NS> sm{s_xT, s_qB, s_qx, s_h8, s_vec, s_vw, s_ss};
-  const u16* xT = s_xT;
-  const int8_t* qxl = s_qx;
+  // x^T, Q(Xs)^T and the per-position vectors are double buffered: chunk k
+  // computes from buffer k & 1 while the producer waves stage chunk k + 1 into
+  // the other; the Q(B) rows (single buffer) are written between the two
+  // barriers of a chunk
+  constexpr int XTN = kP * (LC + kXTPad), QXN = kP * LC, VN = 2 * LC;
+  const auto smem = [&](int kc) {
+    const int o = kc & 1;
+    return Smem<LC, NS>{s_xT + o * XTN, s_qB, s_qx + o * QXN, s_h8, s_vec + o * VN, s_vw, s_ss};
+  };
   int8_t* H8l = s_h8;
   const int8_t* qBl = s_qB;
-  const float* vA2 = s_vec;
-  const float* vDt = vA2 + LC;
   float* SSl = s_ss;
 
   const Dims& d = a.d;
@@ -494,7 +501,9 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
   const int64_t b = unit / d.G;
   const int g_h = (int)(unit % d.G);
   const int h = g_h * d.hpg + (int)hl;
-  const int w = wave_id();
+  const int w = wave_id();  // compute waves 0 .. kWaves - 1, then the producers
+  const bool producer = w >= kWaves;
+  const int ptid = (int)threadIdx.x - kThreads;  // producer thread index
   const int64_t Lp = (int64_t)d.c * LC;
   const int H = d.H;
   T* const ybase = (T*)a.Y + (b * d.L * H + h) * (int64_t)kP;  // uniform
@@ -517,7 +526,7 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
 
   uint32_t H8[PTW];  // passed state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
   const bool has_init = a.init != nullptr;
-  {
+  if (!producer) {
     const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
@@ -529,29 +538,90 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
     }
   }
 
-  const LaneOff<LC, NS, PW> lo = lane_offsets<DT, LC, NS, PW>(d, tid0, 2 * pt_base);
-  // Q(C) rows (B operand over N) of this wave's two row tiles {w, 15 - w}
-  const auto load_qc2 = [&](int k, int lane, v4i (&qc)[2][KN]) {
+  // Q(C) rows (B operand over N) of row tile {w, 15 - w}[rr] of chunk k (compute waves)
+  const auto load_qc = [&](int k, int lane, int rr, v4i (&qc)[KN]) {
     const int8_t* qcb = a.qC + ((b * Lp + (int64_t)k * LC) * d.G + g_h) * (int64_t)NS;  // uniform
     const int l16 = lane & 15, lg = lane >> 4;
+    const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
+    const int8_t* src = qcb + (__umul24(16 * i + l16, d.G * NS) + 16 * lg);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
-      const int8_t* src = qcb + (__umul24(16 * i + l16, d.G * NS) + 16 * lg);
+    for (int kn = 0; kn < KN; ++kn) qc[kn] = *(const v4i*)(src + 64 * kn);
+  };
+  // the dword holding Q(Decay) of chunk k
+  const auto load_qd = [&](int k) {
+    const int64_t qi = (b * H + h) * d.c + k;
+    return *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
+  };
+
+  // Producer side: thread ptid stages x items ptid + 256 u (u < NIT, items
+  // below XI) and copies the Q(B) rows through registers, 16 bytes x QBN per
+  // thread. (XI >= l, so the threads that store the per-position vectors,
+  // ptid < l, all have an item.)
+  constexpr int NPT = kProdWaves * kWave;
+  constexpr int NIT = (PF::XI + NPT - 1) / NPT;
+  static_assert(PF::XI >= LC && (PF::XI % NPT == 0 || PF::XI < NPT), "producer split");
+  constexpr int QBN = LC * NS / 16 / NPT;
+  static_assert(QBN >= 1, "Q(B) split");
+  const auto qb_src = [&](int kc, int v) {  // Q(B) row chunk ptid + 256 v of chunk kc
+    const int ci = ptid + NPT * v;
+    const int r = ci / (NS / 16), c16 = ci % (NS / 16);
+    return a.qB + ((b * Lp + (int64_t)kc * LC + r) * d.G + g_h) * (int64_t)NS + 16 * c16;
+  };
+  // (the register arrays are passed as arguments, not captured, so they stay in
+  // registers)
+  const auto produce_load = [&](int kc, PF (&pfs)[NIT], v4i (&qbr)[QBN]) {  // issue every load of chunk kc
 #pragma unroll
-      for (int kn = 0; kn < KN; ++kn) qc[rr][kn] = *(const v4i*)(src + 64 * kn);
+    for (int v = 0; v < QBN; ++v) qbr[v] = *(const v4i*)qb_src(kc, v);
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int it = ptid + NPT * u;
+      if (it < PF::XI) {
+        const LaneOff<LC, NS, PW> lo = lane_offsets<DT, LC, NS, PW>(d, it, 2 * pt_base);
+        prefetch_load<DT, LC, NS, PW>(a, b, h, kc, it, 2 * pt_base, lo, pfs[u]);
+      }
     }
   };
-  v4i qc2[2][KN];
-  load_qc2(0, tid0 & (kWave - 1), qc2);
-  uint32_t qd_word;  // dword holding Q(Decay) of the current chunk
-  {  // chunk 0
-    PF pf;
-    dma_qb<LC, NS, PW>(a, s_qB, b, g_h, 0, w, lo);
-    prefetch_load<DT, LC, NS, PW>(a, b, h, 0, tid0, 2 * pt_base, lo, pf);
-    prefetch_store<DT, LC, NS, PW, TAPS>(a, sm, b, h, 0, tid0, 2 * pt_base, pf);
-    qd_word = pf.qd;
+  const auto produce_stage = [&](int kc, const PF (&pfs)[NIT]) {  // x^T, Q(Xs)^T, vectors of chunk kc into buffer kc & 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < NIT; ++u)
+      if (ptid + NPT * u < PF::XI)
+        prefetch_store<DT, LC, NS, PW, TAPS>(a, smem(kc), b, h, kc, ptid + NPT * u, 2 * pt_base, pfs[u]);
+  };
+  const auto produce_qb = [&](const v4i (&qbr)[QBN]) {  // the Q(B) rows into LDS (b_off layout)
+#pragma unroll
+    for (int v = 0; v < QBN; ++v) {
+      const int ci = ptid + NPT * v;
+      const int r = ci / (NS / 16), c16 = ci % (NS / 16);
+      *(v4i*)(s_qB + b_off<NS>(r, 16 * c16)) = qbr[v];
+    }
+  };
+
+  if (producer) {
+    // The producer waves run their own loop, with the same two barriers per
+    // chunk as the compute waves' loop below (so no value of one role is live
+    // in the other's loop).
+    PF pfs[NIT];
+    v4i qbr[QBN];  // (a vector type: struct copies would keep the array in scratch)
+    produce_load(0, pfs, qbr);
+    produce_stage(0, pfs);
+    produce_qb(qbr);
+    for (int k = 0; k < d.c; ++k) {
+      __syncthreads();  // chunk k staged (B1)
+      if (k + 1 < d.c) {
+        produce_load(k + 1, pfs, qbr);
+        produce_stage(k + 1, pfs);
+      }
+      __syncthreads();  // chunk k's Q(B) rows no longer read (B2)
+      if (k + 1 < d.c) produce_qb(qbr);
+    }
+    return;
   }
+
+  v4i qc2[2][KN];
+  load_qc(0, tid0 & (kWave - 1), 0, qc2[0]);
+  load_qc(0, tid0 & (kWave - 1), 1, qc2[1]);
+  uint32_t qd_cur = load_qd(0);  // dword holding Q(Decay) of the current chunk
 
   for (int k = 0; k < d.c; ++k) {
     // Lane indices re-derived from an opaque copy every chunk: the swizzled LDS
@@ -562,28 +632,30 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
     const int lane = tid & (kWave - 1);
     const int l16 = lane & 15, lg = lane >> 4;
     const int64_t t0 = (int64_t)k * LC;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(B) copies and Q(C) rows have landed
-    __syncthreads();  // chunk k staged; H8l holds H_{k-1}
-    PF pf;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's Q(C) rows and Q(Decay) have landed
+    __syncthreads();  // chunk k staged (x^T, Q(Xs), vectors, Q(B)); H8l holds H_{k-1}
     // The next chunk's loads are issued unconditionally (the last chunk reloads
     // itself): with no branch around them the compiler counts outstanding loads
     // exactly instead of waiting for all of them where the paths merge.
     const int kn = min(k + 1, d.c - 1);
-
-    // The Q(C) rows are complete (they were loaded during the previous chunk's
-    // tail); passing them through an empty asm here keeps the compiler from
-    // placing its own wait for them inside the scan loops, where the in-order
-    // load counter would also wait for every prefetch load.
+    const Smem<LC, NS> sm = smem(k);
+    const u16* xT = sm.xT;
+    const int8_t* qxl = sm.qx;
+    const float* vA2 = sm.vec;
+    const float* vDt = vA2 + LC;
+    v2s S8a[PTW], S8b[PTW];  // local state codes n = 4 lg + {0, 1} and {2, 3} of each dword
+    v4i qcn1[KN];            // Q(C) rows of row tile 15 - w of the next chunk
+    // The Q(C) rows are complete (they were loaded during the previous chunk);
+    // passing them through an empty asm here keeps the compiler from placing its
+    // own wait for them inside the scan loops.
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
       for (int q = 0; q < KN; ++q) asm volatile("" : "+v"(qc2[rr][q]));
-    // next chunk: x and vectors into registers, issued before ChunkState so the
-    // load issue overlaps its MFMA work (Q(B) rows follow after the scan)
-    prefetch_load<DT, LC, NS, PW>(a, b, h, kn, tid, 2 * pt_base, lo, pf);
+    load_qc(kn, lane, 1, qcn1);
+    const uint32_t qd_next = load_qd(kn);
 
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
-    v2s S8a[PTW], S8b[PTW];  // local state codes n = 4 lg + {0, 1} and {2, 3} of each dword
     {
       v4i acc[PTW];
       // A operand Q(B)^T[n, s] straight from the Q(B) rows with two transposing
@@ -782,18 +854,13 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
       if (rr == 0 && w >= kWaves / 2) __builtin_amdgcn_s_setprio(0);
+      if (rr == 0) load_qc(kn, lane, 0, qc2[0]);  // row tile w of the next chunk
     }
     __builtin_amdgcn_s_setprio(0);  // (also when a row tile was skipped)
-    __syncthreads();  // chunk k's tiles and H8l are no longer read
-    // stage the next chunk's x tile, then start its Q(B) rows (straight into the
-    // now free LDS buffer) and Q(C) rows; they land while StatePassing runs
-    asm volatile("" : "+v"(pf.qd));  // landed before the copies below are issued
-    prefetch_store<DT, LC, NS, PW, TAPS>(a, sm, b, h, kn, tid, 2 * pt_base, pf);
-    dma_qb<LC, NS, PW>(a, s_qB, b, g_h, kn, w, lo);
-    load_qc2(kn, lane, qc2);
+    __syncthreads();  // chunk k's tiles, Q(B) rows and H8l are no longer read; chunk k + 1 staged (B2)
 
     // ---- StatePassing (Eq. 6) in registers; publish H8 for the next ChunkScan1 ----
-    const int qd = (int)((qd_word >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
+    const int qd = (int)((qd_cur >> (8 * (((b * H + h) * d.c + k) & 3))) & 0xff);
     const v2s qd2 = {(short)qd, (short)qd};
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
@@ -811,9 +878,11 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
       if (TAPS && a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = pack_pairs(S8a[j], S8b[j]);
       if (TAPS && a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
-    qd_word = pf.qd;
+#pragma unroll
+    for (int q = 0; q < KN; ++q) qc2[1][q] = qcn1[q];
+    qd_cur = qd_next;
   }
-  // the last (redundant) Q(B) copy must land before the workgroup's LDS is released
+  // the last (redundant) loads land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (a.final_state) {
     const int l16 = tid0 & 15, lg = (tid0 & (kWave - 1)) >> 4;
@@ -832,12 +901,12 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
 // objects (the compiler then knows the Q(B) copy target aliases none of the
 // other arrays).
 template <int DT, int LC, int NS, bool TAPS>
-__global__ __launch_bounds__(kThreads, 1) void k_fused_i8(FusedArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * (LC + kXTPad)];
+__global__ __launch_bounds__(kThreadsI8, 1) void k_fused_i8(FusedArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 s_xT[2 * kP * (LC + kXTPad)];
   __shared__ __attribute__((aligned(16))) int8_t s_qB[LC * NS];
-  __shared__ __attribute__((aligned(16))) int8_t s_qx[kP * LC];
+  __shared__ __attribute__((aligned(16))) int8_t s_qx[2 * kP * LC];
   __shared__ __attribute__((aligned(16))) int8_t s_h8[kP * NS];
-  __shared__ __attribute__((aligned(16))) float s_vec[2 * LC];
+  __shared__ __attribute__((aligned(16))) float s_vec[2 * 2 * LC];
   __shared__ __attribute__((aligned(16))) float s_vw[kWaves * LC];
   __shared__ __attribute__((aligned(16))) float s_ss[3 * kP];
   const int64_t bid = blockIdx.x;
@@ -1445,9 +1514,9 @@ struct Int8Launch {
     const int64_t blocks = nfull + 2 * nhalf;
     if (blocks == 0) return hipSuccess;
     if (fa.tap_qxs || fa.tap_s32 || fa.tap_s8 || fa.tap_passed)
-      hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+      hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, true>), dim3((unsigned)blocks), dim3(kThreadsI8), 0, st, fa);
     else
-      hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
+      hipLaunchKernelGGL((k_fused_i8<DT, LC, NS, false>), dim3((unsigned)blocks), dim3(kThreadsI8), 0, st, fa);
     return hipGetLastError();
   }
 };
