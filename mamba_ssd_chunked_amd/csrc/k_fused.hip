@@ -209,9 +209,7 @@ struct FusedArgs {
   int xcd_half;  //    whole (batch, group) units
 };
 
-// LDS of one workgroup: separate arrays, so the compiler knows the Q(B) buffer
-// (written by the memory-to-LDS copies) is distinct from the others and does
-// not make their reads wait for the copies.
+// The LDS arrays of one chunk buffer of the INT8 kernel.
 template <int LC, int NS>
 struct Smem {
   u16* xT;      // x^T [p][s], 2-byte elements (swizzled, see xT_pair)
@@ -229,12 +227,11 @@ __device__ __forceinline__ int qx_off(int p, int s) {
   return p * LC + 16 * ((s >> 4) ^ xsw(p)) + (s & 15);
 }
 
-// Registers holding the next chunk's x and per-position vectors while the
-// current chunk computes (Q(B) rows go straight to LDS, see dma_qb). Thread
-// (q = tid / 8, c8 = tid % 8) owns x rows 4q .. 4q+3 at p = 8 c8 .. 8 c8 + 7.
-// Every load is unconditional (addresses are clamped into the tensor and
-// out-of-range rows are zeroed when stored to LDS), so no branch forces the
-// compiler to wait for them before the chunk's compute.
+// Registers holding one staging item of a chunk: item it = (q = it / C8N, c8 =
+// it % C8N) owns x rows 4q .. 4q+3 at p = 8 c8 .. 8 c8 + 7, plus the
+// per-position vectors of position it % l. Every load is unconditional
+// (addresses are clamped into the tensor and out-of-range rows are zeroed when
+// stored to LDS).
 template <int LC, int NS, int PW>
 struct Prefetch {
   static constexpr int C8N = 2 * PW;          // 8-column groups of p per workgroup
@@ -244,20 +241,16 @@ struct Prefetch {
   float4 lut;
   float va;     // dAcs (scaled by log2(e) when stored)
   uint32_t vd;  // dt bits in the input type (converted when stored)
-  uint32_t qd;  // the dword holding Q(Decay) of the chunk
 };
 
-// Per-lane byte offsets of the staging loads, computed once per workgroup (the
-// per-chunk parts are wave-uniform and live in scalar registers).
+// Per-item byte offsets of the staging loads (the per-chunk parts are
+// wave-uniform and live in scalar registers).
 template <int LC, int NS, int PW>
 struct LaneOff {
-  static constexpr int OPS = LC * NS / 1024;  // 1 KB Q(B) copies per chunk
-  static constexpr int PER = OPS / kWaves;
-  uint32_t q4;        // first x row of this thread (4q)
-  uint32_t xc;        // byte offset of columns 8 c8 .. 8 c8 + 7 within a row
-  uint32_t lut;       // lut / dAcs entries 4q .. 4q + 3
-  uint32_t sv;        // position of the per-position vectors (dAcs, dt)
-  uint32_t dma[PER];  // Q(B) source of each 1 KB copy
+  uint32_t q4;   // first x row of this item (4q)
+  uint32_t xc;   // byte offset of columns 8 c8 .. 8 c8 + 7 within a row
+  uint32_t lut;  // lut / dAcs entries 4q .. 4q + 3
+  uint32_t sv;   // position of the per-position vectors (dAcs, dt)
 };
 
 template <int DT, int LC, int NS, int PW>
@@ -265,7 +258,6 @@ __device__ __forceinline__ LaneOff<LC, NS, PW> lane_offsets(const Dims& d, int t
   typedef typename Store<DT>::T T;
   typedef Prefetch<LC, NS, PW> PF;
   typedef LaneOff<LC, NS, PW> LO;
-  constexpr int nch = NS / 16;
   LO o;
   const int it = tid % PF::XI;
   const int q = it / PF::C8N, c8 = c8base + it % PF::C8N;
@@ -273,14 +265,6 @@ __device__ __forceinline__ LaneOff<LC, NS, PW> lane_offsets(const Dims& d, int t
   o.xc = (uint32_t)(8 * c8 * (int)sizeof(T));
   o.lut = (uint32_t)(16 * q);
   o.sv = (uint32_t)(tid % LC);
-  const int w = tid >> 6, lane = tid & (kWave - 1);
-#pragma unroll
-  for (int m = 0; m < LO::PER; ++m) {
-    const int byte = 1024 * (w * LO::PER + m) + 16 * lane;
-    const int r = byte / NS, pc = (byte % NS) / 16;
-    const int c16 = pc ^ (r & (nch - 1) & 7);
-    o.dma[m] = (uint32_t)(r * d.G * NS + 16 * c16);
-  }
   return o;
 }
 
@@ -310,28 +294,6 @@ __device__ __forceinline__ void prefetch_load(const FusedArgs& a, int64_t b, int
     pf.vd = *(const u16*)(dtk + __umul24(min(lo.sv, lim), (uint32_t)(d.H * sizeof(T))));
   pf.lut = *(const float4*)((const char*)(a.lut + cs0) + lo.lut);
   pf.va = *(const float*)((const char*)(a.dAcs + cs0) + 4 * lo.sv);
-  const int64_t qi = (b * d.H + h) * d.c + k;
-  pf.qd = *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
-}
-
-// Q(B) rows of chunk k, copied from memory straight into LDS buffer k & 1 (no
-// registers): each wave copy moves 1 KB, lane L filling bytes 16 L .. 16 L + 15
-// of it, so the source address of each lane is chosen to produce the swizzled
-// b_off layout.
-template <int LC, int NS, int PW>
-__device__ __forceinline__ void dma_qb(const FusedArgs& a, int8_t* qBl, int64_t b, int g_h, int k, int w,
-                                       const LaneOff<LC, NS, PW>& lo) {
-  typedef LaneOff<LC, NS, PW> LO;
-  static_assert(LO::OPS % kWaves == 0 && LO::PER >= 1, "copy split");
-  const Dims& d = a.d;
-  const int8_t* qb = a.qB + ((b * (int64_t)d.c * LC + (int64_t)k * LC) * d.G + g_h) * (int64_t)NS;
-  int8_t* dst = qBl;
-#pragma unroll
-  for (int m = 0; m < LO::PER; ++m) {
-    const int gi = w * LO::PER + m;
-    __builtin_amdgcn_global_load_lds((const void*)(qb + lo.dma[m]),
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * gi), 16, 0, 0);
-  }
 }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
