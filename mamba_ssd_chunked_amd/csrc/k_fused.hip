@@ -656,11 +656,6 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
       }
     }
 
-    // Waves w and w + 4 share a SIMD, and at equal priority the older wave w is
-    // issued first, so waves 4..7 used to reach the barrier after the scan about
-    // 10% later. They run their first row tile at a raised priority.
-    if (w >= kWaves / 2) __builtin_amdgcn_s_setprio(1);
-
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
     // (outputs land as 4 consecutive p per lane for one position s)
 #pragma unroll
@@ -815,10 +810,8 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
         if (t < d.L) *(uint2*)(yrow + 16 * pt * (int)sizeof(T)) = make_uint2(pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3]));
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
-      if (rr == 0 && w >= kWaves / 2) __builtin_amdgcn_s_setprio(0);
       if (rr == 0) load_qc(kn, lane, 0, qc2[0]);  // row tile w of the next chunk
     }
-    __builtin_amdgcn_s_setprio(0);  // (also when a row tile was skipped)
     __syncthreads();  // chunk k's tiles, Q(B) rows and H8l are no longer read; chunk k + 1 staged (B2)
 
     // ---- StatePassing (Eq. 6) in registers; publish H8 for the next ChunkScan1 ----
