@@ -167,6 +167,86 @@ __global__ __launch_bounds__(kEpThreads) void k_epilogue(const void* Y,
   }
 }
 
+// Wave-per-row form, for 16-bit rows of 512 * V channels (V <= 12): a
+// workgroup of 16 waves keeps the weight and correction vectors in LDS (loaded
+// once) and each wave streams whole rows. A wave holds its row in registers as
+// loaded (16-bit, 4 V dwords per lane), forms y + alpha c for the sum of
+// squares, reduces it within the wave (no workgroup barrier per row), then
+// forms y + alpha c again (the same fused multiply-add, so the same value) for
+// the normalised write. With 16 rows in flight per CU, more of the HBM latency
+// is covered than with the workgroup-per-row form. The grid is at most one
+// workgroup per CU; its waves take rows r, r + 16 * gridDim.x, ...
+constexpr int kEpwWaves = 16;
+constexpr int kEpwMaxDc = 512 * 12;
+
+template <int DT, int V>
+__global__ __launch_bounds__(kEpwWaves * kWave) void k_epilogue_w(const void* Y,
+                                                                   const float* __restrict__ corr,
+                                                                   float alpha,
+                                                                   const float* __restrict__ weight,
+                                                                   float eps, void* out,
+                                                                   int64_t rows) {
+  static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit rows");
+  typedef typename Store<DT>::T T;
+  typedef uint32_t v4u_ __attribute__((ext_vector_type(4)));
+  constexpr int Dc = 512 * V;
+  __shared__ __attribute__((aligned(16))) float s_w[Dc];
+  __shared__ __attribute__((aligned(16))) float s_c[Dc];
+  const float* const cp = corr ? corr : weight;  // weight stands in with a zero coefficient
+  const float al = corr ? alpha : 0.f;
+  for (int i = threadIdx.x; i < Dc / 4; i += kEpwWaves * kWave) {
+    ((float4*)s_w)[i] = ((const float4*)weight)[i];
+    ((float4*)s_c)[i] = ((const float4*)cp)[i];
+  }
+  __syncthreads();
+  const int lane = lane_id();
+  const auto elem = [](const v4u_& v, int e) {
+    const uint32_t dw = v[e >> 1];
+    return Store<DT>::to_f(__builtin_bit_cast(T, (u16)((e & 1) ? (dw >> 16) : (dw & 0xffffu))));
+  };
+  for (int64_t row = (int64_t)blockIdx.x * kEpwWaves + wave_id(); row < rows;
+       row += (int64_t)gridDim.x * kEpwWaves) {
+    const int64_t base = row * (int64_t)Dc;
+    v4u_ yv[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      yv[j] = __builtin_nontemporal_load((const v4u_*)((const u16*)Y + base + (int64_t)(lane + kWave * j) * kEpVec));
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const float* c8 = s_c + (lane + kWave * j) * kEpVec;
+      const float4 c0 = *(const float4*)c8, c1 = *(const float4*)(c8 + 4);
+      const float cv[kEpVec] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int e = 0; e < kEpVec; ++e) {
+        const float t = fmaf(al, cv[e], elem(yv[j], e));
+        ss = fmaf(t, t, ss);
+      }
+    }
+#pragma unroll
+    for (int m = kWave / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    const float rs = rsqrtf(ss / (float)Dc + eps);
+    // the loaded row and the correction are opaque here, so the second pass
+    // recomputes y + alpha c instead of keeping the first pass's 8 V values live
+#pragma unroll
+    for (int j = 0; j < V; ++j) asm volatile("" : "+v"(yv[j]));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const float* c8 = s_c + (lane + kWave * j) * kEpVec;
+      const float* w8 = s_w + (lane + kWave * j) * kEpVec;
+      const float4 c0 = *(const float4*)c8, c1 = *(const float4*)(c8 + 4);
+      const float4 w0 = *(const float4*)w8, w1 = *(const float4*)(w8 + 4);
+      const float cv[kEpVec] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float wv[kEpVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float o[kEpVec];
+#pragma unroll
+      for (int e = 0; e < kEpVec; ++e) o[e] = fmaf(al, cv[e], elem(yv[j], e)) * rs * wv[e];
+      st8_nt<DT>(out, base + (int64_t)(lane + kWave * j) * kEpVec, o);
+    }
+  }
+}
+
 // c[ch] = mean over the rows of (Y_ref - Y_q)[., ch]. One workgroup per 64
 // channels: thread (phase, lane) sums rows phase, phase + 4, ... of channel
 // 64 * blockIdx.x + lane in float64, and the four phases are added in order, so
@@ -200,6 +280,34 @@ hipError_t launch_epilogue(const Dims& d, int dtype, const void* Y, const float*
                            const float* weight, float eps, void* out, hipStream_t st) {
   const int64_t rows = d.B * d.L;
   const int Dc = d.H * d.P;
+  if ((dtype == DT_F16 || dtype == DT_BF16) && Dc % 512 == 0 && Dc <= kEpwMaxDc) {
+    const int64_t ncu = cu_count() > 0 ? cu_count() : 256;
+    const dim3 gw((unsigned)min((rows + kEpwWaves - 1) / kEpwWaves, ncu));
+#define EPW_(DT_, V_) hipLaunchKernelGGL((k_epilogue_w<DT_, V_>), gw, dim3(kEpwWaves * kWave), 0, st, Y, corr, alpha, weight, eps, out, rows)
+#define EPW_DT_(DT_)                  \
+    switch (Dc / 512) {               \
+      case 1: EPW_(DT_, 1); break;     \
+      case 2: EPW_(DT_, 2); break;     \
+      case 3: EPW_(DT_, 3); break;     \
+      case 4: EPW_(DT_, 4); break;     \
+      case 5: EPW_(DT_, 5); break;     \
+      case 6: EPW_(DT_, 6); break;     \
+      case 7: EPW_(DT_, 7); break;     \
+      case 8: EPW_(DT_, 8); break;     \
+      case 9: EPW_(DT_, 9); break;     \
+      case 10: EPW_(DT_, 10); break;   \
+      case 11: EPW_(DT_, 11); break;   \
+      default: EPW_(DT_, 12); break;   \
+    }
+    if (dtype == DT_F16) {
+      EPW_DT_(DT_F16);
+    } else {
+      EPW_DT_(DT_BF16);
+    }
+#undef EPW_DT_
+#undef EPW_
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((rows + kEpRows - 1) / kEpRows));
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL(k_epilogue<DT_F32>, grid, dim3(kEpThreads), 0, st, Y, corr, alpha, weight, eps, out, Dc, rows); break;

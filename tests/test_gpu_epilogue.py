@@ -85,3 +85,30 @@ def test_epilogue_layer_shape(gpu_lib):
     for b, t in rows:
         ref = O.epilogue(y64[b:b + 1, t:t + 1], corr, O.MEAN_CORRECTION_ALPHA, wt, EPS)
         assert _elem_ok(H.f64(out[b:b + 1, t:t + 1]), ref, w.dtype) <= 1.0, (b, t)
+
+
+@pytest.mark.parametrize("dtype,nh,hp,nb,nl", [("fp16", 8, 64, 1, 37), ("bf16", 16, 64, 2, 45),
+                                                ("fp16", 48, 64, 1, 300), ("bf16", 80, 64, 1, 33),
+                                                ("fp16", 96, 64, 3, 7)])
+def test_epilogue_wave_rows(gpu_lib, dtype, nh, hp, nb, nl):
+    """Row widths of 512 * V channels (V = 1, 2, 6, 10, 12) take the wave-per-row
+    kernel: every row against the oracle, with and without a correction, row
+    counts that leave the last workgroup's waves partly idle."""
+    import torch
+    L = gpu_lib
+    print(f"epilogue wave rows {dtype} H={nh} P={hp} B={nb} L={nl}", flush=True)
+    rng = np.random.default_rng(11 + nh)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    y = torch.from_numpy(rng.standard_normal((nb, nl, nh, hp)).astype(np.float32)).to(tdt).cuda()
+    corr = (0.05 * rng.standard_normal((nh, hp))).astype(np.float32)
+    wt = (1.0 + 0.1 * rng.standard_normal((nh, hp))).astype(np.float32)
+    sh = L.make_shape(nb, nl, nh, hp, 16, 1, 64, dtype)
+    y64 = H.f64(y)
+    for c in (corr, None):
+        alpha = L.MEAN_CORRECTION_ALPHA if c is not None else 0.0
+        out = torch.empty_like(y)
+        L.ssd_epilogue(sh, y, None if c is None else torch.from_numpy(c).cuda(), alpha,
+                       torch.from_numpy(wt).cuda(), EPS, out)
+        torch.cuda.synchronize()
+        ref = O.epilogue(y64, c, alpha, wt, EPS)
+        assert _elem_ok(H.f64(out), ref, dtype) <= 1.0, (dtype, nh, c is None)
