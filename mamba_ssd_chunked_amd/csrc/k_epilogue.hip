@@ -168,15 +168,16 @@ __global__ __launch_bounds__(kEpThreads) void k_epilogue(const void* Y,
 }
 
 // Wave-per-row form, for 16-bit rows of 512 * V channels (V <= 12): a
-// workgroup of 16 waves keeps the weight and correction vectors in LDS (loaded
+// workgroup of 8 waves keeps the weight and correction vectors in LDS (loaded
 // once) and each wave streams whole rows. A wave holds its row in registers as
 // loaded (16-bit, 4 V dwords per lane), forms y + alpha c for the sum of
 // squares, reduces it within the wave (no workgroup barrier per row), then
 // forms y + alpha c again (the same fused multiply-add, so the same value) for
-// the normalised write. With 16 rows in flight per CU, more of the HBM latency
-// is covered than with the workgroup-per-row form. The grid is at most one
-// workgroup per CU; its waves take rows r, r + 16 * gridDim.x, ...
-constexpr int kEpwWaves = 16;
+// the normalised write. At about 76 VGPRs three such workgroups share a CU, so
+// 24 rows are in flight per CU, which covers more of the HBM latency than the
+// workgroup-per-row form. The grid is at most three workgroups per CU; their
+// waves take rows r, r + 8 * gridDim.x, ...
+constexpr int kEpwWaves = 8;
 constexpr int kEpwMaxDc = 512 * 12;
 
 template <int DT, int V>
@@ -282,7 +283,7 @@ hipError_t launch_epilogue(const Dims& d, int dtype, const void* Y, const float*
   const int Dc = d.H * d.P;
   if ((dtype == DT_F16 || dtype == DT_BF16) && Dc % 512 == 0 && Dc <= kEpwMaxDc) {
     const int64_t ncu = cu_count() > 0 ? cu_count() : 256;
-    const dim3 gw((unsigned)min((rows + kEpwWaves - 1) / kEpwWaves, ncu));
+    const dim3 gw((unsigned)min((rows + kEpwWaves - 1) / kEpwWaves, 3 * ncu));
 #define EPW_(DT_, V_) hipLaunchKernelGGL((k_epilogue_w<DT_, V_>), gw, dim3(kEpwWaves * kWave), 0, st, Y, corr, alpha, weight, eps, out, rows)
 #define EPW_DT_(DT_)                  \
     switch (Dc / 512) {               \
