@@ -1116,18 +1116,16 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     }
   };
   // C rows (B operand over N) of this wave's row tiles {w, 15 - w}
-  const auto load_C = [&](int kc, int lane, uint4 (&cf)[2][KNF]) {
+  // C rows of row tile {w, 15 - w}[rr] of chunk kc
+  const auto load_C = [&](int kc, int lane, int rr, uint4 (&cf)[KNF]) {
     const int t0 = kc * LC;
     const int lim = min(LC - 1, (int)d.L - 1 - t0);
     const int l16 = lane & 15, lg = lane >> 4;
     const T* c0 = Cb + (int64_t)t0 * rowB;
+    const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
+    const T* src = c0 + (__umul24(min(16 * i + l16, lim), rowB) + 8 * lg);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
-      const T* src = c0 + (__umul24(min(16 * i + l16, lim), rowB) + 8 * lg);
-#pragma unroll
-      for (int kn = 0; kn < KNF; ++kn) cf[rr][kn] = *(const uint4*)(src + 32 * kn);
-    }
+    for (int kn = 0; kn < KNF; ++kn) cf[kn] = *(const uint4*)(src + 32 * kn);
   };
 
   float Hs[PTW][4];  // fp32 state: lane (p = 16 (pt0 + j) + lane % 16, n = 16 nt_own + 4 (lane / 16) + r)
@@ -1158,7 +1156,8 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
   {  // chunk 0
     Pf pf;
     dma_B(0, tid0 & (kWave - 1));
-    load_C(0, tid0 & (kWave - 1), cf2);
+    load_C(0, tid0 & (kWave - 1), 0, cf2[0]);
+    load_C(0, tid0 & (kWave - 1), 1, cf2[1]);
     stage_load(0, tid0, pf);
     stage_store(0, tid0, pf);
   }
@@ -1181,6 +1180,10 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     const int kn1 = min(k + 1, d.c - 1);
     Pf pf;
     stage_load(kn1, tid, pf);  // issued before ChunkState (as in the INT8 kernel)
+    // the next chunk's C rows of row tile 15 - w now, those of tile w once the
+    // scan is done with them (as in the INT8 kernel)
+    uint4 cfn1[KNF];
+    load_C(kn1, lane, 1, cfn1);
 
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..) ----
     v4f sacc[PTW];
@@ -1371,11 +1374,11 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
           *(uint2*)(yrow + 32 * pt) = make_uint2(pack2<DT>(acc[jp][0], acc[jp][1]), pack2<DT>(acc[jp][2], acc[jp][3]));
       }
       __builtin_amdgcn_wave_barrier();
+      if (rr == 0) load_C(kn1, lane, 0, cf2[0]);
     }
     __syncthreads();  // chunk k's tiles and s_H are no longer read
     stage_store(kn1, tid, pf);
     dma_B(kn1, lane);
-    load_C(kn1, lane, cf2);
 
     // ---- StatePassing in fp32 registers; 16-bit copy for the next ChunkScan1 ----
     const float decay = fast_exp2(alast2);
@@ -1391,6 +1394,8 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
             make_uint2(pack2<DT>(resid16<DT>(Hs[j][0]), resid16<DT>(Hs[j][1])),
                        pack2<DT>(resid16<DT>(Hs[j][2]), resid16<DT>(Hs[j][3])));
     }
+#pragma unroll
+    for (int kn = 0; kn < KNF; ++kn) cf2[1][kn] = cfn1[kn];
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (a.final_state) {
