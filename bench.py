@@ -432,7 +432,8 @@ def main() -> int:
                          "io_only_frac": io_bytes_per_token(w) * tokens / avg_call_s / 1e9 / HBM_PEAK_GBS,
                          "frac_of_copy": achieved / copy_gbs},
         }
-    head = results.get("int8") or next(iter(results.values()))
+    head_path = "int8" if "int8" in results else next(iter(results))
+    head = results[head_path]
     out = {
         "metric": "SSD-layer tokens/s (INT8 & fp16) at 1 MI355X; % of HBM/int8-MFMA roofline",
         "value": head["value"],
@@ -448,7 +449,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
-                   "chunk": w.chunk, "input_dtype": w.dtype, "path": "int8"},
+                   "chunk": w.chunk, "input_dtype": w.dtype, "path": head_path},
         "roofline": head["roofline"],
         "paths": results,
         "kernel_source_hash": kernel_source_hash(),
