@@ -94,14 +94,13 @@ __device__ __forceinline__ FragF<DT> frag16(const u16* p) {
 // block of NT threads quantises one 64-row x N tile: tile (bx, by) with bx over
 // c * l / 64 row blocks and by over B * G.
 // ---------------------------------------------------------------------------
-template <int DT, int NT>
+template <int DT, int NT, int RB>  // RB rows of one chunk per block
 __device__ __forceinline__ void prologue_bc_block(const Dims& d, const void* __restrict__ B,
                                                   const void* __restrict__ C,
                                                   const float* __restrict__ inv_B,
                                                   const float* __restrict__ inv_C,
                                                   int8_t* __restrict__ qB,
                                                   int8_t* __restrict__ qC, int bx, int64_t by) {
-  constexpr int RB = 64;  // rows per block
   const int nsb = d.l / RB;
   const int k = bx / nsb, sb = bx % nsb;
   const int64_t bg = by;
@@ -150,14 +149,18 @@ __global__ __launch_bounds__(256) void k_prologue_bc(Dims d, const void* __restr
                                                      const float* __restrict__ inv_C,
                                                      int8_t* __restrict__ qB,
                                                      int8_t* __restrict__ qC) {
-  prologue_bc_block<DT, 256>(d, B, C, inv_B, inv_C, qB, qC, blockIdx.x, blockIdx.y);
+  prologue_bc_block<DT, 256, 64>(d, B, C, inv_B, inv_C, qB, qC, blockIdx.x, blockIdx.y);
 }
 
 // The INT8 path's preparation in one launch: blocks [0, ncs) run ChunkCumsum
-// (dAcs, LUT_state, Q(Decay)), the rest the B/C prologue. Both parts are short
-// and latency-bound, so running them side by side hides one behind the other.
+// (dAcs, LUT_state, Q(Decay)), the rest the B/C prologue, kPrepRows rows of a
+// chunk each (chunks of 128 or 256). Both parts are short and latency-bound, so
+// running them side by side hides one behind the other. Registers are capped so
+// that two blocks share a CU: at config sizes the whole grid is then resident
+// at once.
+constexpr int kPrepRows = 128;
 template <int DT>
-__global__ __launch_bounds__(kCsThreads) void k_prep_i8(Dims d, const void* __restrict__ dt,
+__global__ __launch_bounds__(kCsThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_prep_i8(Dims d, const void* __restrict__ dt,
                                                  const float* __restrict__ A,
                                                  float* __restrict__ dAcs, float* __restrict__ lut,
                                                  uint8_t* __restrict__ qdecay,
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(kCsThreads) void k_prep_i8(Dims d, const void* __re
     chunk_cumsum_block<DT>(dt, A, dAcs, lut, qdecay, d, k, b, (int)(rest / d.B));
   } else {
     const int pi = bi - ncs;
-    const int nbx = d.c * (d.l / 64);
-    prologue_bc_block<DT, kCsThreads>(d, B, C, inv_B, inv_C, qB, qC, pi % nbx, pi / nbx);
+    const int nbx = d.c * (d.l / kPrepRows);
+    prologue_bc_block<DT, kCsThreads, kPrepRows>(d, B, C, inv_B, inv_C, qB, qC, pi % nbx, pi / nbx);
   }
 }
 
@@ -1573,7 +1576,7 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
 
   // ChunkCumsum and the B/C prologue in one launch when the block count allows
   const int64_t ncs = (int64_t)d.c * d.B * ((d.H + kCsHeads - 1) / kCsHeads);
-  const int64_t npro = (int64_t)d.c * (d.l / 64) * d.B * d.G;
+  const int64_t npro = (int64_t)d.c * (d.l / kPrepRows) * d.B * d.G;
   hipError_t e;
   if (ncs + npro < ((int64_t)1 << 24) && d.B <= 65535) {
     const dim3 grid((unsigned)(ncs + npro));

@@ -353,3 +353,50 @@ def test_continuation_at_a_chunk_boundary(gpu_lib, name, path):
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([y1, y2], dim=1), y)
     assert torch.equal(f2, fin)
+
+
+def _cumsum_dt_A(dtype, L, H, seed):
+    """dt [1, L, H] and A [H] with three kinds of heads: ordinary draws (h % 5 in
+    0, 3, 4); a spread of about 2^30 in dt within each chunk (h % 5 == 1); and a
+    sum that needs 52 of float64's 53 bits when added exactly (h % 5 == 2: A
+    with a full float32 significand, one dt of 2^-24, the rest 0.1 or 0.2)."""
+    from mamba_ssd_chunked_amd import synth
+    rng = np.random.default_rng(seed)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(1, L, H)))
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), size=H))).astype(np.float32)
+    s = np.arange(L)
+    for h in range(H):
+        if h % 5 == 1:
+            dt[0, :, h] = np.where(s % 7 == 0, 2.0 ** -24, rng.uniform(1.0, 60.0, size=L))
+        elif h % 5 == 2:
+            dt[0, :, h] = 0.1 if h % 2 == 0 else 0.2
+            dt[0, 3::97, h] = 2.0 ** -24
+            A[h] = np.float32(-(1.0 + 2.0 ** -23))
+    stored = synth.cast(dt, dtype)
+    return stored, synth.to_f64(stored, dtype), A
+
+
+@pytest.mark.parametrize("dtype,chunk", [("fp16", 256), ("fp16", 64), ("bf16", 128)])
+def test_chunk_cumsum_exact_scan_and_chain(gpu_lib, dtype, chunk):
+    """dAcs must equal the sequential float64 sums bit for bit whether a head is
+    summed by the exact wave scan or by the sequential chain; the heads above
+    sit on both sides of the exactness bound (20 heads: a full and a partial
+    block of 16; a ragged last chunk)."""
+    import torch
+    L = gpu_lib
+    nh, Lseq = 20, 3 * chunk - 37
+    stored, dt64, A = _cumsum_dt_A(dtype, Lseq, nh, seed=11 + chunk)
+    nc = (Lseq + chunk - 1) // chunk
+    sh = L.make_shape(1, Lseq, nh, 64, 64, 1, chunk, dtype)
+    dt_d = torch.from_numpy(np.ascontiguousarray(stored)).cuda()
+    A_d = torch.from_numpy(A).cuda()
+    dAcs = torch.empty((1, nh, nc, chunk), dtype=torch.float32, device="cuda")
+    lut = torch.empty_like(dAcs)
+    qd = torch.empty((1, nh, nc), dtype=torch.uint8, device="cuda")
+    L.ssd_chunk_cumsum(sh, dt_d, A_d, dAcs, lut, qd)
+    torch.cuda.synchronize()
+    cs = O.chunk_cumsum(dt64, A, chunk)
+    assert np.array_equal(dAcs.cpu().numpy(), cs["dAcs"].astype(np.float32))
+    assert np.array_equal(qd.cpu().numpy(), cs["qdecay"])
+    ud = H.ulp_diff_f32(lut.cpu().numpy(), cs["lut"].astype(np.float32))
+    assert ud.max() <= 1 and (ud > 0).mean() < 1e-3
