@@ -79,8 +79,11 @@ enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_F16 = 1, SSD_DTYPE_BF16 = 2 };
  *                       floating point on B and C. */
 enum { SSD_PATH_FLOAT = 0, SSD_PATH_INT8 = 1, SSD_PATH_ABL_QX = 2, SSD_PATH_ABL_RECON = 3 };
 
-/* Problem shape. batch == 0 or seqlen == 0 is a valid empty problem (calls
- * return SSD_OK and enqueue nothing); every other size must be > 0. */
+/* Problem shape. batch == 0 or seqlen == 0 is a valid empty problem: calls
+ * return SSD_OK and enqueue nothing, except that with seqlen == 0 and batch > 0
+ * ssd_forward and ssd_state_passing write final_state (when given) as the state
+ * after no positions: a copy of initial_state, or zeros without one. Every
+ * other size must be > 0. */
 typedef struct ssd_shape {
   int64_t batch;    /* B */
   int64_t seqlen;   /* L */

@@ -711,4 +711,20 @@ hipError_t launch_chunk_scan(const Dims& d, int dtype, int mode, const void* X, 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// zero fill (16 bytes per thread, grid-stride)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_zero_fill(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, st, (uint4*)p, n16);
+  return hipGetLastError();
+}
+
 }  // namespace ssd

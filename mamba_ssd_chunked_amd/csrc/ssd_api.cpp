@@ -233,6 +233,17 @@ const char* ssd_status_string(int status) {
   }
 }
 
+// seqlen == 0 with batch > 0: the state after no positions is the initial state
+// (zero without one), so final_state, when given, receives it.
+int zero_length_state(const Dims& d, size_t elem, const void* initial_state, void* final_state,
+                      hipStream_t st) {
+  if (d.B == 0 || d.L != 0 || !final_state) return SSD_OK;
+  const size_t bytes = (size_t)d.B * d.H * d.P * d.N * elem;
+  if (initial_state)
+    return hip_status(hipMemcpyAsync(final_state, initial_state, bytes, hipMemcpyDeviceToDevice, st));
+  return hip_status(ssd::launch_zero_fill(final_state, bytes, st));
+}
+
 int ssd_quantize_bc(const ssd_shape* shape, const void* B, const void* C,
                     const ssd_scales* scales, int8_t* qB, int8_t* qC, void* stream) {
   Dims d;
@@ -291,7 +302,7 @@ int ssd_state_passing(const ssd_shape* shape, int path, void* states, const floa
   const bool i8 = path == SSD_PATH_INT8;
   if ((rc = check_ptrs({states, i8 ? (const void*)qdecay : (const void*)dAcs}))) return rc;
   if ((rc = check_opt({initial_state, final_state}))) return rc;
-  if (empty) return SSD_OK;
+  if (empty) return zero_length_state(d, i8 ? 1 : 4, initial_state, final_state, (hipStream_t)stream);
   return hip_status(ssd::launch_state_passing(d, i8, states, dAcs, qdecay, initial_state,
                                               final_state, (hipStream_t)stream));
 }
@@ -361,7 +372,7 @@ int ssd_forward(const ssd_shape* shape, int path, const void* X, const void* dt,
   int8_t* t8 = (i8 && taps) ? taps->s8_local : nullptr;
   int8_t* tp = (i8 && taps) ? taps->passed : nullptr;
   if ((rc = check_opt({initial_state, final_state, workspace, tq, ts, t8, tp}))) return rc;
-  if (empty) return SSD_OK;
+  if (empty) return zero_length_state(d, i8 ? 1 : 4, initial_state, final_state, (hipStream_t)stream);
   const size_t need = ssd_workspace_bytes(shape, path);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;

@@ -82,4 +82,8 @@ hipError_t launch_epilogue(const Dims& d, int dtype, const void* Y, const float*
 hipError_t launch_mean_correction(const Dims& d, int dtype, const void* Yr, const void* Yq, float* c,
                                   hipStream_t st);
 
+// Zero fill of a device buffer by a kernel (so that a captured graph holds no
+// memset node); bytes is a multiple of 16 and p 16-byte aligned.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
+
 }  // namespace ssd

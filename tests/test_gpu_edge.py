@@ -92,3 +92,35 @@ def test_empty_problem_writes_nothing(gpu_lib):
             L.ssd_forward(sh, path, buf, buf, A, buf, buf, A, sc, buf)
         torch.cuda.synchronize()
         assert bool((buf == 7.0).all())
+
+
+def test_zero_length_carries_the_state(gpu_lib):
+    """seqlen 0 with batch > 0: no position is processed, so the final state is
+    the initial state (zeros without one), for ssd_forward and
+    ssd_state_passing on both paths; Y is not touched."""
+    import torch
+    L = gpu_lib
+    w = H.CASES["f16_ragged"]
+    nb = 2
+    sh = L.make_shape(nb, 0, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+    n = (nb, w.nheads, w.headdim, w.dstate)
+    rng = np.random.default_rng(5)
+    buf = torch.full((64,), 7.0, dtype=torch.float16, device="cuda")
+    A = torch.zeros(w.nheads, dtype=torch.float32, device="cuda")
+    sc = L.ScalePack({k: np.ones(1024, np.float32) for k in L.ScalePack.ORDER})
+    for path, dt, ref in ((L.SSD_PATH_INT8, torch.int8, rng.integers(-127, 128, size=n).astype(np.int8)),
+                          (L.SSD_PATH_FLOAT, torch.float32, rng.standard_normal(n).astype(np.float32))):
+        init = torch.from_numpy(ref).cuda()
+        for with_init in (True, False):
+            expect = ref if with_init else np.zeros_like(ref)
+            fin = torch.full(n, 5, dtype=dt, device="cuda")
+            L.ssd_forward(sh, path, buf, buf, A, buf, buf, A, sc, buf, final_state=fin,
+                          initial_state=init if with_init else None)
+            torch.cuda.synchronize()
+            assert np.array_equal(fin.cpu().numpy(), expect)
+            fin2 = torch.full(n, 5, dtype=dt, device="cuda")
+            L.ssd_state_passing(sh, path, buf, dAcs=A, qdecay=buf, initial_state=init if with_init else None,
+                                final_state=fin2)
+            torch.cuda.synchronize()
+            assert np.array_equal(fin2.cpu().numpy(), expect)
+    assert bool((buf == 7.0).all())
