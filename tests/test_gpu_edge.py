@@ -124,3 +124,60 @@ def test_zero_length_carries_the_state(gpu_lib):
             torch.cuda.synchronize()
             assert np.array_equal(fin2.cpu().numpy(), expect)
     assert bool((buf == 7.0).all())
+
+
+def _bits(t):
+    """A tensor's storage bits, for bitwise comparison."""
+    import torch
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32) if t.element_size() == 4 else t
+
+
+@pytest.mark.parametrize("name", ["f16_ragged", "bf16_n64_l128", "w0"])
+def test_forward_replayed_from_a_graph(gpu_lib, name):
+    """ssd_forward captured in one HIP graph (workspace allocated before the
+    capture) and replayed three times, with an eager forward on other buffers
+    and a synchronisation between the replays: every replay's Y and final state
+    equal an eager call's bit for bit, on both paths (the fused kernels for the
+    fp16 and bf16 cases, the module kernels for the fp32 one)."""
+    import torch
+    L = gpu_lib
+    w = H.CASES[name]
+    consts = synth.layer_constants(w)
+    ev = synth.evaluation_batch(w, consts)
+    cal = [synth.as_f64(s, w.dtype) for s in synth.calibration_sequences(w, consts, seqlen=max(w.seqlen, 64))]
+    am = O.calibrate(cal, consts["A"], w.ngroups, w.chunk)
+    sc = L.ScalePack(O.scale_pack(am["B"], am["C"], am["Xs"], am["S"], w.nheads))
+    d = {k: H.to_dev(v, w.dtype) for k, v in ev.items()}
+    A = torch.from_numpy(consts["A"]).cuda()
+    D = torch.from_numpy(consts["D"]).cuda()
+    sh = H.shape_of(L, w)
+    n = (w.batch, w.nheads, w.headdim, w.dstate)
+    for path in (L.SSD_PATH_INT8, L.SSD_PATH_FLOAT):
+        i8 = path == L.SSD_PATH_INT8
+        scp = sc if i8 else None
+        fdt = torch.int8 if i8 else torch.float32
+        nws = max(1, L.ssd_workspace_bytes(sh, path))
+
+        def fwd(y, fin, ws):
+            L.ssd_forward(sh, path, d["x"], d["dt"], A, d["B"], d["C"], D, scp, y, final_state=fin, workspace=ws)
+
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        y_ref, f_ref = torch.empty_like(d["x"]), torch.empty(n, dtype=fdt, device="cuda")
+        fwd(y_ref, f_ref, ws)
+        torch.cuda.synchronize()
+        y, fin = torch.zeros_like(d["x"]), torch.zeros(n, dtype=fdt, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fwd(y, fin, ws)
+        y_e, f_e = torch.empty_like(d["x"]), torch.empty(n, dtype=fdt, device="cuda")
+        ws_e = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        for rep in range(3):
+            y.zero_()
+            fin.zero_()
+            g.replay()
+            fwd(y_e, f_e, ws_e)  # eager work between the replays
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(y), _bits(y_ref)), (path, rep)
+            assert torch.equal(_bits(fin), _bits(f_ref)), (path, rep)
+            assert torch.equal(_bits(y_e), _bits(y_ref)), (path, rep)
+        del g
