@@ -272,15 +272,20 @@ def rounding_shift(v, shift: int):
 def scale_pack(amax_B, amax_C, amax_Xs, amax_S, nheads: int, bits: int = 8) -> dict:
     """Static scale pack from calibration maxima (R1).
 
-    s = fp32(amax / q_max) (s = 1 when amax is 0 or not finite); inv = fp32(1 / s);
+    s = fp32(amax / q_max) (s = 1 when amax is 0: an empty range); inv = fp32(1 / s);
     M_req[h,p] = fp32(s_X[h,p] * s_B[g(h)] / s_S[h,p]). Returns float32 arrays.
+
+    A maximum that is negative, NaN or infinite raises ValueError: the static
+    scales of "Training strategy" are ranges of finite calibration activations
+    (the SSM inputs are finite), so such a maximum has no scale.
     """
     qm = float(qmax_of(bits))
 
     def step(a):
         a = np.asarray(a, np.float64)
-        ok = (a > 0) & np.isfinite(a)
-        return np.where(ok, a / qm, 1.0).astype(np.float32)
+        if not np.all(np.isfinite(a)) or np.any(a < 0):
+            raise ValueError("calibration maxima must be finite and >= 0")
+        return np.where(a > 0, a / qm, 1.0).astype(np.float32)
 
     s_B, s_C, s_X, s_S = step(amax_B), step(amax_C), step(amax_Xs), step(amax_S)
     G = s_B.shape[0]
@@ -505,10 +510,12 @@ def calibrate_x(seqs) -> np.ndarray:
 
 def scale_pack_x(amax_X, bits: int = 8) -> dict:
     """Step and inverse step of Q(X) (R15) by the pack rule of R1:
-    s_Xq = fp32(amax / q_max) (1 when amax is 0 or not finite), inv_Xq = fp32(1 / s_Xq)."""
+    s_Xq = fp32(amax / q_max) (1 when amax is 0), inv_Xq = fp32(1 / s_Xq); a
+    negative or non-finite maximum raises ValueError, as in scale_pack."""
     a = np.asarray(amax_X, np.float64)
-    ok = (a > 0) & np.isfinite(a)
-    s = np.where(ok, a / float(qmax_of(bits)), 1.0).astype(np.float32)
+    if not np.all(np.isfinite(a)) or np.any(a < 0):
+        raise ValueError("calibration maxima must be finite and >= 0")
+    s = np.where(a > 0, a / float(qmax_of(bits)), 1.0).astype(np.float32)
     return {"s_Xq": s, "inv_Xq": (1.0 / s.astype(np.float64)).astype(np.float32)}
 
 

@@ -245,9 +245,85 @@ def test_scale_pack_algebra():
     assert sc["M_req"][1, 0] == np.float32(m)
     for k in ("s_B", "s_C", "inv_B", "inv_C", "s_X", "inv_X", "s_S", "M_req"):
         assert sc[k].dtype == np.float32
-    # a non-finite maximum also gives a unit step, as in the library's host routine
-    sc2 = O.scale_pack(np.array([np.inf, np.nan]), amC, amX, amS, nheads=2)
-    assert sc2["s_B"][0] == 1.0 and sc2["s_B"][1] == 1.0 and sc2["inv_B"][0] == 1.0
+    # a maximum that is not a finite range of activations has no scale
+    for bad in (np.inf, np.nan, -1.0):
+        with pytest.raises(ValueError):
+            O.scale_pack(np.array([bad, 1.0]), amC, amX, amS, nheads=2)
+        with pytest.raises(ValueError):
+            O.scale_pack(amB, amC, amX, np.array([[bad, 1.0], [1.0, 1.0]]), nheads=2)
+        with pytest.raises(ValueError):
+            O.scale_pack_x(np.array([[bad, 1.0]]))
+
+
+# Calibration axes ("Key design 2": the X_scaled and state scales are per
+# (H, P) and never span N; "Key design 3": B and C are quantised along G). The
+# inputs below are zero except where stated, so each maximum is known by hand
+# and a reduction over a wrong axis puts a nonzero where a zero belongs.
+def _calib_seq(b, L, H, P, N, G):
+    z = lambda *s: np.zeros(s)  # noqa: E731
+    return {"x": z(b, L, H, P), "dt": z(b, L, H), "B": z(b, L, G, N), "C": z(b, L, G, N)}
+
+
+def test_calibrate_xs_is_per_head_and_channel():
+    L, H, P, N, l = 8, 3, 4, 2, 4
+    delta = 0.25
+    A = np.array([-0.5, -1.0, -2.0])
+    s1, s2 = _calib_seq(1, L, H, P, N, 1), _calib_seq(1, L, H, P, N, 1)
+    for sq in (s1, s2):
+        sq["dt"][:] = delta
+        sq["B"][:] = 1.0
+        sq["C"][:] = 1.0
+    s1["x"][0, 1, 2, 3] = 1.75      # chunk 0, position 1, head 2, channel 3
+    s2["x"][0, 6, 0, 1] = -4.0      # chunk 1, position 2, head 0, channel 1
+    am = O.calibrate([s1, s2], A, ngroups=1, chunk=l)
+    # LUT_state of position s in a chunk of constant dt: dt exp(dt A (l - 1 - s))
+    want = np.zeros((H, P))
+    want[2, 3] = 1.75 * delta * math.exp(delta * A[2] * (l - 1 - 1))
+    want[0, 1] = 4.0 * delta * math.exp(delta * A[0] * (l - 1 - 2))
+    assert am["Xs"].shape == (H, P)
+    np.testing.assert_allclose(am["Xs"], want, rtol=1e-14, atol=0)
+
+
+def test_calibrate_bc_is_per_group():
+    L, H, P, N, G = 8, 4, 2, 3, 2
+    s1 = _calib_seq(1, L, H, P, N, G)
+    s1["dt"][:] = 0.1
+    s1["B"][0, 5, 1, 0] = -3.0
+    s1["C"][0, 2, 0, 1] = 2.5
+    s2 = _calib_seq(1, L, H, P, N, G)
+    s2["C"][0, 7, 0, 2] = -4.5
+    am = O.calibrate([s1, s2], -np.ones(H), ngroups=G, chunk=4)
+    assert am["B"].shape == (G,) and am["C"].shape == (G,)
+    np.testing.assert_array_equal(am["B"], [0.0, 3.0])
+    np.testing.assert_array_equal(am["C"], [4.5, 0.0])
+
+
+def test_calibrate_state_is_per_head_and_channel():
+    # one position: the padded chunk has dt = 0 past it, so LUT_state = dt and
+    # the chunk state is S[h,p,n] = dt_h x[h,p] B[n] (= the passed state)
+    H, P, N = 2, 3, 2
+    s1 = _calib_seq(1, 1, H, P, N, 1)
+    s1["dt"][0, 0] = [0.5, 0.125]
+    s1["x"][0, 0] = [[1.0, -2.0, 3.0], [0.5, 4.0, -1.5]]
+    s1["B"][0, 0, 0] = [0.5, -2.0]
+    am = O.calibrate([s1], np.array([-1.0, -3.0]), ngroups=1, chunk=4)
+    want = np.array([0.5, 0.125])[:, None] * np.abs(s1["x"][0, 0]) * 2.0
+    assert am["S"].shape == (H, P)
+    np.testing.assert_allclose(am["S"], want, rtol=1e-15, atol=0)
+
+
+def test_calibrate_state_takes_local_and_passed_maxima():
+    # chunks of one position, H = P = N = 1: S_0 = d, H_0 = d; S_1 = d x_1,
+    # H_1 = e^{d a} d + d x_1. One scale serves both kinds of state.
+    d, a = 0.5, -0.2
+    for x1, want in ((0.5, d * (math.exp(d * a) + 0.5)),    # passed state is larger
+                     (-3.0, 3.0 * d)):                       # local state is larger
+        s = _calib_seq(1, 2, 1, 1, 1, 1)
+        s["dt"][:] = d
+        s["x"][0, :, 0, 0] = [1.0, x1]
+        s["B"][:] = 1.0
+        am = O.calibrate([s], np.array([a]), ngroups=1, chunk=1)
+        assert am["S"][0, 0] == pytest.approx(want, rel=1e-14)
 
 
 # PIN7: high-bit convergence of the INT8 method toward the float64 definition.
@@ -312,6 +388,17 @@ def test_constants_match_the_page():
     assert O.rounding_shift(np.array([g["S"]["value"] * 5]), g["shift_k"]["value"])[0] == 5
     cs = O.chunk_cumsum(np.zeros((1, 4, 1)), np.array([-1.0], np.float32), 4)
     assert cs["qdecay"].max() == g["S"]["value"]      # decay 1 maps to S
+    # the scale axes the page names are the axes of the calibration maxima
+    b, L, Hh, P, N, G = 1, 8, 4, 3, 5, 2
+    sizes = {"H": Hh, "P": P, "N": N, "G": G}
+    seq = _calib_seq(b, L, Hh, P, N, G)
+    seq["dt"][:] = 0.1
+    am = O.calibrate([seq], -np.ones(Hh), ngroups=G, chunk=4)
+    state_axes = tuple(sizes[a] for a in g["state_scale_axes"]["value"])
+    bc_axes = tuple(sizes[a] for a in g["bc_scale_axis"]["value"])
+    assert am["S"].shape == state_axes and am["Xs"].shape == state_axes
+    assert am["B"].shape == bc_axes and am["C"].shape == bc_axes
+    assert "N" not in g["state_scale_axes"]["value"]
 
 
 # R13: continuation from an initial state. Splitting a sequence at a chunk
@@ -479,9 +566,9 @@ def test_recon_mode_shares_the_int8_chunk_state():
 
 def test_qx_scale_pack_follows_the_pack_rule():
     """Q(X)'s step uses the same rule as every other scale (R1): compare with the
-    X_scaled entry of scale_pack on the same maxima, including zero and
-    non-finite maxima."""
-    a = np.array([[3.0, 0.0], [np.inf, 1e-30]])
+    X_scaled entry of scale_pack on the same maxima, including zero and tiny
+    maxima (non-finite ones raise in both, test_scale_pack_algebra)."""
+    a = np.array([[3.0, 0.0], [2.5e3, 1e-30]])
     px = O.scale_pack_x(a)
     ref = O.scale_pack(np.ones(1), np.ones(1), a, np.ones((2, 2)), nheads=2)
     assert np.array_equal(px["s_Xq"], ref["s_X"]) and np.array_equal(px["inv_Xq"], ref["inv_X"])
