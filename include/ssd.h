@@ -59,7 +59,8 @@ enum {
   SSD_E_ALIGN = 4,       /* a buffer is not 16-byte aligned */
   SSD_E_WORKSPACE = 5,   /* workspace smaller than ssd_workspace_bytes() */
   SSD_E_HIP = 6,         /* the HIP runtime reported a launch error */
-  SSD_E_INTERNAL = 7
+  SSD_E_INTERNAL = 7,
+  SSD_E_VALUE = 8        /* a calibration maximum is negative, NaN or infinite */
 };
 
 /* Element type of X, dt, B, C and Y. */
@@ -275,8 +276,10 @@ size_t ssd_calibrate_workspace_bytes(const ssd_shape* shape);
  * amax = [amax_B[G], amax_C[G], amax_Xs[H*P], amax_S[H*P]];
  * pack (host, 4*G + 4*H*P floats) = [s_B, s_C, inv_B, inv_C (G each),
  * s_X, inv_X, s_S, M_req (H*P each)], with s = fp32(amax / 127) (1 when
- * amax is 0 or not finite), inv = fp32(1 / s), M_req = fp32(s_X s_B / s_S)
- * evaluated in float64. */
+ * amax is 0, an empty range), inv = fp32(1 / s), M_req = fp32(s_X s_B / s_S)
+ * evaluated in float64. A maximum that is negative, NaN or infinite has no
+ * scale ("Training strategy": static ranges of finite calibration
+ * activations): the call then returns SSD_E_VALUE and writes nothing. */
 int ssd_scales_from_amax(int64_t ngroups, int64_t nheads, int64_t headdim,
                          const float* amax, float* pack);
 

@@ -28,6 +28,7 @@ SSD_E_ALIGN = 4
 SSD_E_WORKSPACE = 5
 SSD_E_HIP = 6
 SSD_E_INTERNAL = 7
+SSD_E_VALUE = 8
 
 SSD_DTYPE_F32 = 0
 SSD_DTYPE_F16 = 1

@@ -185,6 +185,50 @@ __global__ __launch_bounds__(kCsThreads) __attribute__((amdgpu_waves_per_eu(8)))
 }
 
 // ---------------------------------------------------------------------------
+// Block -> head. Slots 0 .. B*H - 1 list every head once. With unit_map
+// ((B*G) % 8 == 0) slot s serves unit (s % 8) + 8 ((s / 8) / hpg), head
+// (s / 8) % hpg of that unit (unit = batch * G + group), so slots on one XCD
+// (block i runs on XCD i % 8) cover whole units and the int8 B/C rows of a
+// unit stay in one XCD's L2; otherwise slot s is unit s / hpg. Whole-head
+// blocks [0, nfull) take slot = block. The p-half blocks after them take slots
+// nfull .. B*H - 1, two blocks per slot: with half_il (nfull and the half count
+// both multiples of 8) block nfull + bx takes slot nfull + bx % 8 + 8 (j / 2)
+// and half j % 2 (j = bx / 8), so it runs on its slot's XCD; otherwise slot
+// nfull + bx / 2 and half bx % 2. One slot map serves both parts, so every
+// head is computed exactly once.
+// ---------------------------------------------------------------------------
+struct BlockHead {
+  int64_t unit, hl;
+  int ph;
+};
+template <int PW>
+__device__ __forceinline__ BlockHead block_head(const Dims& d, int64_t bx, int64_t nfull, int unit_map,
+                                                int half_il) {
+  BlockHead r;
+  int64_t slot;
+  r.ph = 0;
+  if (PW == 4) {
+    slot = bx;
+  } else if (half_il) {
+    const int64_t j = bx / 8;
+    slot = nfull + (bx % 8) + 8 * (j >> 1);
+    r.ph = (int)(j & 1);
+  } else {
+    slot = nfull + bx / 2;
+    r.ph = (int)(bx & 1);
+  }
+  if (unit_map) {
+    const int64_t j = slot / 8;
+    r.unit = (slot % 8) + 8 * (j / d.hpg);
+    r.hl = j % d.hpg;
+  } else {
+    r.unit = slot / d.hpg;
+    r.hl = slot % d.hpg;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // main fused kernel
 // ---------------------------------------------------------------------------
 struct FusedArgs {
@@ -208,8 +252,8 @@ struct FusedArgs {
   // launch layout: blocks [0, nfull) run whole heads (slots 0 .. nfull - 1), the
   // rest run p halves of heads nfull .. (two blocks per head)
   int64_t nfull;
-  int xcd_full;  // 1: the slots of that part are laid out so each XCD serves
-  int xcd_half;  //    whole (batch, group) units
+  int unit_map;  // slot -> head map that keeps whole (batch, group) units on one XCD
+  int half_il;   // the p-half blocks are interleaved by 8 (see block_head)
 };
 
 // The LDS arrays of one chunk buffer of the INT8 kernel.
@@ -435,33 +479,10 @@ __device__ __forceinline__ void fused_i8_body(const FusedArgs& a, const int64_t 
   float* SSl = s_ss;
 
   const Dims& d = a.d;
-  // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8). With
-  // xcd_map, slot s runs on XCD s % 8 and every XCD gets whole (batch, group)
-  // units, so the int8 Q(B)/Q(C) rows its heads share stay in that XCD's L2.
   // bx: the block's index within its part of the launch
-  const int64_t slot0 = (PW == 4) ? 0 : a.nfull;
-  const bool xcd_map = (PW == 4) ? a.xcd_full : a.xcd_half;
-  int64_t slot;
-  int ph = 0;
-  if (PW == 4) {
-    slot = bx;
-  } else if (xcd_map) {
-    const int64_t j = bx / 8;
-    slot = slot0 + (bx % 8) + 8 * (j >> 1);
-    ph = (int)(j & 1);
-  } else {
-    slot = slot0 + bx / 2;
-    ph = (int)(bx & 1);
-  }
-  int64_t unit, hl;
-  if (xcd_map) {
-    const int64_t j = slot / 8;
-    unit = (slot % 8) + 8 * (j / d.hpg);
-    hl = j % d.hpg;
-  } else {
-    unit = slot / d.hpg;
-    hl = slot % d.hpg;
-  }
+  const BlockHead bh = block_head<PW>(d, bx, a.nfull, a.unit_map, a.half_il);
+  const int64_t unit = bh.unit, hl = bh.hl;
+  const int ph = bh.ph;
   const int pt_base = (PW == 4) ? 0 : 2 * ph;  // first p tile of this workgroup
   const int64_t b = unit / d.G;
   const int g_h = (int)(unit % d.G);
@@ -941,8 +962,8 @@ struct FusedFArgs {
   const float* init;  // optional initial state [B,H,P,N] fp32
   float* final_state;
   int64_t nfull;  // launch layout as in FusedArgs
-  int xcd_full;
-  int xcd_half;
+  int unit_map;
+  int half_il;
 };
 
 // LDS arrays of the float kernel, declared once per kernel (see k_fused_i8)
@@ -987,31 +1008,11 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
 
   const Dims& d = a.d;
   // bx: the block's index within its part of the launch
-  const int64_t slot0 = (PW == 4) ? 0 : a.nfull;
-  const bool xcd_map = (PW == 4) ? a.xcd_full : a.xcd_half;
-  int64_t slot;
-  int ph = 0;
-  if (PW == 4) {
-    slot = bx;
-  } else if (xcd_map) {
-    const int64_t j = bx / 8;
-    slot = slot0 + (bx % 8) + 8 * (j >> 1);
-    ph = (int)(j & 1);
-  } else {
-    slot = slot0 + bx / 2;
-    ph = (int)(bx & 1);
-  }
+  const BlockHead bh = block_head<PW>(d, bx, a.nfull, a.unit_map, a.half_il);
+  const int64_t unit = bh.unit, hl = bh.hl;
+  const int ph = bh.ph;
   const int pt_base = (PW == 4) ? 0 : 2 * ph;
   const int c8b = 2 * pt_base;  // first 8-column group of p
-  int64_t unit, hl;
-  if (xcd_map) {
-    const int64_t j = slot / 8;
-    unit = (slot % 8) + 8 * (j / d.hpg);
-    hl = j % d.hpg;
-  } else {
-    unit = slot / d.hpg;
-    hl = slot % d.hpg;
-  }
   const int64_t b = unit / d.G;
   const int g_h = (int)(unit % d.G);
   const int h = g_h * d.hpg + (int)hl;
@@ -1448,18 +1449,17 @@ hipError_t launch_split(Args fa, hipStream_t st) {
     if (rem != 0 && 2 * rem <= ncu) nhalf = rem;
   }
   const int64_t nfull = BH - nhalf;
-  const bool unit_map = (d.B * d.G) % 8 == 0;
-  return K::launch(fa, nfull, nhalf, unit_map, unit_map && nfull % 8 == 0 && nhalf % 8 == 0, st);
+  return K::launch(fa, nfull, nhalf, (d.B * d.G) % 8 == 0, nfull % 8 == 0 && nhalf % 8 == 0, st);
 }
 
 // both parts in one launch
 template <int DT, int LC, int NS>
 struct FloatLaunch {
-  static hipError_t launch(FusedFArgs fa, int64_t nfull, int64_t nhalf, bool xcd_full, bool xcd_half,
+  static hipError_t launch(FusedFArgs fa, int64_t nfull, int64_t nhalf, bool unit_map, bool half_il,
                            hipStream_t st) {
     fa.nfull = nfull;
-    fa.xcd_full = xcd_full;
-    fa.xcd_half = xcd_half;
+    fa.unit_map = unit_map;
+    fa.half_il = half_il;
     const int64_t blocks = nfull + 2 * nhalf;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_fused_f16<DT, LC, NS>), dim3((unsigned)blocks), dim3(kThreads), 0, st, fa);
@@ -1469,11 +1469,11 @@ struct FloatLaunch {
 
 template <int DT, int LC, int NS>
 struct Int8Launch {
-  static hipError_t launch(FusedArgs fa, int64_t nfull, int64_t nhalf, bool xcd_full, bool xcd_half,
+  static hipError_t launch(FusedArgs fa, int64_t nfull, int64_t nhalf, bool unit_map, bool half_il,
                            hipStream_t st) {
     fa.nfull = nfull;
-    fa.xcd_full = xcd_full;
-    fa.xcd_half = xcd_half;
+    fa.unit_map = unit_map;
+    fa.half_il = half_il;
     const int64_t blocks = nfull + 2 * nhalf;
     if (blocks == 0) return hipSuccess;
     if (fa.tap_qxs || fa.tap_s32 || fa.tap_s8 || fa.tap_passed)
@@ -1491,16 +1491,13 @@ hipError_t launch_main(const FusedArgs& fa, hipStream_t st) {
 
 }  // namespace
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (0 when the runtime cannot say). Asked
+// of the runtime on every call, so the library keeps no mutable state.
 int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
-  }
-  return cached[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
 }
 
 bool fused_supported(const Dims& d, int dtype, bool int8) {

@@ -215,6 +215,17 @@ int forward_ablation(const Dims& d, int dtype, int path, const void* X, const vo
   return SSD_OK;
 }
 
+// seqlen == 0 with batch > 0: the state after no positions is the initial state
+// (zero without one), so final_state, when given, receives it.
+int zero_length_state(const Dims& d, size_t elem, const void* initial_state, void* final_state,
+                      hipStream_t st) {
+  if (d.B == 0 || d.L != 0 || !final_state) return SSD_OK;
+  const size_t bytes = (size_t)d.B * d.H * d.P * d.N * elem;
+  if (initial_state)
+    return hip_status(hipMemcpyAsync(final_state, initial_state, bytes, hipMemcpyDeviceToDevice, st));
+  return hip_status(ssd::launch_zero_fill(final_state, bytes, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,19 +240,9 @@ const char* ssd_status_string(int status) {
     case SSD_E_WORKSPACE: return "workspace too small";
     case SSD_E_HIP: return "HIP runtime error";
     case SSD_E_INTERNAL: return "internal error";
+    case SSD_E_VALUE: return "a calibration maximum is negative, NaN or infinite";
     default: return "unknown status";
   }
-}
-
-// seqlen == 0 with batch > 0: the state after no positions is the initial state
-// (zero without one), so final_state, when given, receives it.
-int zero_length_state(const Dims& d, size_t elem, const void* initial_state, void* final_state,
-                      hipStream_t st) {
-  if (d.B == 0 || d.L != 0 || !final_state) return SSD_OK;
-  const size_t bytes = (size_t)d.B * d.H * d.P * d.N * elem;
-  if (initial_state)
-    return hip_status(hipMemcpyAsync(final_state, initial_state, bytes, hipMemcpyDeviceToDevice, st));
-  return hip_status(ssd::launch_zero_fill(final_state, bytes, st));
 }
 
 int ssd_quantize_bc(const ssd_shape* shape, const void* B, const void* C,
@@ -530,9 +531,12 @@ int ssd_scales_from_amax(int64_t ngroups, int64_t nheads, int64_t headdim, const
   if (!amax || !pack) return SSD_E_NULL;
   if (ngroups <= 0 || nheads <= 0 || headdim <= 0 || nheads % ngroups) return SSD_E_SHAPE;
   const int64_t G = ngroups, HP = nheads * headdim, hpg = nheads / ngroups;
+  // every maximum is checked before anything is written
+  for (int64_t i = 0; i < 2 * G + 2 * HP; ++i)
+    if (!std::isfinite(amax[i]) || amax[i] < 0.f) return SSD_E_VALUE;
   auto step = [](float a) -> float {
     const double v = (double)a;
-    if (!(v > 0.0) || !std::isfinite(v)) return 1.0f;
+    if (!(v > 0.0)) return 1.0f;  // an empty range
     return (float)(v / 127.0);
   };
   float* s_B = pack;

@@ -32,10 +32,16 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(L.LIB, n), n
     assert set(names) == set(L.EXPORTED)
+    # and the library exports no other C (unmangled) function
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB._name], capture_output=True, text=True).stdout
+    c_syms = {ln.split()[-1] for ln in out.splitlines()
+              if len(ln.split()) == 3 and ln.split()[1] == "T" and not ln.split()[-1].startswith("_")}
+    assert c_syms == set(names), c_syms ^ set(names)
 
 
 def test_status_strings():
-    for rc in range(8):
+    for rc in range(9):
         assert L.status_string(rc)
     assert L.status_string(99) == "unknown status"
 
@@ -161,6 +167,17 @@ def test_scales_from_amax_matches_the_oracle_rule():
     for k in ("s_B", "s_C", "inv_B", "inv_C", "s_X", "inv_X", "s_S", "M_req"):
         assert np.array_equal(got[k], ref[k].reshape(-1)), k
     assert L.LIB.ssd_scales_from_amax(2, 5, 16, amax.ctypes.data, got["s_B"].ctypes.data) == L.SSD_E_SHAPE
+    # a maximum that is negative or not finite has no scale, on both sides, and
+    # the call writes nothing
+    for i, bad in ((0, np.inf), (3, np.nan), (2 * G + 5, -1.0), (amax.size - 1, -np.inf)):
+        a2 = amax.copy()
+        a2[i] = bad
+        pack = np.full(4 * G + 4 * H * P, 7.0, np.float32)
+        assert L.LIB.ssd_scales_from_amax(G, H, P, a2.ctypes.data, pack.ctypes.data) == L.SSD_E_VALUE
+        assert np.all(pack == 7.0)
+        parts = np.split(a2.astype(np.float64), [G, 2 * G, 2 * G + H * P])
+        with pytest.raises(ValueError):
+            O.scale_pack(parts[0], parts[1], parts[2].reshape(H, P), parts[3].reshape(H, P), H)
 
 
 def test_decode_step_validates():
