@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kCsThreads) void k_chunk_cumsum(const void* __restr
                                                       float* __restrict__ dAcs,
                                                       float* __restrict__ lut,
                                                       uint8_t* __restrict__ qdecay, Dims d) {
-  chunk_cumsum_block<DT>(dt, A, dAcs, lut, qdecay, d, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ CsLds cs;
+  chunk_cumsum_block<DT>(dt, A, dAcs, lut, qdecay, d, blockIdx.x, blockIdx.y, blockIdx.z, cs);
 }
 
 // ---------------------------------------------------------------------------

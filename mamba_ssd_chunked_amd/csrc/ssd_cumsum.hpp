@@ -39,16 +39,23 @@ __device__ __forceinline__ int cs_lsb_exp(double p) {
   return E - 1075 + (int)__builtin_ctzll(m);
 }
 
+// LDS the block body needs (the caller provides it, so that launches holding
+// other block kinds can share one allocation).
+struct CsLds {
+  float sdt[kCsHeads][256 + 1];
+  double sa[kCsHeads][256];  // the sequential chain's prefixes (fallback only)
+};
+
 template <int DT>
 __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
                                                    const float* __restrict__ A,
                                                    float* __restrict__ dAcs,
                                                    float* __restrict__ lut,
                                                    uint8_t* __restrict__ qdecay, const Dims& d,
-                                                   int k, int64_t b, int hblk) {
+                                                   int k, int64_t b, int hblk, CsLds& cs) {
   constexpr int kPer = kCsHeads * 256 / kCsThreads;  // staged entries per thread (chunks <= 256)
-  __shared__ float sdt[kCsHeads][256 + 1];
-  __shared__ double sa[kCsHeads][256];  // the sequential chain's prefixes (fallback only)
+  float(&sdt)[kCsHeads][256 + 1] = cs.sdt;
+  double(&sa)[kCsHeads][256] = cs.sa;
   const int h0 = hblk * kCsHeads;
   const int nh = min(kCsHeads, d.H - h0);
   const int l = d.l;

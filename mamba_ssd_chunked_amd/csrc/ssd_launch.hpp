@@ -61,6 +61,14 @@ hipError_t launch_forward_fused(const Dims& d, int dtype, bool int8, const void*
 size_t fused_workspace_bytes(const Dims& d, bool int8);
 bool fused_supported(const Dims& d, int dtype, bool int8);
 
+// Fused INT8 forward (k_fused_i8.hip): ChunkCumsum, the per-(batch, chunk,
+// group) B/C quantisation and ChunkBMM, then the per-head main kernel.
+hipError_t launch_forward_i8(const Dims& d, int dtype, const void* X, const void* dt, const float* A,
+                             const void* B, const void* C, const float* D, const ScalePtrs& sc, void* Y,
+                             const void* init, void* final_state, void* ws, int8_t* tap_qxs, int32_t* tap_s32,
+                             int8_t* tap_s8, int8_t* tap_passed, hipStream_t st);
+size_t fused_i8_workspace_bytes(const Dims& d);
+
 // Calibration helpers (k_calib.hip).
 hipError_t launch_amax_bc(const Dims& d, int dtype, const void* B, const void* C, float* amax_B,
                           float* amax_C, hipStream_t st);
@@ -68,7 +76,7 @@ hipError_t launch_amax_xs(const Dims& d, int dtype, const void* X, const float* 
                           float* amax_X, hipStream_t st);
 hipError_t launch_amax_states(const Dims& d, const float* states, float* amax_S, hipStream_t st);
 
-// Compute units of the current device (cached per device; 0 if unknown).
+// Compute units of the current device (0 if unknown).
 int cu_count();
 
 // Single-token decode step (seqlen 1), state [B,H,P,N] updated in place.
