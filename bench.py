@@ -356,6 +356,8 @@ def main() -> int:
     ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step (prints its JSON object)")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_ID,
+                    help="workload id of the headline line (default: the 2.7B-shaped layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the SSD layer runs on a single MI355X here "
@@ -368,7 +370,7 @@ def main() -> int:
     from mamba_ssd_chunked_amd import _lib as L
     from mamba_ssd_chunked_amd import synth
 
-    w = synth.WORKLOADS[WORKLOAD_ID]
+    w = synth.WORKLOADS[args.workload]
     consts = synth.layer_constants(w)
     ev = synth.evaluation_batch(w, consts)
     dev = {k: torch.from_numpy(v).cuda() for k, v in ev.items()}

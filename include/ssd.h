@@ -94,8 +94,23 @@ typedef struct ssd_shape {
   int64_t ngroups;  /* G, divides H */
   int64_t chunk;    /* l */
   int32_t dtype;    /* SSD_DTYPE_* */
-  int32_t reserved; /* must be 0 */
+  int32_t schedule; /* SSD_SCHED_*: 0 (auto) unless a schedule is wanted */
 } ssd_shape;
+
+/* Work schedule of ssd_forward on SSD_PATH_INT8 with fp16 or bf16 inputs
+ * (other calls, paths and dtypes accept any of these values and ignore it;
+ * any other value returns SSD_E_SHAPE):
+ *   SSD_SCHED_HEAD   one persistent workgroup per head walks its chunks in
+ *                    order, the state kept on chip (fewest HBM bytes);
+ *   SSD_SCHED_CHUNK  ChunkState for every chunk in parallel, StatePassing,
+ *                    then ChunkScan for every chunk in parallel (more bytes,
+ *                    but B * c * H workgroups fill the GPU when B * H heads
+ *                    cannot);
+ *   SSD_SCHED_AUTO   SSD_SCHED_CHUNK when B * H is below twice the device's
+ *                    compute-unit count, SSD_SCHED_HEAD otherwise.
+ * Both give the same integers (taps, final state) and Y to within fp32
+ * rounding order; ssd_workspace_bytes depends on the schedule. */
+enum { SSD_SCHED_AUTO = 0, SSD_SCHED_HEAD = 1, SSD_SCHED_CHUNK = 2 };
 
 /* Static scale pack of the INT8 path (device fp32 arrays). Step sizes
  * s = amax / 127 ("Key design 2" and "Training strategy": static symmetric

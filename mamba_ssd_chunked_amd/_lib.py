@@ -37,6 +37,9 @@ SSD_PATH_FLOAT = 0
 SSD_PATH_INT8 = 1
 SSD_PATH_ABL_QX = 2
 SSD_PATH_ABL_RECON = 3
+SSD_SCHED_AUTO = 0
+SSD_SCHED_HEAD = 1
+SSD_SCHED_CHUNK = 2
 
 DTYPE_CODE = {torch.float32: SSD_DTYPE_F32, torch.float16: SSD_DTYPE_F16,
               torch.bfloat16: SSD_DTYPE_BF16}
@@ -48,7 +51,7 @@ class SsdShape(ctypes.Structure):
                 ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32)]
 
     @property
     def nchunks(self) -> int:
@@ -147,9 +150,10 @@ def _stream(stream):
     return None
 
 
-def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype) -> SsdShape:
+def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+               schedule=0) -> SsdShape:
     code = dtype if isinstance(dtype, int) else DTYPE_CODE[DTYPE_NAME.get(dtype, dtype)]
-    return SsdShape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, code, 0)
+    return SsdShape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, code, schedule)
 
 
 class ScalePack:

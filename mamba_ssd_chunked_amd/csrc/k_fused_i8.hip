@@ -35,77 +35,14 @@
 #include "ssd_cumsum.hpp"
 #include "ssd_device.hpp"
 #include "ssd_fused.hpp"
+#include "ssd_i8_layout.hpp"
 #include "ssd_launch.hpp"
 
 namespace ssd {
 namespace {
 
-constexpr int kHP = 64;                       // head dim covered (P)
 constexpr int kCompW = 8;                     // waves per workgroup
 constexpr int kCompT = kCompW * kWave;        // 512
-constexpr float kLn2Inv = 1.4426950408889634f;  // log2(e)
-
-typedef int v2i_t __attribute__((ext_vector_type(2)));
-typedef unsigned u2v_t __attribute__((ext_vector_type(2)));
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef short v8s_t __attribute__((ext_vector_type(8)));
-
-// ChunkScan2 operand fragments per (batch, chunk, group): row tile i (16
-// positions s) pairs with column tiles (2m, 2m + 1), m = 0 .. i / 2.
-__host__ __device__ constexpr int cb_frags(int lc) {
-  int n = 0;
-  for (int i = 0; i < lc / 16; ++i) n += i / 2 + 1;
-  return n;
-}
-__host__ __device__ constexpr int cb_frag_base(int i) {  // sum over i' < i of (i' / 2 + 1)
-  return (i & 1) ? ((i + 1) / 2) * ((i + 1) / 2) : (i / 2) * (i / 2 + 1);
-}
-
-// The power of two E of the CB' fragments of a group: t = N 127^2 s_C s_B bounds
-// |CB s_C s_B|; with t = f 2^e, f in [0.5, 1), |CB s_C s_B 2^(15 - e)| < 2^15.
-__device__ __forceinline__ int cb_exp(float scb, int N) {
-  const float t = scb * (float)(N * 16129);
-  const int e = (int)((__float_as_uint(t) >> 23) & 0xff) - 126;
-  return min(max(15 - e, -100), 100);
-}
-
-// Transposing LDS reads. 8-bit: the 16 lanes of a group each point at 8 bytes;
-// lanes 2r, 2r + 1 form row r (16 bytes) of an 8 x 16 byte matrix and lane i
-// receives column i (byte i of rows 0..7). 16-bit: lanes 4r .. 4r + 3 form row r
-// (16 elements) of a 4 x 16 matrix and lane i receives element i of rows 0..3.
-__device__ __forceinline__ v2i_t ldtr8(const int8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_t*)(int8_t*)p);
-}
-__device__ __forceinline__ v4s_t ldtr16(const u16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(u16*)p);
-}
-
-// byte tiles [rows][W]: 16-byte chunks XOR-swizzled with the low row bits
-template <int W>
-__device__ __forceinline__ int bsw(int r, int c) {
-  constexpr int nch = W / 16;
-  return r * W + 16 * ((c >> 4) ^ (r & (nch - 1) & 7)) + (c & 15);
-}
-
-// x tile [s][64] (2-byte elements, rows of 128 bytes): the 16-byte chunk index
-// is XORed with 2 ((s ^ (s >> 2)) & 3). The transposing reads of a ChunkScan2
-// operand (16 consecutive rows, 32 bytes each) and the producers' row writes
-// are then free of bank conflicts, and the swizzle of row s = 32 m + 16 h +
-// 4 g + r is 2 (g ^ r), the same for every m and h.
-__device__ __forceinline__ int xsw_off(int s, int p) {  // element offset; p multiple of 4
-  return s * kHP + 8 * ((p >> 3) ^ (2 * ((s ^ (s >> 2)) & 3))) + (p & 7);
-}
-// Q(X_scaled) tile [s][64] (bytes): chunk index XOR ((s >> 1) & 3) ^ ((s >> 4) & 3);
-// for the ChunkState reads (rows s = 64 ks + 16 g + 8 h + r) that is (r >> 1) ^ g.
-__device__ __forceinline__ int qsw_off(int s, int p) {  // byte offset; p multiple of 8
-  return s * kHP + 16 * ((p >> 4) ^ (((s >> 1) & 3) ^ ((s >> 4) & 3))) + (p & 15);
-}
-// Position order of the per-position tables that ChunkScan2 reads by K slot:
-// s' = 32 m + 16 h + 4 g + r sits at 32 m + 8 g + 4 h + r, so lane group g reads
-// its eight K values (h = 0, 1; r = 0..3) as 32 contiguous bytes.
-__device__ __forceinline__ int kperm(int s) {
-  return (s & ~31) + 8 * ((s >> 2) & 3) + 4 * ((s >> 4) & 1) + (s & 3);
-}
 
 // ===========================================================================
 // Preparation launch (1024 threads per block). Blocks [0, ncs) run
@@ -364,8 +301,8 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     else
       r.vd = *(const u16*)((const T*)a.dt + (b * d.L + tv) * H + h);
   };
-  const float4 ix0 = *(const float4*)&a.sc.inv_X[h * kHP + 8 * c8];
-  const float4 ix1 = *(const float4*)&a.sc.inv_X[h * kHP + 8 * c8 + 4];
+  const float4 ix0 = ld_scale4(&a.sc.inv_X[h * kHP + 8 * c8]);
+  const float4 ix1 = ld_scale4(&a.sc.inv_X[h * kHP + 8 * c8 + 4]);
   const float ix[8] = {ix0.x, ix0.y, ix0.z, ix0.w, ix1.x, ix1.y, ix1.z, ix1.w};
   const auto stage_store = [&](int kc, const SRegs<LC>& r) {
     const int o = kc & 1;
@@ -399,11 +336,10 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
       else
         dtv = Store<DT>::to_f(__builtin_bit_cast(T, (u16)r.vd));
       if (t0 + sv >= d.L) dtv = 0.f;
-      const float A2 = r.va * kLn2Inv;
-      // B_s = a_s log2(e) - log2(dt_s) + E, so exp2(A - B_s) = exp(.. - a_s) dt_s 2^-E
-      // (dt = 0 past L gives B = +inf and weight 0)
+      float A2, B2;
+      scan_vectors(r.va, dtv, Eg, A2, B2);
       s_va[o * LC + sv] = A2;
-      s_vb[o * LC + kperm(sv)] = A2 - __builtin_amdgcn_logf(dtv) + Eg;
+      s_vb[o * LC + kperm(sv)] = B2;
     }
   };
 
@@ -738,6 +674,11 @@ hipError_t launch_i8v2(const Dims& d, const void* X, const void* dt, const float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  if (use_chunked_i8(d)) {
+    int8_t* states = (int8_t*)((char*)ws + i8_states_offset(d));
+    return launch_chunked_i8(d, DT, X, dt, qC, qbt, cbf, dAcs, lut, qd, D, sc, Y, init, final_state, states, tap_qxs,
+                             tap_s32, tap_s8, tap_passed, st);
+  }
   const SplitPlan p = split_plan(d);
   const I8Args fa{d, X, dt, qC, qbt, cbf, dAcs, lut, qd, D, sc, Y, (const int8_t*)init, (int8_t*)final_state,
                   tap_qxs, tap_s32, tap_s8, tap_passed, p.nfull, p.unit_map, p.half_il};
@@ -752,12 +693,27 @@ hipError_t launch_i8v2(const Dims& d, const void* X, const void* dt, const float
 
 }  // namespace
 
-size_t fused_i8_workspace_bytes(const Dims& d) {
+// Workspace: Q(C) rows, Q(B)^T fragments, CB' fragments, dAcs, LUT_state,
+// Q(Decay), then (chunk-parallel schedule) the int8 states [B, c, H, P, N].
+size_t i8_states_offset(const Dims& d) {
   const size_t Lp = (size_t)d.c * d.l;
   const size_t bkg = (size_t)d.B * d.c * d.G;
   const size_t cs = (size_t)d.B * d.H * d.c * d.l * sizeof(float);
   return ws_align((size_t)d.B * Lp * d.G * d.N) + ws_align(bkg * d.N * d.l) +
          ws_align(bkg * cb_frags(d.l) * 1024) + 2 * ws_align(cs) + ws_align((size_t)d.B * d.H * d.c);
+}
+
+// The chunk-parallel schedule serves layers whose heads cannot fill the chip
+// with one workgroup per head (measured: at B*H = 64 and 80 on 256 CUs it is
+// 2-5x faster; at B*H = 512 and 640 the head-persistent kernel is 1.2x faster).
+bool use_chunked_i8(const Dims& d) {
+  if (d.sched == kSchedHead) return false;
+  if (d.sched == kSchedChunk) return true;
+  return d.B * d.H < 2 * (int64_t)cu_count();
+}
+
+size_t fused_i8_workspace_bytes(const Dims& d) {
+  return i8_states_offset(d) + (use_chunked_i8(d) ? ws_align(chunked_i8_states_bytes(d)) : 0);
 }
 
 hipError_t launch_forward_i8(const Dims& d, int dtype, const void* X, const void* dt, const float* A,

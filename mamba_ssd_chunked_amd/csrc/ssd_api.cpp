@@ -29,7 +29,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 // Validates the shape; fills d. *empty is set for batch == 0 or seqlen == 0.
 int check_shape(const ssd_shape* s, Dims* d, bool* empty) {
   if (!s) return SSD_E_NULL;
-  if (s->reserved != 0) return SSD_E_SHAPE;
+  if (s->schedule < SSD_SCHED_AUTO || s->schedule > SSD_SCHED_CHUNK) return SSD_E_SHAPE;
   if (s->batch < 0 || s->seqlen < 0) return SSD_E_SHAPE;
   if (s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 || s->ngroups <= 0 || s->chunk <= 0)
     return SSD_E_SHAPE;
@@ -64,6 +64,7 @@ int check_shape(const ssd_shape* s, Dims* d, bool* empty) {
   d->l = (int)s->chunk;
   d->c = (int)c;
   d->hpg = d->H / d->G;
+  d->sched = s->schedule;
   *empty = (s->batch == 0 || s->seqlen == 0);
   return SSD_OK;
 }

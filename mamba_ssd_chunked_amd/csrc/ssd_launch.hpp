@@ -10,6 +10,7 @@ namespace ssd {
 struct Dims {
   int64_t B, L;
   int H, P, N, G, l, c, hpg;
+  int sched;  // kSched* of the shape (INT8 forward only)
 };
 
 struct ScalePtrs {
@@ -24,6 +25,9 @@ struct ScalePtrs {
   const float* s_Xq;
   const float* inv_Xq;
 };
+
+// INT8 forward schedules; the values equal the C ABI's SSD_SCHED_* codes.
+enum { kSchedAuto = 0, kSchedHead = 1, kSchedChunk = 2 };
 
 // Module-kernel modes; the values equal the C ABI's SSD_PATH_* codes.
 enum { kModeFloat = 0, kModeInt8 = 1, kModeQx = 2, kModeRecon = 3 };
@@ -68,6 +72,17 @@ hipError_t launch_forward_i8(const Dims& d, int dtype, const void* X, const void
                              const void* init, void* final_state, void* ws, int8_t* tap_qxs, int32_t* tap_s32,
                              int8_t* tap_s8, int8_t* tap_passed, hipStream_t st);
 size_t fused_i8_workspace_bytes(const Dims& d);
+size_t i8_states_offset(const Dims& d);
+bool use_chunked_i8(const Dims& d);
+
+// Chunk-parallel schedule of the fused INT8 forward (k_chunked_i8.hip), run on
+// the preparation launch's outputs; states: int8 [B, c, H, P, N] workspace.
+hipError_t launch_chunked_i8(const Dims& d, int dtype, const void* X, const void* dt, const int8_t* qC,
+                             const int8_t* qbt, const uint16_t* cbf, const float* dAcs, const float* lut,
+                             const uint8_t* qdecay, const float* D, const ScalePtrs& sc, void* Y, const void* init,
+                             void* final_state, int8_t* states, int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
+                             int8_t* tap_passed, hipStream_t st);
+size_t chunked_i8_states_bytes(const Dims& d);
 
 // Calibration helpers (k_calib.hip).
 hipError_t launch_amax_bc(const Dims& d, int dtype, const void* B, const void* C, float* amax_B,

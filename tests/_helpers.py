@@ -55,9 +55,14 @@ def dev_inputs(case: Case) -> dict:
     return d
 
 
-def shape_of(L, w: synth.Workload, batch=None, seqlen=None):
+# INT8 forward schedules the parity tests run (by name -> SSD_SCHED_* value).
+SCHEDULES = {"head": 1, "chunk": 2}
+
+
+def shape_of(L, w: synth.Workload, batch=None, seqlen=None, schedule=0):
+    sched = SCHEDULES[schedule] if isinstance(schedule, str) else schedule
     return L.make_shape(w.batch if batch is None else batch, w.seqlen if seqlen is None else seqlen,
-                        w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+                        w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype, sched)
 
 
 def torch_dtype(dtype: str):
@@ -106,3 +111,9 @@ def ulp_diff_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
     bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
     return np.abs(ai - bi)
+
+
+def bits(t):
+    """A device or host tensor's stored bits, for bitwise comparison (NaN included)."""
+    import torch
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()])

@@ -87,10 +87,22 @@ def test_invalid_shapes(kw, rc):
     assert fwd(shape(**kw)) == rc
 
 
-def test_reserved_must_be_zero():
+@pytest.mark.parametrize("sched", [-1, 3, 1 << 20])
+def test_unknown_schedule(sched):
     sh = shape()
-    sh.reserved = 1
+    sh.schedule = sched
     assert fwd(sh) == L.SSD_E_SHAPE
+
+
+def test_schedule_sets_int8_workspace():
+    # the chunk-parallel schedule keeps every chunk's int8 state in the
+    # workspace, the head-persistent one keeps it on chip; the float path has
+    # one schedule
+    def ws(sched, path):
+        return L.ssd_workspace_bytes(L.make_shape(2, 1000, 8, 64, 128, 1, 256, "fp16", sched), path)
+
+    assert ws(L.SSD_SCHED_CHUNK, L.SSD_PATH_INT8) >= ws(L.SSD_SCHED_HEAD, L.SSD_PATH_INT8) + 2 * 4 * 8 * 64 * 128
+    assert ws(L.SSD_SCHED_CHUNK, L.SSD_PATH_FLOAT) == ws(L.SSD_SCHED_HEAD, L.SSD_PATH_FLOAT)
 
 
 def test_null_and_alignment():

@@ -18,7 +18,7 @@ from tests import _helpers as H
 pytestmark = pytest.mark.gpu
 
 
-def _run_both(L, torch, w, consts, ev):
+def _run_both(L, torch, w, consts, ev, sched=0):
     e = synth.as_f64(ev, w.dtype)
     cal = [synth.as_f64(s, w.dtype) for s in synth.calibration_sequences(w, consts, seqlen=max(w.seqlen, 64))]
     am = O.calibrate(cal, consts["A"], w.ngroups, w.chunk)
@@ -28,7 +28,7 @@ def _run_both(L, torch, w, consts, ev):
     d = {k: H.to_dev(v, w.dtype) for k, v in ev.items()}
     A = torch.from_numpy(consts["A"]).cuda()
     D = torch.from_numpy(consts["D"]).cuda()
-    sh = H.shape_of(L, w)
+    sh = H.shape_of(L, w, schedule=sched)
     y8 = torch.empty_like(d["x"])
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
     stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
@@ -41,19 +41,20 @@ def _run_both(L, torch, w, consts, ev):
     return r8, yf, y8, fin, taps, y32
 
 
+@pytest.mark.parametrize("sched", list(H.SCHEDULES))
 @pytest.mark.parametrize("name", ["f16_ragged", "w0", "bf16_n64_l128"])
-def test_degenerate_decays(gpu_lib, name):
+def test_degenerate_decays(gpu_lib, name, sched):
     import torch
     L = gpu_lib
     w = H.CASES[name]
-    print(f"degenerate decays {name}", flush=True)
+    print(f"degenerate decays {name} {sched}", flush=True)
     consts = synth.layer_constants(w)
     A = consts["A"].copy()
     A[0] = 0.0
     A[-1] = -1e4
     consts = dict(consts, A=A)
     ev = synth.evaluation_batch(w, consts)
-    r8, yf, y8, fin, taps, y32 = _run_both(L, torch, w, consts, ev)
+    r8, yf, y8, fin, taps, y32 = _run_both(L, torch, w, consts, ev, sched)
     qd = r8["cumsum"]["qdecay"]
     assert (qd[:, 0] == 128).all() and (qd[:, -1] == 0).all()
     assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
@@ -62,17 +63,18 @@ def test_degenerate_decays(gpu_lib, name):
     assert H.chan_err(H.f64(y32), yf, w.dtype) <= 2e-2
 
 
+@pytest.mark.parametrize("sched", list(H.SCHEDULES))
 @pytest.mark.parametrize("seqlen", [1, 17, 255, 256, 257])
-def test_short_sequences(gpu_lib, seqlen):
+def test_short_sequences(gpu_lib, seqlen, sched):
     """One position, a partial chunk, exactly one chunk, one past it (the
     fused kernels at chunk 256)."""
     import torch
     L = gpu_lib
     w = H.CASES["f16_ragged"].replace(seqlen=seqlen)
-    print(f"short sequence L={seqlen}", flush=True)
+    print(f"short sequence L={seqlen} {sched}", flush=True)
     consts = synth.layer_constants(w)
     ev = synth.evaluation_batch(w, consts)
-    r8, yf, y8, fin, taps, y32 = _run_both(L, torch, w, consts, ev)
+    r8, yf, y8, fin, taps, y32 = _run_both(L, torch, w, consts, ev, sched)
     assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
     assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
     assert H.chan_err(H.f64(y8), r8["y"], w.dtype) <= 5e-2
@@ -126,12 +128,6 @@ def test_zero_length_carries_the_state(gpu_lib):
     assert bool((buf == 7.0).all())
 
 
-def _bits(t):
-    """A tensor's storage bits, for bitwise comparison."""
-    import torch
-    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32) if t.element_size() == 4 else t
-
-
 @pytest.mark.parametrize("name", ["f16_ragged", "bf16_n64_l128", "w0"])
 def test_forward_replayed_from_a_graph(gpu_lib, name):
     """ssd_forward captured in one HIP graph (workspace allocated before the
@@ -150,9 +146,9 @@ def test_forward_replayed_from_a_graph(gpu_lib, name):
     d = {k: H.to_dev(v, w.dtype) for k, v in ev.items()}
     A = torch.from_numpy(consts["A"]).cuda()
     D = torch.from_numpy(consts["D"]).cuda()
-    sh = H.shape_of(L, w)
     n = (w.batch, w.nheads, w.headdim, w.dstate)
-    for path in (L.SSD_PATH_INT8, L.SSD_PATH_FLOAT):
+    for path, sched in ((L.SSD_PATH_INT8, "head"), (L.SSD_PATH_INT8, "chunk"), (L.SSD_PATH_FLOAT, 0)):
+        sh = H.shape_of(L, w, schedule=sched)
         i8 = path == L.SSD_PATH_INT8
         scp = sc if i8 else None
         fdt = torch.int8 if i8 else torch.float32
@@ -177,7 +173,7 @@ def test_forward_replayed_from_a_graph(gpu_lib, name):
             g.replay()
             fwd(y_e, f_e, ws_e)  # eager work between the replays
             torch.cuda.synchronize()
-            assert torch.equal(_bits(y), _bits(y_ref)), (path, rep)
-            assert torch.equal(_bits(fin), _bits(f_ref)), (path, rep)
-            assert torch.equal(_bits(y_e), _bits(y_ref)), (path, rep)
+            assert torch.equal(H.bits(y), H.bits(y_ref)), (path, sched, rep)
+            assert torch.equal(H.bits(fin), H.bits(f_ref)), (path, sched, rep)
+            assert torch.equal(H.bits(y_e), H.bits(y_ref)), (path, sched, rep)
         del g

@@ -204,11 +204,13 @@ def _modular_int8(L, torch, c, d, sh, sc):
     return {"passed": st.cpu().numpy(), "y": H.f64(y)}
 
 
+@pytest.mark.parametrize("sched", list(H.SCHEDULES))
 @pytest.mark.parametrize("name", CASE_NAMES)
-def test_forward_int8(gpu_lib, name):
+def test_forward_int8(gpu_lib, name, sched):
     L = gpu_lib
-    torch, c, r8, (yf, _, _, _), d, sh, sc = _setup(L, name)
+    torch, c, r8, (yf, _, _, _), d, _, sc = _setup(L, name)
     w = c.w
+    sh = H.shape_of(L, w, schedule=sched)
     y = torch.empty_like(d["x"])
     stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
@@ -236,6 +238,27 @@ def test_forward_int8(gpu_lib, name):
     ym = _modular_int8(L, torch, c, d, sh, sc)
     assert np.array_equal(ym["passed"], r8["passed"])
     assert H.chan_err(ym["y"], H.f64(y)) <= 5e-2
+
+
+@pytest.mark.parametrize("name", CASE_NAMES)
+def test_int8_schedules_agree(gpu_lib, name):
+    """The head-persistent and chunk-parallel schedules do the same arithmetic
+    per output element, so they give the same final state and Y bit for bit."""
+    L = gpu_lib
+    torch, c, _, _, d, _, sc = _setup(L, name)
+    w = c.w
+    out = {}
+    for sched in H.SCHEDULES:
+        y = torch.empty_like(d["x"])
+        fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
+        L.ssd_forward(H.shape_of(L, w, schedule=sched), L.SSD_PATH_INT8, d["x"], d["dt"], d["A"], d["B"],
+                      d["C"], d["D"], sc, y, final_state=fin)
+        torch.cuda.synchronize()
+        out[sched] = (y.cpu(), fin.cpu().numpy())
+    (yh, fh), (yc, fc) = out["head"], out["chunk"]
+    assert np.array_equal(fh, fc)
+    print(f"{name}: head vs chunk Y max channel error {H.chan_err(H.f64(yc), H.f64(yh)):.3g}", flush=True)
+    assert torch.equal(H.bits(yh), H.bits(yc))
 
 
 @pytest.mark.parametrize("name", CASE_NAMES)
@@ -285,11 +308,13 @@ def _init_int8(w, seed=7):
     return rng.integers(-127, 128, size=(w.batch, w.nheads, w.headdim, w.dstate)).astype(np.int8)
 
 
+@pytest.mark.parametrize("sched", list(H.SCHEDULES))
 @pytest.mark.parametrize("name", CASE_NAMES)
-def test_forward_int8_initial_state(gpu_lib, name):
+def test_forward_int8_initial_state(gpu_lib, name, sched):
     L = gpu_lib
-    torch, c, _, _, d, sh, sc = _setup(L, name)
+    torch, c, _, _, d, _, sc = _setup(L, name)
     w, e = c.w, c.ev64
+    sh = H.shape_of(L, w, schedule=sched)
     h0 = _init_int8(w)
     r = O.forward_int8(e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"], c.scales, w.chunk,
                        h_init=h0.astype(np.int64))
@@ -322,15 +347,17 @@ def test_forward_float_initial_state(gpu_lib, name):
     assert np.abs(fg - hr).max() <= 2e-1 * np.sqrt(np.mean(hr * hr))
 
 
-@pytest.mark.parametrize("path", ["int8", "float"])
+@pytest.mark.parametrize("path", ["int8-head", "int8-chunk", "float"])
 @pytest.mark.parametrize("name", ["f16_ragged", "bf16_n64_l128", "w0"])
 def test_continuation_at_a_chunk_boundary(gpu_lib, name, path):
     """Two calls (the second starting from the first's final state) give bitwise
     the outputs and final state of one call over the whole sequence."""
     L = gpu_lib
-    torch, c, _, _, d, sh, sc = _setup(L, name)
+    torch, c, _, _, d, _, sc = _setup(L, name)
     w = c.w
-    i8 = path == "int8"
+    i8 = path != "float"
+    sched = path.split("-")[1] if i8 else 0
+    sh = H.shape_of(L, w, schedule=sched)
     p = L.SSD_PATH_INT8 if i8 else L.SSD_PATH_FLOAT
     scales = sc if i8 else None
     fdt = torch.int8 if i8 else torch.float32
@@ -340,8 +367,8 @@ def test_continuation_at_a_chunk_boundary(gpu_lib, name, path):
     L.ssd_forward(sh, p, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], scales, y, final_state=fin)
     L1 = w.chunk
     part = lambda t, a_, b_: t[:, a_:b_].contiguous()  # noqa: E731
-    sh1 = H.shape_of(L, w, seqlen=L1)
-    sh2 = H.shape_of(L, w, seqlen=w.seqlen - L1)
+    sh1 = H.shape_of(L, w, seqlen=L1, schedule=sched)
+    sh2 = H.shape_of(L, w, seqlen=w.seqlen - L1, schedule=sched)
     y1 = torch.empty_like(part(d["x"], 0, L1))
     y2 = torch.empty_like(part(d["x"], L1, None))
     f1 = torch.empty(fshape, dtype=fdt, device="cuda")

@@ -4,7 +4,8 @@ and state size they cover.
 With 128 < B*H < 256 heads on 256 CUs the launcher runs every head as one
 workgroup (no p-half split), so these shapes take the whole-head code path
 (all four 16-wide p tiles per workgroup) at l = 128 and N = 64, which the
-other cases reach only through the half-head path. INT8: every tap (Q(Xs),
+other cases reach only through the half-head path. The INT8 cases run under
+both schedules (head-persistent and chunk-parallel). INT8: every tap (Q(Xs),
 S32, S8, passed states) bit-exact against the oracle, the final state too, Y
 within 5e-2; float: Y within 2e-2 of the float64 definition, the final state
 within the bound the module tests use.
@@ -37,16 +38,17 @@ def _case(name):
     return c, r8, yf, hf
 
 
+@pytest.mark.parametrize("sched", list(H.SCHEDULES))
 @pytest.mark.parametrize("name", list(SHAPES))
-def test_whole_head_int8(gpu_lib, name):
+def test_whole_head_int8(gpu_lib, name, sched):
     import torch
     L = gpu_lib
-    print(f"whole-head int8 {name}", flush=True)
+    print(f"whole-head int8 {name} {sched}", flush=True)
     c, r8, _, _ = _case(name)
     w = c.w
     assert 128 < w.batch * w.nheads < 256
     d = H.dev_inputs(c)
-    sh = H.shape_of(L, w)
+    sh = H.shape_of(L, w, schedule=sched)
     y = torch.empty_like(d["x"])
     stshape = (w.batch, w.nchunks, w.nheads, w.headdim, w.dstate)
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.int8, device="cuda")
