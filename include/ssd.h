@@ -60,7 +60,9 @@ enum {
   SSD_E_WORKSPACE = 5,   /* workspace smaller than ssd_workspace_bytes() */
   SSD_E_HIP = 6,         /* the HIP runtime reported a launch error */
   SSD_E_INTERNAL = 7,
-  SSD_E_VALUE = 8        /* a calibration maximum is negative, NaN or infinite */
+  SSD_E_VALUE = 8,       /* a calibration maximum is negative, NaN or infinite */
+  SSD_E_TOO_LARGE = 9    /* ssd_forward_noalloc: the problem needs more workspace
+                            than SSD_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Element type of X, dt, B, C and Y. */
@@ -274,6 +276,26 @@ int ssd_mean_correction(const ssd_shape* shape, const void* Y_ref, const void* Y
 
 /* Workspace bytes ssd_forward needs (0 for an invalid shape). Host only. */
 size_t ssd_workspace_bytes(const ssd_shape* shape, int path);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ssd_forward
+ * with the same arguments, less workspace and workspace_bytes, whose workspace
+ * is a fixed array of SSD_NOALLOC_SCRATCH_BYTES bytes of device memory that the
+ * library holds on each device it runs on, from that device's first call until
+ * the process ends. The call allocates nothing. It uses the current device's
+ * array (the stream must belong to the current device). A problem whose
+ * ssd_workspace_bytes exceeds that size returns SSD_E_TOO_LARGE and enqueues
+ * nothing; with shape->schedule SSD_SCHED_AUTO the head-persistent INT8
+ * schedule is taken when the chunk-parallel one would not fit. All calls on
+ * one device share its array: calls that may overlap on one device (different
+ * streams, or host threads without ordering) race and must not be made. The
+ * results equal ssd_forward's bit for bit; nothing in the array needs to start
+ * at zero. Other errors as ssd_forward. */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int ssd_forward_noalloc(const ssd_shape* shape, int path, const void* X, const void* dt,
+                        const float* A, const void* B, const void* C, const float* D,
+                        const ssd_scales* scales, void* Y, const void* initial_state,
+                        void* final_state, const ssd_taps* taps, void* stream);
 
 /* Calibration maxima for the static scales ("Training strategy": static
  * scales from calibration data). Over one sequence batch, raises (running

@@ -29,6 +29,8 @@ SSD_E_WORKSPACE = 5
 SSD_E_HIP = 6
 SSD_E_INTERNAL = 7
 SSD_E_VALUE = 8
+SSD_E_TOO_LARGE = 9
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 SSD_DTYPE_F32 = 0
 SSD_DTYPE_F16 = 1
@@ -90,6 +92,8 @@ def _load() -> ctypes.CDLL:
         "ssd_chunk_scan": [SP, ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P],
         "ssd_forward": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P, P, P,
                         ctypes.c_size_t, ctypes.POINTER(SsdTaps), P],
+        "ssd_forward_noalloc": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P, P,
+                                ctypes.POINTER(SsdTaps), P],
         "ssd_decode_step": [SP, ctypes.c_int, P, P, P, P, P, P, ctypes.POINTER(SsdScales), P, P,
                             P],
         "ssd_epilogue": [SP, P, P, ctypes.c_float, P, ctypes.c_float, P, P],
@@ -115,7 +119,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTED = ("ssd_quantize_bc", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-            "ssd_chunk_bmm", "ssd_chunk_scan", "ssd_forward", "ssd_decode_step",
+            "ssd_chunk_bmm", "ssd_chunk_scan", "ssd_forward", "ssd_forward_noalloc", "ssd_decode_step",
             "ssd_epilogue", "ssd_mean_correction",
             "ssd_workspace_bytes",
             "ssd_calibrate_amax", "ssd_calibrate_workspace_bytes", "ssd_scales_from_amax",
@@ -260,6 +264,16 @@ def ssd_forward(shape, path, X, dt, A, B, C, D, scales, Y, final_state=None, wor
                                           _taps(taps),
                                           _stream(stream)))
     return workspace
+
+
+def ssd_forward_noalloc(shape, path, X, dt, A, B, C, D, scales, Y, final_state=None, taps=None,
+                        stream=None, initial_state=None):
+    """Whole forward on the library's fixed device workspace (allocates nothing;
+    calls that may overlap on one device race)."""
+    _check("ssd_forward_noalloc",
+           LIB.ssd_forward_noalloc(ctypes.byref(shape), path, _p(X), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                                   _scales(scales), _p(Y), _p(initial_state), _p(final_state),
+                                   _taps(taps), _stream(stream)))
 
 
 def ssd_decode_step(shape, path, X, dt, A, B, C, D, scales, state, Y, stream=None):

@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libssd.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
 HIP_SOURCES = ["k_modules.hip", "k_fused.hip", "k_fused_i8.hip", "k_chunked_i8.hip", "k_calib.hip",
-               "k_decode.hip", "k_epilogue.hip"]
+               "k_decode.hip", "k_epilogue.hip", "ssd_noalloc.hip"]
 CPP_SOURCES = ["ssd_api.cpp"]
 
 ARCH = "gfx950"

@@ -242,6 +242,7 @@ const char* ssd_status_string(int status) {
     case SSD_E_HIP: return "HIP runtime error";
     case SSD_E_INTERNAL: return "internal error";
     case SSD_E_VALUE: return "a calibration maximum is negative, NaN or infinite";
+    case SSD_E_TOO_LARGE: return "problem needs more workspace than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

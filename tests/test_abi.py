@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for rc in range(9):
+    for rc in range(10):
         assert L.status_string(rc)
     assert L.status_string(99) == "unknown status"
 
@@ -92,6 +92,19 @@ def test_unknown_schedule(sched):
     sh = shape()
     sh.schedule = sched
     assert fwd(sh) == L.SSD_E_SHAPE
+
+
+def test_noalloc_rejects_a_problem_beyond_its_array():
+    # returned before the entry point looks up its device array, so no GPU is
+    # touched; an explicitly chunk-parallel INT8 layer of 4 x 4096 positions,
+    # 128 heads and 8 groups needs about 148 MiB of workspace
+    sh = L.make_shape(4, 4096, 128, 64, 128, 8, 256, "bf16", L.SSD_SCHED_CHUNK)
+    assert L.ssd_workspace_bytes(sh, L.SSD_PATH_INT8) > L.NOALLOC_SCRATCH_BYTES
+    rc = L.LIB.ssd_forward_noalloc(ctypes.byref(sh), L.SSD_PATH_INT8, A16, A16, A16, A16, A16, A16, None,
+                                   A16, None, None, None, None)
+    assert rc == L.SSD_E_TOO_LARGE
+    assert L.LIB.ssd_forward_noalloc(None, 0, A16, A16, A16, A16, A16, A16, None, A16, None, None, None,
+                                     None) == L.SSD_E_NULL
 
 
 def test_schedule_sets_int8_workspace():
