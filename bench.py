@@ -313,16 +313,28 @@ def cpu_baseline(w, consts, ev) -> dict:
             # a head block inside whole groups keeps the head -> group map
             jobs.append((x[b:b + 1, :, h0:h1], dt[b:b + 1, :, h0:h1], consts["A"][h0:h1],
                          B[b:b + 1, :, g0:g1], C[b:b + 1, :, g0:g1], consts["D"][h0:h1], h0, hpg, g0))
-    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
-        list(ex.map(_warm, range(workers)))          # workers started and imported
-        t0 = time.perf_counter()
-        list(ex.map(_recurrence_job, jobs))
-        t1 = time.perf_counter()
+    # one BLAS thread per worker process, so the workers are the threads used
+    threads = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in threads}
+    os.environ.update({k: "1" for k in threads})
+    try:
+        with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+            list(ex.map(_warm, range(workers)))          # workers started and imported
+            t0 = time.perf_counter()
+            list(ex.map(_recurrence_job, jobs))
+            t1 = time.perf_counter()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     tokens_per_s = nb * w.seqlen / (t1 - t0)
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"float64 recurrence on {nb} of {w.batch} sequences (all {w.nheads} heads, "
-                      f"L={w.seqlen}); {t1 - t0:.2f} s wall on {workers} processes",
-            "seconds": t1 - t0, "cpu": cpu_model()}
+                      f"L={w.seqlen}); {t1 - t0:.2f} s wall on {workers} single-threaded processes",
+            "seconds": t1 - t0, "cpu": cpu_model(),
+            "host_cpus_available": ncpu, "host_cpus_total": os.cpu_count()}
 
 
 def _warm(_):

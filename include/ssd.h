@@ -26,9 +26,11 @@
  *
  * Ownership: every buffer is allocated by the caller in device memory (except
  * the shape, scale and tap descriptors, which are host structs holding device
- * pointers) and must be 16-byte aligned (the scale arrays: 4-byte aligned). The library never allocates, frees or
- * keeps a pointer after a call returns; it holds no mutable global state and
- * may be called from several threads on different streams.
+ * pointers) and must be 16-byte aligned (the scale arrays: 4-byte aligned).
+ * The library never allocates, frees or keeps a caller's pointer after a call
+ * returns, and may be called from several threads on different streams. Its
+ * only global state belongs to ssd_forward_noalloc: one fixed device array per
+ * device and a mutex-guarded table of their addresses.
  *
  * Streams: `stream` is a hipStream_t (NULL = the null stream). Calls only
  * enqueue work; results are valid once the stream has been synchronised.

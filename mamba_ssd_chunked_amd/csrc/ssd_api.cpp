@@ -40,7 +40,7 @@ int check_shape(const ssd_shape* s, Dims* d, bool* empty) {
   if (s->dstate != 16 && s->dstate != 32 && s->dstate != 64 && s->dstate != 128)
     return SSD_E_UNSUPPORTED;
   // grid limits: H in x, chunks in y, batch in z
-  const int64_t c = (s->seqlen + s->chunk - 1) / s->chunk;
+  const int64_t c = s->seqlen / s->chunk + (s->seqlen % s->chunk != 0);  // no overflow near INT64_MAX
   if (s->nheads > 65535 || s->batch > 65535 || c > 65535) return SSD_E_SHAPE;
   // every element count must fit an int64 byte offset
   int64_t t;

@@ -27,3 +27,27 @@ def test_rounding_shift_arithmetic_form():
     ref = np.sign(v) * ((np.abs(v) + 64) >> 7)
     fast = (v + 64 + (v >> 63)) >> 7
     assert np.array_equal(fast, ref)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"),
+                    reason="g++ or the ROCm headers not available")
+def test_abi_host_code_under_address_and_ub_sanitizers(tmp_path):
+    """ssd_api.cpp (validation, size arithmetic, workspace carving) built for
+    the host with AddressSanitizer and UBSan, every error fatal, linked to
+    counting stand-ins of the kernel launchers, and driven through every entry
+    point's branches on fake device addresses."""
+    repo = os.path.dirname(HERE)
+    csrc = os.path.join(repo, "mamba_ssd_chunked_amd", "csrc")
+    exe = tmp_path / "abi_san"
+    cmd = ["g++", "-std=c++17", "-g", "-O1", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           f"-I{os.path.join(repo, 'include')}", f"-I{csrc}", os.path.join(csrc, "ssd_api.cpp"),
+           os.path.join(HERE, "native", "abi_stubs.cpp"), os.path.join(HERE, "native", "abi_sanitize.cpp"),
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=300)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
+    assert " 0 failures" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
