@@ -117,3 +117,106 @@ def bits(t):
     """A device or host tensor's stored bits, for bitwise comparison (NaN included)."""
     import torch
     return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()])
+
+
+# ---------------------------------------------------------------------------
+# The rounding budget: a per-element bound on |GPU - oracle| from the roundings
+# the kernels make, for the tight regression check beside the tolerance bars.
+# Each output is a sum of contributions (Scan2 weights times x, Q(C) times the
+# passed state, D x; for the float path also LUT x times B in the state).
+# Evaluating the oracle on |inputs| gives A = sum |contribution| per element
+# (every map is linear in x, B, C, Q(C), CB, the passed states and D, with
+# nonnegative dt, decays and scales). A kernel that rounds each computed MFMA
+# operand once (relative u_op), forms decays from fp32 dAcs (u_exp) and
+# accumulates in fp32 (u_acc) is then within
+#   (u_op + u_exp + u_acc) A + (subnormal steps) + half an ulp of its output.
+# ---------------------------------------------------------------------------
+
+# one rounding of a computed operand into the MFMA type, at most 2^-p of its
+# value for p significant bits (fp16 11, bf16 8): INT8 kernels round the Scan2
+# weight (and cache CB' in fp16 before it); the float kernels round LUT x, the
+# Scan2 weight and the 16-bit state copy once each, and carry bf16 operands as
+# hi + lo pairs (16 significant bits); fp32 inputs use fp32 arithmetic
+U_OP = {("int8", "fp16"): 2.0 ** -10, ("int8", "bf16"): 2.0 ** -8 + 2.0 ** -11,
+        ("int8", "fp32"): 2.0 ** -20, ("float", "fp16"): 2.0 ** -10,
+        ("float", "bf16"): 2.0 ** -15, ("float", "fp32"): 2.0 ** -20}
+
+
+def u_exp(a_max: float) -> float:
+    """Relative error of a decay factor exp(a_s - a_s') (times dt) when a comes
+    from fp32 dAcs (|a| <= a_max), is scaled by log2(e) in fp32, and passes
+    through the hardware exp2 and log2: a few fp32 roundings of the exponent,
+    each at most 2^-24 of its magnitude, times ln 2, plus the instructions'
+    own 1-ulp errors."""
+    return 2.0 ** -24 * (4.0 * a_max * 1.4427 + 250.0) * 0.6931 + 2.0 ** -21
+
+
+def u_acc(l: int) -> float:
+    """fp32 accumulation along one output's chain (l / 16 MFMA accumulations,
+    the rescale, the Scan1 multiply-adds)."""
+    return 2.0 ** -24 * (l / 16 + 16)
+
+
+def budget_ratio(y, ref, absum, u: float, dtype: str, tiny=0.0) -> float:
+    """max over elements of |y - ref| / bound, bound = u * absum + tiny + half
+    an ulp of y in its storage type (<= 1 passes)."""
+    y = np.asarray(y, np.float64)
+    bound = u * np.asarray(absum, np.float64) + tiny + half_ulp(y, dtype) + 1e-300
+    return float(np.max(np.abs(y - np.asarray(ref, np.float64)) / bound))
+
+
+def int8_absum(x, dt, r8, D, scales, chunk, h_init=None):
+    """sum |contribution| of every INT8 output element, from the oracle's
+    ChunkScan on absolute values of its own intermediates."""
+    return O.chunk_scan_int8(np.abs(x), dt, r8["cumsum"]["a"], np.abs(r8["qC"]), np.abs(r8["cb"]),
+                             np.abs(r8["passed"]), np.abs(np.asarray(D, np.float64)), scales, chunk,
+                             None if h_init is None else np.abs(h_init))
+
+
+def int8_budget(y, r8, x, dt, D, scales, chunk, dtype, h_init=None) -> float:
+    """Rounding-budget ratio of an INT8 output y against the oracle's r8["y"]."""
+    a_max = float(np.abs(r8["cumsum"]["a"]).max())
+    ab = int8_absum(x, dt, r8, D, scales, chunk, h_init)
+    # a Scan2 weight below fp16's normal range is off by at most half its
+    # subnormal step, 2^-25, times |x|, for at most `chunk` terms
+    tiny = 2.0 ** -25 * chunk * np.abs(np.asarray(x, np.float64)).max(axis=(0, 1))
+    return budget_ratio(y, r8["y"], ab, U_OP[("int8", dtype)] + u_exp(a_max) + u_acc(chunk), dtype, tiny)
+
+
+def float_budget(y, fin, x, dt, A, B, C, D, chunk, dtype, y_ref, h_ref, h_init=None):
+    """Rounding-budget ratios (Y, final state) of a float-path output against
+    the float64 definition (y_ref, h_ref from oracle.chunked)."""
+    cs = O.chunk_cumsum(np.asarray(dt, np.float64), A, chunk)
+    a_max = float(np.abs(cs["a"]).max())
+    ya, ha = O.chunked(np.abs(x), dt, A, np.abs(B), np.abs(C), np.abs(np.asarray(D, np.float64)), chunk,
+                       *(() if h_init is None else (np.abs(h_init),)))[:2]
+    u = U_OP[("float", dtype)] + u_exp(a_max) + u_acc(chunk)
+    L = np.asarray(x).shape[1]
+    c = -(-L // chunk)
+    tiny_y = 2.0 ** -25 * chunk * np.abs(np.asarray(x, np.float64)).max(axis=(0, 1))
+    ry = budget_ratio(y, y_ref, ya, u, dtype, tiny_y)
+    rh = None
+    if fin is not None:
+        # the state adds one fp32 multiply-add per chunk; a LUT x operand below
+        # fp16's normal range is off by 2^-25 |B| per position
+        tiny_h = 2.0 ** -25 * L * np.abs(np.asarray(B, np.float64)).max() if dtype == "fp16" else 0.0
+        fin = np.asarray(fin, np.float64)
+        bound = (u + c * 2.0 ** -23) * ha + tiny_h + 1e-300
+        rh = float(np.max(np.abs(fin - h_ref) / bound))
+    return ry, rh
+
+
+def state_chan_err(fin, ref) -> float:
+    """max over channels (h, p) of max_{b,n} |fin - ref| / RMS_{b,n}(ref) for
+    states [B, H, P, N] (each channel against its own size)."""
+    fin = np.asarray(fin, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=(0, 3)))
+    err = np.abs(fin - ref).max(axis=(0, 3))
+    return float(np.max(err / np.maximum(rms, 1e-30)))
+
+
+def report(tag: str, **metrics) -> None:
+    """One line of measured errors (shown with pytest -s, and in the tail of
+    a failing test)."""
+    print(tag + ": " + ", ".join(f"{k} {v:.3g}" for k, v in metrics.items() if v is not None), flush=True)

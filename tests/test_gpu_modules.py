@@ -226,7 +226,12 @@ def test_forward_int8(gpu_lib, name, sched):
     assert np.array_equal(taps["s8_local"].cpu().numpy(), r8["s8"])
     assert np.array_equal(taps["passed"].cpu().numpy(), r8["passed"])
     assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
-    assert H.chan_err(H.f64(y), r8["y"], c.w.dtype) <= 5e-2
+    e = c.ev64
+    err = H.chan_err(H.f64(y), r8["y"], c.w.dtype)
+    bud = H.int8_budget(H.f64(y), r8, e["x"], e["dt"], c.consts["D"], c.scales, w.chunk, w.dtype)
+    H.report(f"int8 {name} {sched}", chan_err=err, budget=bud)
+    assert err <= 5e-2
+    assert bud <= 1.0
     # determinism: a second run (without taps) is bitwise identical, final state too
     y2 = torch.empty_like(y)
     fin2 = torch.empty_like(fin)
@@ -271,9 +276,16 @@ def test_forward_float(gpu_lib, name):
     L.ssd_forward(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None, y,
                   final_state=fin)
     torch.cuda.synchronize()
-    assert H.chan_err(H.f64(y), yf, c.w.dtype) <= 2e-2
+    e = c.ev64
     fg = fin.cpu().numpy().astype(np.float64)
-    assert np.abs(fg - hf).max() <= 2e-2 * np.sqrt(np.mean(hf * hf)) * 10
+    err = H.chan_err(H.f64(y), yf, c.w.dtype)
+    serr = H.state_chan_err(fg, hf)
+    by, bh = H.float_budget(H.f64(y), fg, e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"],
+                            w.chunk, w.dtype, yf, hf)
+    H.report(f"float {name}", chan_err=err, state_chan_err=serr, budget_y=by, budget_state=bh)
+    assert err <= 2e-2
+    assert serr <= 1e-2
+    assert by <= 1.0 and bh <= 1.0
 
 
 @pytest.mark.parametrize("name", CASE_NAMES)
@@ -327,7 +339,12 @@ def test_forward_int8_initial_state(gpu_lib, name, sched):
     torch.cuda.synchronize()
     assert np.array_equal(taps["passed"].cpu().numpy(), r["passed"])
     assert np.array_equal(fin.cpu().numpy(), r["passed"][:, -1])
-    assert H.chan_err(H.f64(y), r["y"], w.dtype) <= 5e-2
+    err = H.chan_err(H.f64(y), r["y"], w.dtype)
+    bud = H.int8_budget(H.f64(y), r, e["x"], e["dt"], c.consts["D"], c.scales, w.chunk, w.dtype,
+                        h_init=h0.astype(np.float64))
+    H.report(f"int8 initial state {name} {sched}", chan_err=err, budget=bud)
+    assert err <= 5e-2
+    assert bud <= 1.0
 
 
 @pytest.mark.parametrize("name", CASE_NAMES)
@@ -342,9 +359,15 @@ def test_forward_float_initial_state(gpu_lib, name):
     L.ssd_forward(sh, L.SSD_PATH_FLOAT, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None, y,
                   final_state=fin, initial_state=_dev(h0, np.float32))
     torch.cuda.synchronize()
-    assert H.chan_err(H.f64(y), yr, w.dtype) <= 2e-2
     fg = fin.cpu().numpy().astype(np.float64)
-    assert np.abs(fg - hr).max() <= 2e-1 * np.sqrt(np.mean(hr * hr))
+    err = H.chan_err(H.f64(y), yr, w.dtype)
+    serr = H.state_chan_err(fg, hr)
+    by, bh = H.float_budget(H.f64(y), fg, e["x"], e["dt"], c.consts["A"], e["B"], e["C"], c.consts["D"],
+                            w.chunk, w.dtype, yr, hr, h_init=h0)
+    H.report(f"float initial state {name}", chan_err=err, state_chan_err=serr, budget_y=by, budget_state=bh)
+    assert err <= 2e-2
+    assert serr <= 1e-2
+    assert by <= 1.0 and bh <= 1.0
 
 
 @pytest.mark.parametrize("path", ["int8-head", "int8-chunk", "float"])
