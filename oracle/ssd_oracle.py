@@ -74,6 +74,13 @@ same way on the GPU side):
       coefficient 0.15 ("Training strategy"). The pages correct the Out Proj
       output; without its trained weights it is applied here to the SSD
       output's own channels (H*P), before the RMSNorm.
+  R19 the per-stage accuracy breakdown (forward_stages) switches the
+      method's quantisers on one at a time in the order of "Overall
+      framework"; a quantiser switched off stands for the exact float64 value
+      it approximates (B, C, LUT_state (.) X, the local state, the passed
+      state), so that each stage's error is measured against the float64
+      definition alone. The passed state in INT8 (Eq. 6) needs the local one
+      in INT8 first, so that stage implies the S8 stage.
 
 Where exactness is claimed, float64 matmuls are used on integer-valued
 operands whose partial sums stay below 2^53, so they are exact in any order.
@@ -599,6 +606,142 @@ def forward_recon(x, dt, A, B, C, D, scales: dict, chunk: int) -> dict:
     qpassed[:, c - 1] = saturate(rhaz(passed[:, c - 1] / s_S[None, :, :, None]), qm)
     return {"qB": qB, "qC": qC, "cumsum": cs, "qxs": qxs, "s32": s32, "S": S,
             "passed": passed, "qpassed": qpassed, "y": y.reshape(b, c * l, H, P)[:, :L]}
+
+
+# ---------------------------------------------------------------------------
+# The INT8 method one quantiser at a time (R19): where its error comes from
+# ---------------------------------------------------------------------------
+
+STAGES = ("bc", "xs", "s8", "eq6")
+
+
+def forward_stages(x, dt, A, B, C, D, scales: dict, chunk: int, stages=STAGES) -> dict:
+    """The SSDi8 forward with a chosen set of its quantisers switched on; every
+    quantiser switched off is replaced by the exact float64 value it stands
+    for (R19). The stages, in the order of [SSDi8] "Overall framework":
+      bc   Q(B), Q(C) once per group (Key design 3): every use of B and C
+           (ChunkState, ChunkBMM, ChunkScan1) sees Q(B) s_B and Q(C) s_C;
+      xs   Q(X_scaled) (Key design 1): ChunkState sees Q(Xs) s_X in place of
+           LUT_state (.) X (ChunkScan2 reads X itself in every mode);
+      s8   the local chunk state in INT8 (Key design 2's requantisation): S_k
+           becomes S8 s_S, with S8 = sat(RHAZ(fl32(fl32(S32) M_req))) when
+           bc and xs are on (the method's integer path) and
+           sat(RHAZ(S_k / s_S)) of the float64 state otherwise;
+      eq6  the passed state in INT8 (Eq. 6: Q(Decay), the rounding shift by
+           2^7, saturation); implies s8. ChunkScan1 then reads the int8 passed
+           state in the state scale; without eq6 the passed state is the
+           float64 H_k = exp(a_last) H_{k-1} + S_k.
+    With every stage on, the integers are those of forward_int8 and y equals
+    its y up to float64 rounding order; with none on, y and the final state
+    are those of chunked. Also returns, per stage switched on, the number of
+    values that saturated (|RHAZ(v)| > q_max before clipping) and the number
+    quantised.
+    """
+    st = set(stages)
+    unknown = st - set(STAGES)
+    if unknown:
+        raise ValueError(f"unknown stages {sorted(unknown)}")
+    if "eq6" in st:
+        st.add("s8")
+    bits = int(scales.get("bits", 8))
+    qm = qmax_of(bits)
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    D = np.asarray(D, np.float64)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    g = head_group(H, G)
+    l = chunk
+    c = -(-L // l)
+    sat = {}
+
+    def count(name, v):
+        r = rhaz(v)
+        sat[name] = (int(np.count_nonzero(np.abs(r) > qm)), int(r.size))
+
+    s_B = np.asarray(scales["s_B"], np.float64)
+    s_C = np.asarray(scales["s_C"], np.float64)
+    s_X = np.asarray(scales["s_X"], np.float64).reshape(H, P)
+    s_S = np.asarray(scales["s_S"], np.float64).reshape(H, P)
+    cs = chunk_cumsum(dt, A, chunk, bits)
+    # B and C as every later step sees them
+    if "bc" in st:
+        vB = fl32(fl32(B) * np.asarray(scales["inv_B"], np.float64)[None, None, :, None])
+        vC = fl32(fl32(C) * np.asarray(scales["inv_C"], np.float64)[None, None, :, None])
+        count("Q(B)", vB)
+        count("Q(C)", vC)
+        qB = saturate(rhaz(vB), qm)
+        qC = saturate(rhaz(vC), qm)
+        Bu = qB * s_B[None, None, :, None]
+        Cu = qC * s_C[None, None, :, None]
+    else:
+        Bu, Cu = B, C
+    # ChunkState, S_k [b,c,H,P,N]
+    lut_t = cs["lut"].transpose(0, 2, 3, 1).reshape(b, -1, H)[:, :L]           # [b,L,H]
+    if "xs" in st:
+        v = fl32(fl32(lut_t[..., None] * x) * np.asarray(scales["inv_X"], np.float64).reshape(H, P)[None, None])
+        count("Q(Xs)", v)
+        qxs = saturate(rhaz(v), qm)
+        xs_used = qxs * s_X[None, None]
+    else:
+        # the LUT of Eq. 4 in float64, not its float32 rounding
+        lut64 = (_pad_chunks(dt, c * l).reshape(b, c, l, H).transpose(0, 3, 1, 2)
+                 * np.exp(cs["a"][..., -1:] - cs["a"]))
+        xs_used = lut64.transpose(0, 2, 3, 1).reshape(b, -1, H)[:, :L][..., None] * x
+    xp = _pad_chunks(xs_used, c * l).reshape(b, c, l, H, P)
+    bp = _pad_chunks(Bu, c * l).reshape(b, c, l, G, N)[:, :, :, g]             # [b,c,l,H,N]
+    S = np.matmul(xp.transpose(0, 1, 3, 4, 2), bp.transpose(0, 1, 3, 2, 4))     # [b,c,H,P,N]
+    # the local state in INT8
+    if "s8" in st:
+        if "bc" in st and "xs" in st:
+            s32 = np.rint(S / (s_X[None, None, :, :, None] * s_B[g][None, None, :, None, None]))
+            v = fl32(fl32(s32) * np.asarray(scales["M_req"], np.float64).reshape(H, P)[None, None, :, :, None])
+        else:
+            v = S / s_S[None, None, :, :, None]
+        count("S8", v)
+        s8 = saturate(rhaz(v), qm).astype(np.int64)
+        S = s8 * s_S[None, None, :, :, None]
+    # StatePassing: the passed states H_k [b,c,H,P,N]
+    if "eq6" in st:
+        passed8 = state_passing_int(s8, cs["qdecay"], bits)
+        prev = np.concatenate([np.zeros_like(passed8[:, :1]), passed8[:, :-1]], axis=1)
+        pre = s8 + rounding_shift(cs["qdecay"].transpose(0, 2, 1)[:, :, :, None, None] * prev, bits - 1)
+        sat["Eq. 6"] = (int(np.count_nonzero(np.abs(pre) > qm)), int(pre.size))
+        Hs = passed8 * s_S[None, None, :, :, None]
+    else:
+        Hs = np.empty_like(S)
+        h = np.zeros((b, H, P, N))
+        for k in range(c):
+            h = cs["decay"][:, :, k][:, :, None, None] * h + S[:, k]
+            Hs[:, k] = h
+    # ChunkScan1 + ChunkScan2 + D x on the B and C each step sees
+    a = cs["a"]
+    xq = _pad_chunks(x, c * l).reshape(b, c, l, H, P)
+    dtp = _pad_chunks(dt, c * l).reshape(b, c, l, H)
+    Bq = _pad_chunks(Bu, c * l).reshape(b, c, l, G, N)
+    Cq = _pad_chunks(Cu, c * l).reshape(b, c, l, G, N)
+    tri = np.tril(np.ones((l, l), dtype=bool))
+    y = np.empty((b, c, l, H, P))
+    for k in range(c):
+        ak = a[:, :, k, :]                                                        # [b,H,l]
+        xk = xq[:, k].transpose(0, 2, 1, 3)                                       # [b,H,l,P]
+        Cs = Cq[:, k][:, :, g].transpose(0, 2, 1, 3)                              # [b,H,l,N]
+        Bs = Bq[:, k][:, :, g].transpose(0, 2, 1, 3)
+        y_off = 0.0
+        if k > 0:
+            y_off = np.exp(ak)[..., None] * np.matmul(Cs, Hs[:, k - 1].transpose(0, 1, 3, 2))
+        seg = ak[:, :, :, None] - ak[:, :, None, :]
+        Lmat = np.where(tri, np.exp(np.where(tri, seg, 0.0)), 0.0)
+        M = np.matmul(Cs, Bs.transpose(0, 1, 3, 2)) * Lmat * dtp[:, k].transpose(0, 2, 1)[:, :, None, :]
+        y[:, k] = (y_off + np.matmul(M, xk) + D[None, :, None, None] * xk).transpose(0, 2, 1, 3)
+    out = {"y": y.reshape(b, c * l, H, P)[:, :L], "final": Hs[:, -1], "saturated": sat}
+    if "s8" in st:
+        out["s8"] = s8
+    if "eq6" in st:
+        out["passed"] = passed8
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -610,3 +610,84 @@ def test_epilogue_rmsnorm_properties():
     tiny = 1e-4 * y
     assert np.sqrt(np.mean(O.epilogue(tiny, None, 0.0, one, 1e-5) ** 2)) < 0.1
     assert O.MEAN_CORRECTION_ALPHA == 0.15
+
+
+# PIN: the per-stage breakdown (R19). Its two ends are the method and the
+# definition; each single stage converges to the definition as the bit width
+# grows, so a stage that used the wrong scale or axis would stay O(1) off.
+def _stage_inputs(wid=0, seqlen=None, nheads=None, cal_on_inputs=False, bits=8):
+    w = synth.WORKLOADS[wid]
+    if seqlen is not None:
+        w = w.replace(seqlen=seqlen, nheads=nheads)
+    c = synth.layer_constants(w)
+    ev = synth.as_f64(synth.evaluation_batch(w, c, batch=1), w.dtype)
+    cal = [ev] if cal_on_inputs else [synth.as_f64(s, w.dtype) for s in synth.calibration_sequences(w, c)]
+    am = O.calibrate(cal, c["A"], w.ngroups, w.chunk)
+    sc = O.scale_pack(am["B"], am["C"], am["Xs"], am["S"], w.nheads, bits=bits)
+    return w, c, ev, sc
+
+
+def _stages(w, c, ev, sc, stages):
+    return O.forward_stages(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"], sc, w.chunk, stages)
+
+
+@pytest.mark.parametrize("wid,seqlen,nheads", [(0, None, None), (1, 600, 4)])
+def test_stages_all_on_is_the_int8_method(wid, seqlen, nheads):
+    w, c, ev, sc = _stage_inputs(wid, seqlen, nheads)
+    r8 = O.forward_int8(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"], sc, w.chunk)
+    r = _stages(w, c, ev, sc, O.STAGES)
+    assert np.array_equal(r["s8"], r8["s8"])
+    assert np.array_equal(r["passed"], r8["passed"])
+    assert O.rel_max_err(r["y"], r8["y"]) < 1e-12
+    assert set(r["saturated"]) == {"Q(B)", "Q(C)", "Q(Xs)", "S8", "Eq. 6"}
+
+
+@pytest.mark.parametrize("wid,seqlen,nheads", [(0, None, None), (1, 600, 4)])
+def test_stages_all_off_is_the_definition(wid, seqlen, nheads):
+    w, c, ev, sc = _stage_inputs(wid, seqlen, nheads)
+    r = _stages(w, c, ev, sc, ())
+    y, h = O.recurrence(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"])
+    assert O.rel_max_err(r["y"], y) < 1e-10
+    assert np.abs(r["final"] - h).max() <= 1e-10 * np.abs(h).max()
+    assert r["saturated"] == {}
+
+
+@pytest.mark.parametrize("stage", O.STAGES)
+def test_each_stage_converges_to_the_definition(stage):
+    """One quantiser on, scales calibrated on the inputs themselves: the error
+    falls by at least 4x per 4 bits and is below 1e-3 of the output's range at
+    20 bits. Nothing saturates, except that Eq. 6's rounded decay (a decay just
+    under 1 rounds to Q(Decay) = 2^(bits-1)) may carry an integer state one
+    step past the calibrated maximum now and then."""
+    errs = {}
+    for bits in (8, 12, 16, 20):
+        w, c, ev, sc = _stage_inputs(1, 600, 4, cal_on_inputs=True, bits=bits)
+        y, _ = O.recurrence(ev["x"], ev["dt"], c["A"], ev["B"], ev["C"], c["D"])
+        r = _stages(w, c, ev, sc, (stage,))
+        errs[bits] = O.rel_max_err(r["y"], y)
+        for name, (n, total) in r["saturated"].items():
+            assert n <= (1e-4 * total if name == "Eq. 6" else 0), (stage, bits, r["saturated"])
+    assert errs[20] <= 1e-3, errs
+    assert errs[8] > 4 * errs[12] > 16 * errs[16], errs
+
+
+def test_stage_eq6_implies_s8_and_unknown_stages_raise():
+    w, c, ev, sc = _stage_inputs()
+    a = _stages(w, c, ev, sc, ("eq6",))
+    b = _stages(w, c, ev, sc, ("s8", "eq6"))
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["passed"], b["passed"])
+    with pytest.raises(ValueError):
+        _stages(w, c, ev, sc, ("bc", "scan2"))
+
+
+def test_stage_saturation_counts_by_hand():
+    """One B value at three times its group's calibrated maximum saturates Q(B)
+    once; nothing else does."""
+    w, c, ev, sc = _stage_inputs(cal_on_inputs=True)
+    ev = dict(ev)
+    B = ev["B"].copy()
+    B[0, 5, 0, 3] = 3.0 * np.abs(B[..., 0, :]).max()
+    ev["B"] = B
+    r = _stages(w, c, ev, sc, ("bc",))
+    assert r["saturated"]["Q(B)"] == (1, B.size)
+    assert r["saturated"]["Q(C)"] == (0, ev["C"].size)
