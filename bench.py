@@ -356,6 +356,174 @@ def _recurrence_job(job):
     return float(y[0, -1, 0, 0])
 
 
+def schedule_of(w, cus: int) -> str:
+    """The INT8 schedule the library's automatic choice takes for a layer."""
+    return "chunk" if w.batch * w.nheads < 2 * cus else "head"
+
+
+def time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, steps, warmup, copy_gbs,
+                 traffic=None, spread=True) -> dict:
+    """Tokens/s and HBM roofline fraction of ssd_forward on resident inputs:
+    `warmup` untimed calls, then `steps` back-to-back calls bracketed by one
+    pair of events on the stream the kernels run on (events between the calls
+    would add their own packets); optionally the spread of single calls from a
+    second, untimed pass."""
+    ws = torch.empty(max(1, L.ssd_workspace_bytes(sh, path)), dtype=torch.uint8, device="cuda")
+    sc = scales if path == L.SSD_PATH_INT8 else None
+
+    def step():
+        L.ssd_forward(sh, path, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, sc, y, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tokens = w.batch * w.seqlen
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    avg_call_s = e0.elapsed_time(e1) * 1e-3 / steps
+    call_ms = {"timed_mean": avg_call_s * 1e3}
+    if spread:
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            ev_s[i].record()
+            step()
+            ev_e[i].record()
+        torch.cuda.synchronize()
+        per_call_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])
+        call_ms.update({"mean": float(per_call_ms.mean()), "median": float(np.median(per_call_ms)),
+                        "p10": float(np.percentile(per_call_ms, 10)),
+                        "p90": float(np.percentile(per_call_ms, 90))})
+    del ws
+    bpt = algorithmic_bytes_per_token(w, path == L.SSD_PATH_INT8)
+    bytes_per_call = bpt * tokens
+    achieved = bytes_per_call / avg_call_s / 1e9
+    return {
+        "value": tokens / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step,
+        "call_ms": call_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "ssd_forward (all kernels of one call)",
+                     "algorithmic_bytes_per_call": bytes_per_call,
+                     "algorithmic_bytes_per_token": bpt,
+                     "io_only_frac": io_bytes_per_token(w) * tokens / avg_call_s / 1e9 / HBM_PEAK_GBS,
+                     "frac_of_copy": achieved / copy_gbs},
+    }
+
+
+CONFIG_IDS = (1, 2, 3, 4)   # every single-GPU layer of the workload table
+
+
+def bench_configs(torch, np, L, synth, steps, warmup, copy_gbs, head=None) -> dict:
+    """Both paths on each workload of the table, on its own seeded inputs and
+    static scales (calibrated on the GPU from its two calibration sequences);
+    the headline layer's figures are reused when given."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for wid in CONFIG_IDS:
+        w = synth.WORKLOADS[wid]
+        rec = {"workload": wid, "int8_schedule": schedule_of(w, cus)}
+        if head is not None and head[0] == wid:
+            res = head[1]
+        else:
+            consts = synth.layer_constants(w)
+            ev = synth.evaluation_batch(w, consts)
+            dev = {k: torch.from_numpy(v).cuda() for k, v in ev.items()}
+            del ev
+            A = torch.from_numpy(consts["A"]).cuda()
+            D = torch.from_numpy(consts["D"]).cuda()
+            sh = L.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+            cal = [{k: torch.from_numpy(v).cuda() for k, v in s.items()}
+                   for s in synth.calibration_sequences(w, consts)]
+            scales = L.calibrate(lambda s: L.make_shape(1, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                                        w.ngroups, w.chunk, w.dtype), cal, A)
+            del cal
+            y = torch.empty_like(dev["x"])
+            res = {}
+            for name, path in (("int8", L.SSD_PATH_INT8), ("float", L.SSD_PATH_FLOAT)):
+                res[name] = time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, steps, warmup,
+                                         copy_gbs, spread=False)
+            del dev, y
+            torch.cuda.empty_cache()
+        for name, r in res.items():
+            rec[name] = {"tokens_per_s": r["value"], "call_ms": r["call_ms"]["timed_mean"],
+                         "roofline_frac": r["roofline"]["frac"],
+                         "achieved_gbs": r["roofline"]["achieved"]}
+        if "int8" in rec and "float" in rec:
+            rec["int8_speedup"] = rec["float"]["call_ms"] / rec["int8"]["call_ms"]
+        out[w.name] = rec
+        print(f"# config {wid}: " + ", ".join(f"{k} {rec[k]['call_ms']:.4f} ms ({rec[k]['roofline_frac']:.3f})"
+                                              for k in ("int8", "float") if k in rec),
+              file=sys.stderr, flush=True)
+    return out
+
+
+TREND_BATCHES = (1, 8, 32)
+TREND_SEQLENS = (256, 2048, 8192)
+
+
+def device_sequence(torch, w, consts, batch, seqlen, seed):
+    """One sequence drawn on the GPU with the input recipe of the workload
+    table (X = N(0, 1) x the per-(h, p) scale, dt = softplus(0.5 N(0, 1) +
+    dt_bias), B, C ~ N(0, 1)), cast once to the storage dtype. For shapes too
+    large to draw on the host in reasonable time."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dt_t = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}[w.dtype]
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    xs = torch.from_numpy(consts["xscale"]).cuda()
+    bias = torch.from_numpy(consts["dt_bias"]).cuda()
+    x = (torch.randn((batch, seqlen, H, P), generator=g, device="cuda") * xs).to(dt_t)
+    dt = torch.nn.functional.softplus(
+        0.5 * torch.randn((batch, seqlen, H), generator=g, device="cuda", dtype=torch.float64) + bias).to(dt_t)
+    Bm = torch.randn((batch, seqlen, G, N), generator=g, device="cuda").to(dt_t)
+    Cm = torch.randn((batch, seqlen, G, N), generator=g, device="cuda").to(dt_t)
+    return {"x": x, "dt": dt, "B": Bm, "C": Cm}
+
+
+def bench_trend(torch, np, L, synth, steps, warmup, copy_gbs) -> dict:
+    """The INT8-over-float speed-up of ssd_forward on the 2.7B layer's head
+    shape (H 80, P 64, N 128, G 1, chunk 256, fp16) over batch x length."""
+    base = synth.WORKLOADS[2]
+    consts = synth.layer_constants(base)
+    A = torch.from_numpy(consts["A"]).cuda()
+    D = torch.from_numpy(consts["D"]).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cal = [device_sequence(torch, base, consts, 1, 2048, 7001 + r) for r in range(2)]
+    scales = L.calibrate(lambda s: L.make_shape(1, 2048, base.nheads, base.headdim, base.dstate,
+                                                base.ngroups, base.chunk, base.dtype), cal, A)
+    del cal
+    points = []
+    for b in TREND_BATCHES:
+        for seqlen in TREND_SEQLENS:
+            w = base.replace(batch=b, seqlen=seqlen)
+            dev = device_sequence(torch, w, consts, b, seqlen, 7100 + 10 * b + seqlen)
+            sh = L.make_shape(b, seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+            y = torch.empty_like(dev["x"])
+            r8 = time_forward(torch, np, L, w, sh, L.SSD_PATH_INT8, dev, A, D, scales, y, steps, warmup,
+                              copy_gbs, spread=False)
+            rf = time_forward(torch, np, L, w, sh, L.SSD_PATH_FLOAT, dev, A, D, None, y, steps, warmup,
+                              copy_gbs, spread=False)
+            del dev, y
+            t8, tf = r8["call_ms"]["timed_mean"], rf["call_ms"]["timed_mean"]
+            points.append({"batch": b, "seqlen": seqlen, "int8_schedule": schedule_of(w, cus),
+                           "int8_ms": t8, "float_ms": tf, "int8_speedup": tf / t8,
+                           "int8_frac": r8["roofline"]["frac"], "float_frac": rf["roofline"]["frac"]})
+            print(f"# trend B={b} L={seqlen}: int8 {t8:.4f} ms, float {tf:.4f} ms, x{tf / t8:.2f}",
+                  file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    return {"shape": "H80 P64 N128 G1 chunk256 fp16 (2.7B layer heads), inputs drawn on the GPU",
+            "points": points}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +536,8 @@ def main() -> int:
     ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step (prints its JSON object)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload figures")
+    ap.add_argument("--no-trend", action="store_true", help="skip the batch x length speed-up ladder")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID,
                     help="workload id of the headline line (default: the 2.7B-shaped layer)")
     args = ap.parse_args()
@@ -401,61 +571,12 @@ def main() -> int:
         print(json.dumps({"decode": dec, "kernel_source_hash": kernel_source_hash()}), flush=True)
         return 0
     y = torch.empty_like(dev["x"])
-    tokens = w.batch * w.seqlen
     copy_gbs = copy_bandwidth(torch)
     results = {}
     for path_name in args.paths.split(","):
         path = L.SSD_PATH_INT8 if path_name == "int8" else L.SSD_PATH_FLOAT
-        ws = torch.empty(max(1, L.ssd_workspace_bytes(sh, path)), dtype=torch.uint8, device="cuda")
-        sc = scales if path == L.SSD_PATH_INT8 else None
-
-        def step():
-            L.ssd_forward(sh, path, dev["x"], dev["dt"], A, dev["B"], dev["C"], D, sc, y,
-                          workspace=ws)
-
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        # timed region: K back-to-back calls, one pair of events on the stream the
-        # kernels run on (events between the calls would add their own packets)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for _ in range(args.steps):
-            step()
-        e1.record()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step = (t1 - t0) * 1e3 / args.steps
-        avg_call_s = e0.elapsed_time(e1) * 1e-3 / args.steps
-        # spread of single calls, from a second, untimed pass
-        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        for i in range(args.steps):
-            ev_s[i].record()
-            step()
-            ev_e[i].record()
-        torch.cuda.synchronize()
-        per_call_ms = np.array([s.elapsed_time(e) for s, e in zip(ev_s, ev_e)])
-        bpt = algorithmic_bytes_per_token(w, path == L.SSD_PATH_INT8)
-        bytes_per_call = bpt * tokens
-        achieved = bytes_per_call / avg_call_s / 1e9
-        traffic = measured_traffic(w.name, path_name)
-        results[path_name] = {
-            "value": tokens / (ms_per_step * 1e-3),
-            "ms_per_step": ms_per_step,
-            "call_ms": {"timed_mean": avg_call_s * 1e3,
-                        "mean": float(per_call_ms.mean()), "median": float(np.median(per_call_ms)),
-                        "p10": float(np.percentile(per_call_ms, 10)),
-                        "p90": float(np.percentile(per_call_ms, 90))},
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "ssd_forward (all kernels of one call)",
-                         "algorithmic_bytes_per_call": bytes_per_call,
-                         "algorithmic_bytes_per_token": bpt,
-                         "io_only_frac": io_bytes_per_token(w) * tokens / avg_call_s / 1e9 / HBM_PEAK_GBS,
-                         "frac_of_copy": achieved / copy_gbs},
-        }
+        results[path_name] = time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, args.steps,
+                                          args.warmup, copy_gbs, traffic=measured_traffic(w.name, path_name))
     head_path = "int8" if "int8" in results else next(iter(results))
     head = results[head_path]
     out = {
@@ -491,6 +612,11 @@ def main() -> int:
     if not args.no_ablation:
         out["ablation"] = bench_ablation(torch, np, L, synth, w, consts, dev, A, D, scales, cal_dev,
                                          args.steps, args.warmup)
+    if not args.no_configs:
+        out["configs"] = bench_configs(torch, np, L, synth, min(args.steps, 20), min(args.warmup, 3), copy_gbs,
+                                       head=(args.workload, results) if len(results) == 2 else None)
+    if not args.no_trend:
+        out["trend"] = bench_trend(torch, np, L, synth, min(args.steps, 10), min(args.warmup, 2), copy_gbs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, consts, ev)
     print(json.dumps(out), flush=True)
