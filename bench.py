@@ -450,13 +450,14 @@ def bench_configs(torch, np, L, synth, steps, warmup, copy_gbs, head=None) -> di
             res = {}
             for name, path in (("int8", L.SSD_PATH_INT8), ("float", L.SSD_PATH_FLOAT)):
                 res[name] = time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, steps, warmup,
-                                         copy_gbs, spread=False)
+                                         copy_gbs, traffic=measured_traffic(w.name, name), spread=False)
             del dev, y
             torch.cuda.empty_cache()
         for name, r in res.items():
             rec[name] = {"tokens_per_s": r["value"], "call_ms": r["call_ms"]["timed_mean"],
                          "roofline_frac": r["roofline"]["frac"],
-                         "achieved_gbs": r["roofline"]["achieved"]}
+                         "achieved_gbs": r["roofline"]["achieved"],
+                         "traffic": r["roofline"]["traffic"]}
         if "int8" in rec and "float" in rec:
             rec["int8_speedup"] = rec["float"]["call_ms"] / rec["int8"]["call_ms"]
         out[w.name] = rec

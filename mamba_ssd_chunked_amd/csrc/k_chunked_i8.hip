@@ -359,8 +359,8 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
       const uint32_t yo = (uint32_t)((l16 * H * kHP + 4 * lg) * (int)sizeof(T));
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-        __builtin_nontemporal_store(u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])},
-                                    (u2v_t*)(yt + (yo + 16 * pt * (uint32_t)sizeof(T))));
+        *(u2v_t*)(yt + (yo + 16 * pt * (uint32_t)sizeof(T))) =
+            u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])};
     }
     __builtin_amdgcn_wave_barrier();
   };

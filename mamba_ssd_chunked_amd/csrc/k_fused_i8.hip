@@ -232,12 +232,13 @@ struct SRegs {
   float lut[NU];
   float va;
   uint32_t vd;
+  uint32_t qd;  // the dword holding the chunk's Q(Decay) byte
 };
 
 template <int DT, int LC, int NS, int PW, bool TAPS>
 __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u16* s_x, int8_t* s_qx,
                                             int8_t* s_h8, float* s_va, float* s_vb, float* s_vw,
-                                            float* s_ss) {
+                                            float* s_ss, int* s_qd) {
   typedef typename Store<DT>::T T;
   typedef FragF<DT> F;
   constexpr int RT = LC / 16;              // row tiles of the chunk
@@ -284,22 +285,27 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   const int64_t rowB = (int64_t)H * kHP * sizeof(T);
   const char* xh = (const char*)a.X + (b * d.L * H + h) * (int64_t)kHP * sizeof(T);
   const uint32_t x_lane = (uint32_t)(16 * c8);
-  const auto stage_load = [&](int kc, SRegs<LC>& r) {
+  // (real == false: the same loads from the chunk's first row, L2-resident
+  // and never used, so that every chunk issues the same vector-memory
+  // operations and the compiler's in-order wait counts stay exact)
+  const auto stage_load = [&](int kc, SRegs<LC>& r, bool real) {
     const int64_t t0 = (int64_t)kc * LC;
     const int64_t cs0 = (bh_ * d.c + kc) * (int64_t)LC;
-    const int64_t lim = d.L - 1 - t0;  // last valid row of the chunk
+    const int64_t lim = real ? d.L - 1 - t0 : 0;  // last valid row of the chunk
+    const int srow = real ? sr0 : 0, svr = real ? sv : 0;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int64_t s = min((int64_t)(sr0 + 8 * u), lim);
+      const int64_t s = min((int64_t)(srow + (real ? 8 * u : 0)), lim);
       r.x[u] = __builtin_nontemporal_load((const v4i*)(xh + (t0 + s) * rowB + x_lane));
-      r.lut[u] = a.lut[cs0 + sr0 + 8 * u];
+      r.lut[u] = a.lut[cs0 + s];
     }
-    r.va = a.dAcs[cs0 + sv];
-    const int64_t tv = t0 + min((int64_t)sv, lim);
+    r.va = a.dAcs[cs0 + svr];
+    const int64_t tv = t0 + min((int64_t)svr, lim);
     if constexpr (sizeof(T) == 4)
       r.vd = *(const uint32_t*)((const T*)a.dt + (b * d.L + tv) * H + h);
     else
       r.vd = *(const u16*)((const T*)a.dt + (b * d.L + tv) * H + h);
+    r.qd = *(const uint32_t*)(a.qdecay + ((bh_ * d.c + kc) & ~(int64_t)3));
   };
   const float4 ix0 = ld_scale4(&a.sc.inv_X[h * kHP + 8 * c8]);
   const float4 ix1 = ld_scale4(&a.sc.inv_X[h * kHP + 8 * c8 + 4]);
@@ -341,6 +347,9 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
       s_va[o * LC + sv] = A2;
       s_vb[o * LC + kperm(sv)] = B2;
     }
+    // Q(Decay) of the chunk, for its StatePassing (through LDS, so no value
+    // loaded in one chunk is carried in a register into the next)
+    if (w == 0 && lane == 0) s_qd[o] = (int)((r.qd >> (8 * ((bh_ * d.c + kc) & 3))) & 0xff);
   };
 
   // per-lane LDS offsets of the transposing reads (see xsw_off / qsw_off)
@@ -378,10 +387,6 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
 #pragma unroll
     for (int kn = 0; kn < KN; ++kn) q[kn] = *(const v4i*)(src + (qc_lane + 64 * kn));
   };
-  const auto load_qd = [&](int kc) {
-    const int64_t qi = bh_ * d.c + kc;
-    return *(const uint32_t*)(a.qdecay + (qi & ~(int64_t)3));
-  };
   // A row tile's operands from memory: its CB' fragments (off-diagonal pairs
   // and the diagonal one) and Q(C) rows, issued one phase ahead of their use and
   // always before this wave's Y stores of the phase in between (the vector
@@ -402,9 +407,11 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   const auto load_tile_ops = [&](int kc, int i, auto& t) {
     constexpr int MF = sizeof(t.off) / sizeof(t.off[0]);
     const char* src = cbf_h + kc * cbf_kstride + cb_frag_base(i) * 1024;
+    // every wave issues MF + 1 fragment loads (a fixed count, so the
+    // compiler's in-order wait counts stay exact); pairs past the diagonal
+    // reload the diagonal fragment, which is in the cache
 #pragma unroll
-    for (int m = 0; m < MF; ++m)
-      if (m < i / 2) t.off[m] = frag(src + m * 1024);
+    for (int m = 0; m < MF; ++m) t.off[m] = frag(src + min(m, i / 2) * 1024);
     t.diag = frag(src + (i / 2) * 1024);
     load_qc(kc, i, t.qc);
   };
@@ -412,12 +419,11 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   // prologue: stage chunk 0 (every wave its share)
   {
     SRegs<LC> r;
-    stage_load(0, r);
+    stage_load(0, r, true);
     stage_store(0, r);
   }
   v4i qbt[KS];
   load_qbt(0, qbt);
-  uint32_t qd_cur = load_qd(0);
 
   for (int k = 0; k < d.c; ++k) {
     const int o = k & 1;
@@ -427,18 +433,18 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     const float* vB = s_vb + o * LC;
     const int8_t* h8r = s_h8 + (o ^ 1) * HN;  // H_{k-1}
     int8_t* h8w = s_h8 + o * HN;              // H_k
-    const int kn1 = min(k + 1, d.c - 1);      // next chunk (the last chunk reloads itself)
+    const int kn1 = min(k + 1, d.c - 1);      // next chunk (clamped; the last chunk prefetches nothing)
     const int64_t t0 = (int64_t)k * LC;
     __syncthreads();  // B1: chunk k staged; H_{k-1} published; chunk k - 1's buffers free
-    // this chunk's tile operands (landing during ChunkState) and the next
-    // chunk's share of x (landing by the time it is staged)
+    // the first row tile's operands (landing during ChunkState) and the next
+    // chunk's share of x (landing by the time it is staged); the second row
+    // tile's operands are issued after the first tile, so that the burst at
+    // the barrier stays short
     TileOps1 op1;
     TileOps2 op2;
     load_tile_ops(k, w, op1);
-    if (NRR == 2) load_tile_ops(k, RT - 1 - w, op2);
     SRegs<LC> sreg;
-    stage_load(kn1, sreg);
-    const uint32_t qd_next = load_qd(kn1);
+    stage_load(kn1, sreg, k + 1 < d.c);
 
     v2s S8a[PTW], S8b[PTW];
     // ---- ChunkState^T for (n tile nt_own, p tiles pt0 ..), requantised to S8 ----
@@ -576,8 +582,10 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
 #pragma unroll
         for (int jp = 0; jp < PW; ++jp) {
           const int pt = pt_base + jp;
-          __builtin_nontemporal_store(u2v_t{pack2<DT>(acc[jp][0], acc[jp][1]), pack2<DT>(acc[jp][2], acc[jp][3])},
-                                      (u2v_t*)(ytile + (yo + 16 * pt * (uint32_t)sizeof(T))));
+          // plain stores: the four 32-byte pieces of a row merge into whole
+          // lines in L2 (streaming stores reach HBM as partial writes)
+          *(u2v_t*)(ytile + (yo + 16 * pt * (uint32_t)sizeof(T))) =
+              u2v_t{pack2<DT>(acc[jp][0], acc[jp][1]), pack2<DT>(acc[jp][2], acc[jp][3])};
         }
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
@@ -587,9 +595,10 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     // the next chunk's Q(B)^T fragments are issued after the last tile's
     // off-diagonal pairs, ahead of its Y stores; the next chunk's share is
     // staged into the other buffer (its readers, chunk k - 1, are past B1)
-    const auto next_qbt = [&] { load_qbt(kn1, qbt); };
+    const auto next_qbt = [&] { load_qbt(kn1, qbt); };  // the last chunk reloads its own (L2-resident)
     if constexpr (NRR == 2) {
       scan_tile(w, op1, [] {});
+      load_tile_ops(k, RT - 1 - w, op2);
       if (k + 1 < d.c) stage_store(k + 1, sreg);
       scan_tile(RT - 1 - w, op2, next_qbt);
     } else {
@@ -598,7 +607,7 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     }
 
     // ---- StatePassing (Eq. 6) in registers; publish H_k for the next ChunkScan1 ----
-    const int qd = (int)((qd_cur >> (8 * ((bh_ * d.c + k) & 3))) & 0xff);
+    const int qd = s_qd[o];
     const v2s qd2 = {(short)qd, (short)qd};
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
@@ -615,7 +624,6 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
       if (TAPS && a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = pack_pairs(S8a[j], S8b[j]);
       if (TAPS && a.tap_passed) *(uint32_t*)(a.tap_passed + so) = H8[j];
     }
-    qd_cur = qd_next;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (a.final_state) {
@@ -637,11 +645,12 @@ __global__ __launch_bounds__(kCompT, 1) void k_fused_i8v2(I8Args a) {
   __shared__ __attribute__((aligned(16))) float s_vb[2 * LC];
   __shared__ __attribute__((aligned(16))) float s_vw[kCompW * LC];
   __shared__ __attribute__((aligned(16))) float s_ss[3 * kHP];
+  __shared__ int s_qd[2];
   const int64_t bid = blockIdx.x;
   if (bid < a.nfull)
-    fused_i8_v2<DT, LC, NS, 4, TAPS>(a, bid, s_x, s_qx, s_h8, s_va, s_vb, s_vw, s_ss);
+    fused_i8_v2<DT, LC, NS, 4, TAPS>(a, bid, s_x, s_qx, s_h8, s_va, s_vb, s_vw, s_ss, s_qd);
   else
-    fused_i8_v2<DT, LC, NS, 2, TAPS>(a, bid - a.nfull, s_x, s_qx, s_h8, s_va, s_vb, s_vw, s_ss);
+    fused_i8_v2<DT, LC, NS, 2, TAPS>(a, bid - a.nfull, s_x, s_qx, s_h8, s_va, s_vb, s_vw, s_ss, s_qd);
 }
 
 template <int DT, int LC, int NS>
