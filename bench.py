@@ -539,6 +539,8 @@ def main() -> int:
                     help="time only the decode step (prints its JSON object)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload figures")
     ap.add_argument("--no-trend", action="store_true", help="skip the batch x length speed-up ladder")
+    ap.add_argument("--schedule", choices=("auto", "head", "chunk"), default="auto",
+                    help="INT8 schedule of the headline layer (default: the library's automatic choice)")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID,
                     help="workload id of the headline line (default: the 2.7B-shaped layer)")
     args = ap.parse_args()
@@ -559,7 +561,8 @@ def main() -> int:
     dev = {k: torch.from_numpy(v).cuda() for k, v in ev.items()}
     A = torch.from_numpy(consts["A"]).cuda()
     D = torch.from_numpy(consts["D"]).cuda()
-    sh = L.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype)
+    sched = {"auto": L.SSD_SCHED_AUTO, "head": L.SSD_SCHED_HEAD, "chunk": L.SSD_SCHED_CHUNK}[args.schedule]
+    sh = L.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, w.dtype, sched)
 
     # static scales from the two calibration sequences, on the GPU
     cal = synth.calibration_sequences(w, consts)
@@ -595,7 +598,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
-                   "chunk": w.chunk, "input_dtype": w.dtype, "path": head_path},
+                   "chunk": w.chunk, "input_dtype": w.dtype, "path": head_path,
+                   "int8_schedule": (schedule_of(w, torch.cuda.get_device_properties(0).multi_processor_count)
+                                     if args.schedule == "auto" else args.schedule)},
         "roofline": head["roofline"],
         "paths": results,
         "kernel_source_hash": kernel_source_hash(),

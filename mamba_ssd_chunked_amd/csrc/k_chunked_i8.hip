@@ -40,21 +40,36 @@ struct ChunkArgs {
   int8_t* tap_qxs;
   int32_t* tap_s32;
   int8_t* tap_s8;
+  int xcd_map;  // (B * c * G) % 8 == 0: the units of one XCD (see chunk_block)
 };
 
-// block -> (b, k, h): consecutive blocks are the heads of one (batch, chunk),
-// so the B/C operand fragments they share are read from L2
+// block -> (b, k, h). The heads of one unit (batch, chunk, group) share its
+// Q(B)^T, Q(C) and CB' operands. With xcd_map, block i runs on XCD i % 8 and
+// serves unit (i % 8) + 8 ((i / 8) / hpg), head (i / 8) % hpg of its group: every
+// unit's heads run on one XCD, whose L2 then fetches the unit's operands once.
+// Otherwise consecutive blocks are the heads of one unit (all groups of a
+// (batch, chunk) in turn).
 struct BKH {
   int64_t b;
   int k, h;
 };
-__device__ __forceinline__ BKH chunk_block(const Dims& d) {
+__device__ __forceinline__ BKH chunk_block(const Dims& d, int xcd_map) {
   BKH r;
   const int64_t bi = blockIdx.x;
-  r.h = (int)(bi % d.H);
-  const int64_t bk = bi / d.H;
-  r.k = (int)(bk % d.c);
-  r.b = bk / d.c;
+  if (xcd_map) {
+    const int64_t j = bi / 8;
+    const int64_t u = bi % 8 + 8 * (j / d.hpg);  // unit = (b c + k) G + g
+    const int g = (int)(u % d.G);
+    const int64_t bk = u / d.G;
+    r.h = g * d.hpg + (int)(j % d.hpg);
+    r.k = (int)(bk % d.c);
+    r.b = bk / d.c;
+  } else {
+    r.h = (int)(bi % d.H);
+    const int64_t bk = bi / d.H;
+    r.k = (int)(bk % d.c);
+    r.b = bk / d.c;
+  }
   return r;
 }
 
@@ -71,7 +86,7 @@ __global__ __launch_bounds__(kCT) void k_cstate_i8(ChunkArgs a) {
   constexpr int NU = LC * 8 / kCT;    // 16-byte x items per thread
   __shared__ __attribute__((aligned(16))) int8_t s_qx[LC * kHP];
   const Dims& d = a.d;
-  const BKH u = chunk_block(d);
+  const BKH u = chunk_block(d, a.xcd_map);
   const int64_t b = u.b;
   const int k = u.k, h = u.h, H = d.H;
   const int g = h / d.hpg;
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) float s_vb[LC];
   __shared__ __attribute__((aligned(16))) float s_vw[4 * LC];
   const Dims& d = a.d;
-  const BKH u = chunk_block(d);
+  const BKH u = chunk_block(d, a.xcd_map);
   const int64_t b = u.b;
   const int k = u.k, h = u.h, H = d.H;
   const int g = h / d.hpg;
@@ -392,7 +407,7 @@ hipError_t launch_chunked_i8(const Dims& d, int dtype, const void* X, const void
                              void* final_state, int8_t* states, int8_t* tap_qxs, int32_t* tap_s32, int8_t* tap_s8,
                              int8_t* tap_passed, hipStream_t st) {
   const ChunkArgs ca{d, X, dt, qC, qbt, cbf, dAcs, lut, D, sc, states, (const int8_t*)init, Y, tap_qxs, tap_s32,
-                     tap_s8};
+                     tap_s8, (int)((d.B * d.c * d.G) % 8 == 0)};
   const int64_t nb = d.B * (int64_t)d.c * d.H;
   if (nb == 0) return hipSuccess;
   if (nb >= ((int64_t)1 << 31)) return hipErrorInvalidValue;

@@ -1,24 +1,28 @@
 // Fused SSD forward on the persistent-INT8 path ("SSDi8" notes page, "Overall
-// framework" and "Key designs 1-3"), in three launches:
+// framework" and "Key designs 1-3"), in two launches:
 //
-//  1. ChunkCumsum: dAcs, LUT_state and Q(Decay) per (batch, head, chunk).
-//  2. Per (batch, chunk, group), k_cbq: Q(B) and Q(C) once per group ("Key
-//     design 3"), and ChunkBMM CB = Q(C) Q(B)^T on int8 MFMA (exact int32,
-//     "Key design 2": ChunkBMM reuses the int8 B and C). CB depends only on
-//     (batch, chunk, group), so it is formed once and shared by every head of
-//     the group. The block writes the operands of the main kernel in the
-//     register layouts its MFMAs read, so they go from memory (L2) straight
-//     into registers:
-//       - Q(C) rows, row-major as the inputs (ChunkScan1's operand);
-//       - Q(B)^T fragments (ChunkState's operand);
-//       - CB' = fp16(CB s_C s_B 2^E) fragments: ChunkScan2's weights before the
-//         head's decay, with the dequantisation folded in and E a power of two
-//         that keeps |CB'| < 2^15 whatever the scales (|CB| <= N 127^2).
-//  3. The main kernel: one workgroup per (batch, head), or per p half of a
-//     head in a last partial round, walking the head's chunks in order with
-//     the int8 state in registers (it never reaches HBM). Per chunk:
-//       Q(Xs)        X_scaled = LUT_state * x quantised once per (s, p) (producer
-//                    waves, into LDS, plain [s][p] layout);
+//  1. k_prep_cb, two kinds of blocks side by side in one launch:
+//     - ChunkCumsum blocks: dAcs, LUT_state and Q(Decay) per (batch, head,
+//       chunk);
+//     - one block per (batch, chunk, group, pair of 16-row tiles): Q(B) and
+//       Q(C) once per group ("Key design 3"), and ChunkBMM CB = Q(C) Q(B)^T
+//       on int8 MFMA (exact int32, "Key design 2": ChunkBMM reuses the int8 B
+//       and C). CB depends only on (batch, chunk, group), so it is formed once
+//       and shared by every head of the group. The blocks write the operands
+//       of the main kernel in the register layouts its MFMAs read, so they go
+//       from memory (L2) straight into registers:
+//         - Q(C) rows, row-major as the inputs (ChunkScan1's operand);
+//         - Q(B)^T fragments (ChunkState's operand);
+//         - CB' = fp16(CB s_C s_B 2^E) fragments: ChunkScan2's weights before
+//           the head's decay, with the dequantisation folded in and E a power
+//           of two that keeps |CB'| < 2^15 whatever the scales
+//           (|CB| <= N 127^2).
+//  2. The main kernel: one 8-wave workgroup per (batch, head), or per p half
+//     of a head in a last partial round, walking the head's chunks in order
+//     with the int8 state in registers (it never reaches HBM). Per chunk:
+//       Q(Xs)        X_scaled = LUT_state * x quantised once per (s, p) while
+//                    the next chunk is staged (each wave stages an eighth of
+//                    it into LDS);
 //       ChunkState   S32^T[n,p] = sum_s Q(B)^T[n,s] Q(Xs)[s,p] (int8 MFMA; the
 //                    Q(Xs) operand by transposing LDS reads), requantised in
 //                    registers to S8;
@@ -32,6 +36,10 @@
 // and V_i[s'] = exp(a_{16i} - a_s') <= 1, so the weights of those tiles are
 // CB' V_i (one mixed-precision multiply each) and u_s scales their sum once.
 // The diagonal pair of column tiles uses exp(a_s - a_s') directly.
+//
+// Layers whose B * H heads cannot fill the GPU with one workgroup per head take
+// the chunk-parallel schedule of k_chunked_i8.hip after launch 1 instead
+// (ssd_shape.schedule chooses; the results are the same bit for bit).
 #include "ssd_cumsum.hpp"
 #include "ssd_device.hpp"
 #include "ssd_fused.hpp"

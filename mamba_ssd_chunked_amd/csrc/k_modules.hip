@@ -250,8 +250,17 @@ __global__ __launch_bounds__(256) void k_chunk_state(Dims d, const void* __restr
 
 // ---------------------------------------------------------------------------
 // StatePassing (Eq. 6), element-parallel over (b, h, p, n), sequential over
-// chunks. Loads for up to 8 chunks are issued before the dependent updates.
+// chunks.
 // ---------------------------------------------------------------------------
+
+// INT8: Eq. 6 over the chunks of every (b, h, p, n) element, four elements
+// (one dword) per thread, updated as int16 pairs. The chain is sequential per
+// element; the loads of the next G chunks are issued before the current G are
+// updated, so 2 G chunk loads per thread are in flight. Every thread issues the
+// same loads and stores in every group (chunks past the end re-read and
+// re-store the last chunk's slot with its final value, unchanged), so the
+// compiler's in-order wait counts are exact and never wait for the prefetch.
+template <int G>
 __global__ __launch_bounds__(256) void k_state_passing_i8(Dims d, int8_t* __restrict__ states,
                                                           const uint8_t* __restrict__ qdecay,
                                                           const int8_t* __restrict__ init,
@@ -266,30 +275,48 @@ __global__ __launch_bounds__(256) void k_state_passing_i8(Dims d, int8_t* __rest
   const int64_t base = b * d.c * slot + r;
   // without an initial state H_0 = S_0; with one, Eq. 6 applies from chunk 0
   uint32_t prev = init ? ((const uint32_t*)init)[b * per_b + r] : st[base];
-  const uint8_t* qd = qdecay + (b * d.H + h) * d.c;
-  for (int k0 = init ? 0 : 1; k0 < d.c; k0 += 8) {
-    uint32_t v[8];
-    int q[8];
+  const int64_t q0 = (b * d.H + h) * d.c;                       // this head's first Q(Decay) byte
+  const int64_t qlast = ((d.B * d.H * d.c - 1) & ~(int64_t)3);  // last whole dword of the array
+  const int k_begin = init ? 0 : 1;
+  const int ngroups = (d.c - k_begin + G - 1) / G;
+  // the group's states, and its G Q(Decay) bytes from G / 4 + 1 aligned dwords
+  // (addresses clamped into the array; a clamped dword only ever feeds chunks
+  // past the end)
+  const auto load = [&](int g, uint32_t (&v)[G], int (&q)[G]) {
+    const int kg = k_begin + g * G;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (k0 + j < d.c) {
-        v[j] = st[base + (int64_t)(k0 + j) * slot];
-        q[j] = qd[k0 + j];
-      }
+    for (int j = 0; j < G; ++j) v[j] = st[base + (int64_t)min(kg + j, d.c - 1) * slot];
+    const int64_t a = q0 + kg;
+    const int sh = (int)(a & 3);
+    uint32_t w[G / 4 + 1];
+#pragma unroll
+    for (int i = 0; i <= G / 4; ++i) w[i] = *(const uint32_t*)(qdecay + min((a & ~(int64_t)3) + 4 * i, qlast));
+#pragma unroll
+    for (int i = 0; i < G / 4; ++i) {
+      const uint32_t u = __builtin_amdgcn_alignbyte(w[i + 1], w[i], (uint32_t)sh);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) q[4 * i + z] = (int)((u >> (8 * z)) & 0xffu);
     }
+  };
+  const auto step = [&](int g, const uint32_t (&v)[G], const int (&q)[G]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (k0 + j < d.c) {
-        int o[4];
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          const int hv = byte_s(v[j], z) + rsh7(q[j] * byte_s(prev, z));
-          o[z] = hv > 127 ? 127 : (hv < -127 ? -127 : hv);
-        }
-        prev = pack4(o[0], o[1], o[2], o[3]);
-        st[base + (int64_t)(k0 + j) * slot] = prev;
-      }
+    for (int j = 0; j < G; ++j) {
+      const int kr = k_begin + g * G + j;
+      const v2s qd2 = {(short)q[j], (short)q[j]};
+      const v2s h01 = sat127_pair(unpack_pair(v[j], 0x010c000cu) + rsh7_pair(qd2, unpack_pair(prev, 0x010c000cu)));
+      const v2s h23 = sat127_pair(unpack_pair(v[j], 0x030c020cu) + rsh7_pair(qd2, unpack_pair(prev, 0x030c020cu)));
+      if (kr < d.c) prev = pack_pairs(h01, h23);
+      st[base + (int64_t)min(kr, d.c - 1) * slot] = prev;
     }
+  };
+  uint32_t va[G], vb[G];
+  int qa[G], qb[G];
+  load(0, va, qa);
+  for (int g = 0; g < ngroups; g += 2) {
+    load(g + 1, vb, qb);
+    step(g, va, qa);
+    load(g + 2, va, qa);
+    step(g + 1, vb, qb);
   }
   if (final_state) ((uint32_t*)final_state)[b * per_b + r] = prev;
 }
@@ -656,8 +683,13 @@ hipError_t launch_state_passing(const Dims& d, bool int8, void* states, const fl
   const int64_t n = d.B * (int64_t)d.H * d.P * d.N / 4;
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (int8) {
-    hipLaunchKernelGGL(k_state_passing_i8, dim3(grid), dim3(256), 0, st, d, (int8_t*)states,
-                       qdecay, (const int8_t*)init, (int8_t*)final_state);
+    // short sequences take short groups (less redundant tail)
+    if (d.c > 32)
+      hipLaunchKernelGGL(k_state_passing_i8<16>, dim3(grid), dim3(256), 0, st, d, (int8_t*)states, qdecay,
+                         (const int8_t*)init, (int8_t*)final_state);
+    else
+      hipLaunchKernelGGL(k_state_passing_i8<4>, dim3(grid), dim3(256), 0, st, d, (int8_t*)states, qdecay,
+                         (const int8_t*)init, (int8_t*)final_state);
   } else {
     hipLaunchKernelGGL(k_state_passing_f, dim3(grid), dim3(256), 0, st, d, (float*)states, dAcs,
                        (const float*)init, (float*)final_state);

@@ -113,6 +113,34 @@ def test_state_passing_int8(gpu_lib, name):
     assert np.array_equal(fin.cpu().numpy(), r8["passed"][:, -1])
 
 
+@pytest.mark.parametrize("nchunks,with_init", [(1, False), (1, True), (7, False), (33, True), (45, False),
+                                               (80, True)])
+def test_state_passing_int8_chain_lengths(gpu_lib, nchunks, with_init):
+    """Eq. 6 over chains of 1 to 80 chunks (both group sizes of the kernel and
+    their ragged last groups), with Q(Decay) rows starting at every byte
+    offset, saturating states and decays of 0 and 128 included: bit-exact
+    against the oracle's chain, the final state too."""
+    import torch
+    L = gpu_lib
+    rng = np.random.default_rng(1000 + nchunks)
+    B, H, P, N, l = 2, 3, 16, 32, 64
+    s8 = rng.integers(-127, 128, size=(B, nchunks, H, P, N)).astype(np.int64)
+    qd = rng.integers(0, 129, size=(B, H, nchunks)).astype(np.int64)
+    qd[0, 0, ::5] = 128
+    qd[1, 2, ::7] = 0
+    h0 = rng.integers(-127, 128, size=(B, H, P, N)).astype(np.int64) if with_init else None
+    ref = O.state_passing_int(s8, qd, 8, h0)
+    sh = L.make_shape(B, nchunks * l, H, P, N, 1, l, "fp16")
+    st = _i8(torch, s8)
+    fin = torch.empty((B, H, P, N), dtype=torch.int8, device="cuda")
+    L.ssd_state_passing(sh, L.SSD_PATH_INT8, st, None, _dev(qd, np.uint8), fin,
+                        initial_state=None if h0 is None else _i8(torch, h0))
+    torch.cuda.synchronize()
+    assert np.array_equal(st.cpu().numpy(), ref)
+    assert np.array_equal(fin.cpu().numpy(), ref[:, -1])
+    assert (np.abs(ref) == 127).any()  # the chain saturates somewhere
+
+
 @pytest.mark.parametrize("name", CASE_NAMES)
 def test_chunk_bmm_int8(gpu_lib, name):
     L = gpu_lib
