@@ -97,7 +97,11 @@ __global__ __launch_bounds__(kCT) void k_cstate_i8(ChunkArgs a) {
   const int64_t t0 = (int64_t)k * LC;
   const int64_t bh = b * H + h;
 
-  // this wave's Q(B)^T fragments, issued first (they land during the staging)
+  // the requantisation factors of this lane's p values, then this wave's
+  // Q(B)^T fragments, issued first (they land during the staging)
+  float mreq[4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) mreq[pt] = a.sc.M_req[h * kHP + 16 * pt + l16];
   v4i qa[NTW][KS];
   {
     const char* src = (const char*)a.qbt + (((b * d.c + k) * d.G + g) * (int64_t)(NT * KS)) * 1024 + 16 * lane;
@@ -168,14 +172,13 @@ __global__ __launch_bounds__(kCT) void k_cstate_i8(ChunkArgs a) {
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) {
     const int p = 16 * pt + l16;
-    const float mreq = a.sc.M_req[h * kHP + p];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int nt = NTW * w + j;
       const int64_t so = (((b * d.c + k) * H + h) * (int64_t)kHP + p) * NS + 16 * nt + 4 * lg;
       if (TAPS && a.tap_s32) *(int4*)(a.tap_s32 + so) = make_int4(acc[j][pt][0], acc[j][pt][1], acc[j][pt][2], acc[j][pt][3]);
-      const uint32_t s8 = q8x4((float)acc[j][pt][0] * mreq, (float)acc[j][pt][1] * mreq, (float)acc[j][pt][2] * mreq,
-                               (float)acc[j][pt][3] * mreq);
+      const uint32_t s8 = q8x4((float)acc[j][pt][0] * mreq[pt], (float)acc[j][pt][1] * mreq[pt],
+                               (float)acc[j][pt][2] * mreq[pt], (float)acc[j][pt][3] * mreq[pt]);
       *(uint32_t*)(a.states + so) = s8;
       if (TAPS && a.tap_s8) *(uint32_t*)(a.tap_s8 + so) = s8;
     }
@@ -217,6 +220,10 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
   const float Eg = (float)cb_exp(scb, NS);
   const float sC = a.sc.s_C[g];
   const float Dh = a.D[h];
+  // the state steps of this lane's p values (16 pt + 4 lg + r), loaded first
+  float4 ssr[4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) ssr[pt] = ld_scale4(&a.sc.s_S[h * kHP + 16 * pt + 4 * lg]);
   // the passed state H_{k-1}: chunk k - 1's slot, the initial state, or none
   const int8_t* hprev = k > 0 ? a.states + ((b * d.c + k - 1) * H + h) * (int64_t)kHP * NS
                               : (a.init ? a.init + bh * (int64_t)kHP * NS : nullptr);
@@ -279,6 +286,8 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
   };
   const auto load_ops = [&](int i, TileOps& t) {
     const char* src = cbk + cb_frag_base(i) * 1024;
+    // (with three workgroups per CU, skipping the pairs past the diagonal is
+    // faster than a fixed load count: measured)
 #pragma unroll
     for (int m = 0; m < RT / 2; ++m)
       if (m < i / 2) t.off[m] = *(const v4i*)(src + m * 1024 + lane16);
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
       }
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const float4 ss = ld_scale4(&a.sc.s_S[h * kHP + 16 * pt + 4 * lg]);
+        const float4 ss = ssr[pt];
         acc[pt][0] = fmaf((float)acc1[pt][0], eo * ss.x, acc[pt][0]);
         acc[pt][1] = fmaf((float)acc1[pt][1], eo * ss.y, acc[pt][1]);
         acc[pt][2] = fmaf((float)acc1[pt][2], eo * ss.z, acc[pt][2]);

@@ -55,24 +55,140 @@ constexpr int kCompT = kCompW * kWave;        // 512
 // ===========================================================================
 // Preparation launch (1024 threads per block). Blocks [0, ncs) run
 // ChunkCumsum for (chunk, batch, block of kCsHeads heads). The other blocks
-// each serve one unit (batch, chunk, group) and one pair j of row tiles
-// {2j, 2j + 1} (32 positions): they quantise Q(C) of those rows and Q(B) of
-// rows 0 .. 32 j + 31 into LDS, write the Q(C) rows, the CB' fragments of the
-// two row tiles and, for odd j, the Q(B)^T fragments of K step (j - 1) / 2.
+// write Q(C) rows, the Q(B)^T fragments of ChunkState and the CB' fragments of
+// ChunkScan2, in one of two layouts:
+//  - per unit (batch, chunk, group), when there are enough units to fill the
+//    GPU: the chunk's Q(B) and Q(C) rows are quantised once into LDS and the
+//    16 waves share the fragments;
+//  - per unit and pair j of row tiles {2j, 2j + 1}, for few units (more,
+//    smaller blocks): Q(C) of those 32 rows and Q(B) of rows 0 .. 32 j + 31 go
+//    into LDS; the block writes the Q(C) rows, the CB' fragments of the two row
+//    tiles and, for odd j, the Q(B)^T fragments of K step (j - 1) / 2.
 // ===========================================================================
 constexpr int kPrepT = 1024;
 template <int LC, int NS>
 struct CbLds {
   int8_t qB[LC * NS];
+  int8_t qC[LC * NS];
+};
+
+template <int DT, int LC, int NS>
+__device__ __forceinline__ void cb_block_unit(const Dims& d, const void* __restrict__ B, const void* __restrict__ C,
+                                         const float* __restrict__ inv_B, const float* __restrict__ inv_C,
+                                         const float* __restrict__ s_B, const float* __restrict__ s_C,
+                                         int8_t* __restrict__ qC, int8_t* __restrict__ qbt, u16* __restrict__ cbf,
+                                         int64_t unit, CbLds<LC, NS>& sm) {
+  typedef typename Store<DT>::T T;
+  constexpr int KN = NS / 64, NT = NS / 16, KS = LC / 64, NF = cb_frags(LC), RT = LC / 16;
+  constexpr int C8 = NS / 8;                  // 8-element items per row
+  constexpr int NIT = 2 * LC * C8 / kPrepT;   // items per thread (B rows, then C rows)
+  static_assert(NIT * kPrepT == 2 * LC * C8, "whole items per thread");
+  constexpr int NW = kPrepT / kWave;          // waves
+  const int64_t g_ = unit % d.G;
+  const int64_t bk = unit / d.G;
+  const int k = (int)(bk % d.c);
+  const int64_t b = bk / d.c;
+  const int g = (int)g_;
+  const int tid = threadIdx.x;
+  const int64_t Lp = (int64_t)d.c * LC;
+  const float ib = inv_B[g], ic = inv_C[g];
+
+  // 1. quantise every row once: items [0, LC C8) are Q(B), the next LC C8 Q(C)
+  //    (rows past L are zero; every load of a thread is issued before any is
+  //    used)
+  uint4 raw[NIT];
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int item = tid + kPrepT * u;
+    const bool isB = item < LC * C8;
+    const int it2 = isB ? item : item - LC * C8;
+    const int s = it2 / C8, n0 = (it2 % C8) * 8;
+    const int64_t t = min((int64_t)k * LC + s, d.L - 1);
+    raw[u] = *(const uint4*)((const T*)(isB ? B : C) + ((b * d.L + t) * d.G + g) * (int64_t)NS + n0);
+  }
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int item = tid + kPrepT * u;
+    const bool isB = item < LC * C8;
+    const int it2 = isB ? item : item - LC * C8;
+    const int s = it2 / C8, n0 = (it2 % C8) * 8;
+    const int64_t t = (int64_t)k * LC + s;
+    const bool ok = t < d.L;
+    const float inv = isB ? ib : ic;
+    const uint32_t wv[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu)));
+      const float v1 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16)));
+      q[2 * e] = ok ? q_sat(v0 * inv, 127.f) : 0;
+      q[2 * e + 1] = ok ? q_sat(v1 * inv, 127.f) : 0;
+    }
+    const uint2 pq = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+    if (isB) {
+      *(uint2*)&sm.qB[bsw<NS>(s, n0)] = pq;
+    } else {
+      *(uint2*)&sm.qC[bsw<NS>(s, n0)] = pq;
+      *(uint2*)(qC + ((b * Lp + t) * d.G + g) * (int64_t)NS + n0) = pq;
+    }
+  }
+  __syncthreads();
+  const int w = wave_id();
+  const int lane = tid & (kWave - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // 2. Q(B)^T fragments (nt, ks): lane (lg, l16) holds Q(B)[64 ks + 16 lg + e][16 nt + l16], e = 0..15
+  for (int f = w; f < NT * KS; f += NW) {
+    const int nt = f / KS, ks = f % KS;
+    const int s0 = 64 * ks + 16 * lg, cB = 16 * nt + 8 * (l16 & 1);
+    const v2i_t lo = ldtr8(sm.qB + bsw<NS>(s0 + (l16 >> 1), cB));
+    const v2i_t hi = ldtr8(sm.qB + bsw<NS>(s0 + 8 + (l16 >> 1), cB));
+    *(v4i*)(qbt + (unit * (NT * KS) + f) * 1024 + 16 * lane) = v4i{lo.x, lo.y, hi.x, hi.y};
+  }
+
+  // 3. CB' fragments (i, m), m = 0 .. i / 2, numbered cb_frag_base(i) + m:
+  //    lane (lg, l16) holds CB'[s][s'] for s = 16 i + l16 and s' = 32 m + 16 h +
+  //    4 lg + r (K slot e = 4 h + r); the two CB^T tiles (2m, 2m + 1) come out
+  //    of the MFMA in exactly that layout
+  const float scb = s_C[g] * s_B[g];
+  const float cg = ldexpf(scb, cb_exp(scb, NS));
+  for (int f = w; f < NF; f += NW) {
+    int i = 0;
+#pragma unroll
+    for (int ii = 1; ii < RT; ++ii) i += (cb_frag_base(ii) <= f) ? 1 : 0;
+    const int m = f - cb_frag_base(i);
+    v4i cbA = v4i{0, 0, 0, 0}, cbB = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int kn = 0; kn < KN; ++kn) {
+      const v4i qcr = *(const v4i*)&sm.qC[bsw<NS>(16 * i + l16, 64 * kn + 16 * lg)];
+      const v4i ba = *(const v4i*)&sm.qB[bsw<NS>(32 * m + l16, 64 * kn + 16 * lg)];
+      const v4i bb = *(const v4i*)&sm.qB[bsw<NS>(32 * m + 16 + l16, 64 * kn + 16 * lg)];
+      cbA = mma_i8(ba, qcr, cbA);
+      cbB = mma_i8(bb, qcr, cbB);
+    }
+    typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+    h8_t hv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hv[r] = (_Float16)((float)cbA[r] * cg);
+      hv[4 + r] = (_Float16)((float)cbB[r] * cg);
+    }
+    *(h8_t*)(cbf + (unit * NF + f) * 512 + 8 * lane) = hv;
+  }
+}
+
+template <int LC, int NS>
+struct CbPairLds {
+  int8_t qB[LC * NS];
   int8_t qC[32 * NS];
 };
 
 template <int DT, int LC, int NS>
-__device__ __forceinline__ void cb_block(const Dims& d, const void* __restrict__ B, const void* __restrict__ C,
+__device__ __forceinline__ void cb_block_pairs(const Dims& d, const void* __restrict__ B, const void* __restrict__ C,
                                          const float* __restrict__ inv_B, const float* __restrict__ inv_C,
                                          const float* __restrict__ s_B, const float* __restrict__ s_C,
                                          int8_t* __restrict__ qC, int8_t* __restrict__ qbt, u16* __restrict__ cbf,
-                                         int64_t unit, int j, CbLds<LC, NS>& sm) {
+                                         int64_t unit, int j, CbPairLds<LC, NS>& sm) {
   typedef typename Store<DT>::T T;
   constexpr int KN = NS / 64, NT = NS / 16, KS = LC / 64, NF = cb_frags(LC);
   constexpr int C8 = NS / 8;  // 8-element items per row
@@ -176,7 +292,9 @@ __device__ __forceinline__ void cb_block(const Dims& d, const void* __restrict__
 
 template <int LC, int NS>
 struct PrepLds {
-  static constexpr size_t kBytes = sizeof(CsLds) > sizeof(CbLds<LC, NS>) ? sizeof(CsLds) : sizeof(CbLds<LC, NS>);
+  static constexpr size_t kCb = sizeof(CbLds<LC, NS>) > sizeof(CbPairLds<LC, NS>) ? sizeof(CbLds<LC, NS>)
+                                                                                     : sizeof(CbPairLds<LC, NS>);
+  static constexpr size_t kBytes = sizeof(CsLds) > kCb ? sizeof(CsLds) : kCb;
 };
 
 template <int DT, int LC, int NS>
@@ -186,7 +304,8 @@ __global__ __launch_bounds__(kPrepT) void k_prep_cb(Dims d, const void* __restri
                                                     const void* __restrict__ C, const float* __restrict__ inv_B,
                                                     const float* __restrict__ inv_C, const float* __restrict__ s_B,
                                                     const float* __restrict__ s_C, int8_t* __restrict__ qC,
-                                                    int8_t* __restrict__ qbt, u16* __restrict__ cbf, int ncs) {
+                                                    int8_t* __restrict__ qbt, u16* __restrict__ cbf, int ncs,
+                                                    int per_unit) {
   static_assert(kPrepT == kCsThreads, "one block size for both kinds");
   __shared__ __attribute__((aligned(16))) char lds[PrepLds<LC, NS>::kBytes];
   const int64_t bi = blockIdx.x;
@@ -197,8 +316,11 @@ __global__ __launch_bounds__(kPrepT) void k_prep_cb(Dims d, const void* __restri
   } else {
     const int64_t ci = bi - ncs;
     constexpr int NJ = LC / 32;
-    cb_block<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci / NJ, (int)(ci % NJ),
-                         *(CbLds<LC, NS>*)lds);
+    if (per_unit)
+      cb_block_unit<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci, *(CbLds<LC, NS>*)lds);
+    else
+      cb_block_pairs<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci / NJ, (int)(ci % NJ),
+                                 *(CbPairLds<LC, NS>*)lds);
   }
 }
 
@@ -684,10 +806,13 @@ hipError_t launch_i8v2(const Dims& d, const void* X, const void* dt, const float
 
   // ChunkCumsum blocks and the B/C + ChunkBMM blocks side by side in one launch
   const int64_t ncs = (int64_t)d.c * d.B * ((d.H + kCsHeads - 1) / kCsHeads);
-  const int64_t ncb = (int64_t)bkg * (LC / 32);
+  // one block per unit when there are enough units (measured: 64 units of the
+  // 2.7B layer favour it, 8 units of the 1.3B layer favour pairs of row tiles)
+  const int per_unit = bkg >= 32;
+  const int64_t ncb = per_unit ? (int64_t)bkg : (int64_t)bkg * (LC / 32);
   if (ncs + ncb >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_prep_cb<DT, LC, NS>), dim3((unsigned)(ncs + ncb)), dim3(kPrepT), 0, st, d, dt, A, dAcs, lut,
-                     qd, B, C, sc.inv_B, sc.inv_C, sc.s_B, sc.s_C, qC, qbt, cbf, (int)ncs);
+                     qd, B, C, sc.inv_B, sc.inv_C, sc.s_B, sc.s_C, qC, qbt, cbf, (int)ncs, per_unit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
