@@ -290,6 +290,10 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
                                        (__attribute__((address_space(3))) void*)((char*)s_B + 1024 * gi), 16, 0, 0);
     }
   };
+  // the wave index, hidden from the compiler at every chunk of the main loop so
+  // that what derives from it is formed per chunk rather than hoisted and
+  // spilled
+  int wk = w;
   // C rows (B operand over N) of this wave's row tiles {w, 15 - w}
   // C rows of row tile {w, 15 - w}[rr] of chunk kc
   const auto load_C = [&](int kc, int lane, int rr, uint4 (&cf)[KNF]) {
@@ -297,7 +301,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     const int lim = min(LC - 1, (int)d.L - 1 - t0);
     const int l16 = lane & 15, lg = lane >> 4;
     const T* c0 = Cb + (int64_t)t0 * rowB;
-    const int i = min((rr == 0) ? w : 2 * kWaves - 1 - w, RT - 1);
+    const int i = min((rr == 0) ? wk : 2 * kWaves - 1 - wk, RT - 1);
     const T* src = c0 + (__umul24(min(16 * i + l16, lim), rowB) + 8 * lg);
 #pragma unroll
     for (int kn = 0; kn < KNF; ++kn) cf[kn] = *(const uint4*)(src + 32 * kn);
@@ -345,6 +349,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     const int64_t t0 = (int64_t)k * LC;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // B rows and C rows have landed
     __syncthreads();  // chunk k staged; s_H holds H_{k-1}
+    asm volatile("" : "+s"(wk));
     const float alast2 = vA2[LC - 1];  // a_{k,l-1} log2(e): StatePassing decay
 
 #pragma unroll
@@ -417,7 +422,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     // ---- ChunkScan, transposed: Y^T[p, s] for row tiles {w, 15 - w} ----
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      const int i = (rr == 0) ? w : 2 * kWaves - 1 - w;
+      const int i = (rr == 0) ? wk : 2 * kWaves - 1 - wk;
       if (i >= RT) continue;
       const int s_row = 16 * i + l16;
       F cr[KNF];

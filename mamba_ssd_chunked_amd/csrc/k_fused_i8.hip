@@ -4,7 +4,7 @@
 //  1. k_prep_cb, two kinds of blocks side by side in one launch:
 //     - ChunkCumsum blocks: dAcs, LUT_state and Q(Decay) per (batch, head,
 //       chunk);
-//     - one block per (batch, chunk, group, pair of 16-row tiles): Q(B) and
+//     - blocks per (batch, chunk, group), whole or in parts: Q(B) and
 //       Q(C) once per group ("Key design 3"), and ChunkBMM CB = Q(C) Q(B)^T
 //       on int8 MFMA (exact int32, "Key design 2": ChunkBMM reuses the int8 B
 //       and C). CB depends only on (batch, chunk, group), so it is formed once
@@ -60,12 +60,16 @@ constexpr int kCompT = kCompW * kWave;        // 512
 //  - per unit (batch, chunk, group), when there are enough units to fill the
 //    GPU: the chunk's Q(B) and Q(C) rows are quantised once into LDS and the
 //    16 waves share the fragments;
+//  - per unit half (two blocks per unit, for fewer units): each half takes the
+//    row tiles of about half the CB' fragments and quantises the Q(B) rows
+//    they reach and its own Q(C) rows;
 //  - per unit and pair j of row tiles {2j, 2j + 1}, for few units (more,
 //    smaller blocks): Q(C) of those 32 rows and Q(B) of rows 0 .. 32 j + 31 go
 //    into LDS; the block writes the Q(C) rows, the CB' fragments of the two row
 //    tiles and, for odd j, the Q(B)^T fragments of K step (j - 1) / 2.
 // ===========================================================================
 constexpr int kPrepT = 1024;
+enum { kCbPairs = 0, kCbUnit = 1, kCbHalves = 2 };  // block kinds of the B/C + ChunkBMM part
 template <int LC, int NS>
 struct CbLds {
   int8_t qB[LC * NS];
@@ -153,6 +157,133 @@ __device__ __forceinline__ void cb_block_unit(const Dims& d, const void* __restr
   const float scb = s_C[g] * s_B[g];
   const float cg = ldexpf(scb, cb_exp(scb, NS));
   for (int f = w; f < NF; f += NW) {
+    int i = 0;
+#pragma unroll
+    for (int ii = 1; ii < RT; ++ii) i += (cb_frag_base(ii) <= f) ? 1 : 0;
+    const int m = f - cb_frag_base(i);
+    v4i cbA = v4i{0, 0, 0, 0}, cbB = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int kn = 0; kn < KN; ++kn) {
+      const v4i qcr = *(const v4i*)&sm.qC[bsw<NS>(16 * i + l16, 64 * kn + 16 * lg)];
+      const v4i ba = *(const v4i*)&sm.qB[bsw<NS>(32 * m + l16, 64 * kn + 16 * lg)];
+      const v4i bb = *(const v4i*)&sm.qB[bsw<NS>(32 * m + 16 + l16, 64 * kn + 16 * lg)];
+      cbA = mma_i8(ba, qcr, cbA);
+      cbB = mma_i8(bb, qcr, cbB);
+    }
+    typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+    h8_t hv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hv[r] = (_Float16)((float)cbA[r] * cg);
+      hv[4 + r] = (_Float16)((float)cbB[r] * cg);
+    }
+    *(h8_t*)(cbf + (unit * NF + f) * 512 + 8 * lane) = hv;
+  }
+}
+
+// The first row tile of the second half of a unit: the halves hold as near an
+// equal number of CB' fragments as whole row tiles allow.
+template <int LC>
+__host__ __device__ constexpr int cb_split_tile() {
+  int i = 0;
+  while (2 * cb_frag_base(i) < cb_frags(LC)) ++i;
+  return i;
+}
+
+// Half sl of a unit: row tiles [i0, i1) (i0 = 0 or the split tile). The block
+// quantises the Q(B) rows its CB' fragments reach (0 .. 32 (i1 - 1) / 2 + 31)
+// and the Q(C) rows of its tiles, writes those Q(C) rows and CB' fragments, and
+// the Q(B)^T fragments of K steps [ks0, ks1): the first half those its Q(B)
+// rows cover whole, the second half the rest.
+template <int DT, int LC, int NS>
+__device__ __forceinline__ void cb_block_half(const Dims& d, const void* __restrict__ B, const void* __restrict__ C,
+                                              const float* __restrict__ inv_B, const float* __restrict__ inv_C,
+                                              const float* __restrict__ s_B, const float* __restrict__ s_C,
+                                              int8_t* __restrict__ qC, int8_t* __restrict__ qbt,
+                                              u16* __restrict__ cbf, int64_t unit, int sl, CbLds<LC, NS>& sm) {
+  typedef typename Store<DT>::T T;
+  constexpr int KN = NS / 64, NT = NS / 16, KS = LC / 64, NF = cb_frags(LC), RT = LC / 16;
+  constexpr int C8 = NS / 8;
+  constexpr int NW = kPrepT / kWave;
+  constexpr int IS = cb_split_tile<LC>();
+  constexpr int nB0 = 32 * ((IS - 1) / 2 + 1);  // Q(B) rows of the first half
+  constexpr int kMaxIt = (2 * LC * C8 + kPrepT - 1) / kPrepT;
+  static_assert(IS > 0 && IS < RT, "two nonempty halves");
+  const int64_t g_ = unit % d.G;
+  const int64_t bk = unit / d.G;
+  const int k = (int)(bk % d.c);
+  const int64_t b = bk / d.c;
+  const int g = (int)g_;
+  const int tid = threadIdx.x;
+  const int64_t Lp = (int64_t)d.c * LC;
+  const float ib = inv_B[g], ic = inv_C[g];
+  const int i0 = sl ? IS : 0, i1 = sl ? RT : IS;
+  const int nB = sl ? LC : nB0;
+  const int nit = (nB + 16 * (i1 - i0)) * C8;
+
+  // 1. quantise: items [0, nB C8) are Q(B) rows 0 .. nB - 1, the rest the Q(C)
+  //    rows of tiles i0 .. i1 - 1 (rows past L are zero; every load of a thread
+  //    is issued before any is used)
+  uint4 raw[kMaxIt];
+#pragma unroll
+  for (int u = 0; u < kMaxIt; ++u) {
+    const int item = tid + kPrepT * u;
+    if (item < nit) {
+      const bool isB = item < nB * C8;
+      const int it2 = isB ? item : item - nB * C8;
+      const int s = (isB ? 0 : 16 * i0) + it2 / C8, n0 = (it2 % C8) * 8;
+      const int64_t t = min((int64_t)k * LC + s, d.L - 1);
+      raw[u] = *(const uint4*)((const T*)(isB ? B : C) + ((b * d.L + t) * d.G + g) * (int64_t)NS + n0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kMaxIt; ++u) {
+    const int item = tid + kPrepT * u;
+    if (item < nit) {
+      const bool isB = item < nB * C8;
+      const int it2 = isB ? item : item - nB * C8;
+      const int s = (isB ? 0 : 16 * i0) + it2 / C8, n0 = (it2 % C8) * 8;
+      const int64_t t = (int64_t)k * LC + s;
+      const bool ok = t < d.L;
+      const float inv = isB ? ib : ic;
+      const uint32_t wv[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      int q[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu)));
+        const float v1 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16)));
+        q[2 * e] = ok ? q_sat(v0 * inv, 127.f) : 0;
+        q[2 * e + 1] = ok ? q_sat(v1 * inv, 127.f) : 0;
+      }
+      const uint2 pq = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      if (isB) {
+        *(uint2*)&sm.qB[bsw<NS>(s, n0)] = pq;
+      } else {
+        *(uint2*)&sm.qC[bsw<NS>(s, n0)] = pq;
+        *(uint2*)(qC + ((b * Lp + t) * d.G + g) * (int64_t)NS + n0) = pq;
+      }
+    }
+  }
+  __syncthreads();
+  const int w = wave_id();
+  const int lane = tid & (kWave - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // 2. Q(B)^T fragments (nt, ks) of K steps [ks0, ks1)
+  const int ks0 = sl ? nB0 / 64 : 0, ks1 = sl ? KS : nB0 / 64;
+  const int nks = ks1 - ks0;
+  for (int f = w; f < NT * nks; f += NW) {
+    const int nt = f / nks, ks = ks0 + f % nks;
+    const int s0 = 64 * ks + 16 * lg, cB = 16 * nt + 8 * (l16 & 1);
+    const v2i_t lo = ldtr8(sm.qB + bsw<NS>(s0 + (l16 >> 1), cB));
+    const v2i_t hi = ldtr8(sm.qB + bsw<NS>(s0 + 8 + (l16 >> 1), cB));
+    *(v4i*)(qbt + (unit * (NT * KS) + nt * KS + ks) * 1024 + 16 * lane) = v4i{lo.x, lo.y, hi.x, hi.y};
+  }
+
+  // 3. CB' fragments of row tiles i0 .. i1 - 1 (layout as in cb_block_unit)
+  const float scb = s_C[g] * s_B[g];
+  const float cg = ldexpf(scb, cb_exp(scb, NS));
+  for (int f = cb_frag_base(i0) + w; f < cb_frag_base(i1); f += NW) {
     int i = 0;
 #pragma unroll
     for (int ii = 1; ii < RT; ++ii) i += (cb_frag_base(ii) <= f) ? 1 : 0;
@@ -305,7 +436,7 @@ __global__ __launch_bounds__(kPrepT) void k_prep_cb(Dims d, const void* __restri
                                                     const float* __restrict__ inv_C, const float* __restrict__ s_B,
                                                     const float* __restrict__ s_C, int8_t* __restrict__ qC,
                                                     int8_t* __restrict__ qbt, u16* __restrict__ cbf, int ncs,
-                                                    int per_unit) {
+                                                    int cb_kind) {
   static_assert(kPrepT == kCsThreads, "one block size for both kinds");
   __shared__ __attribute__((aligned(16))) char lds[PrepLds<LC, NS>::kBytes];
   const int64_t bi = blockIdx.x;
@@ -316,8 +447,11 @@ __global__ __launch_bounds__(kPrepT) void k_prep_cb(Dims d, const void* __restri
   } else {
     const int64_t ci = bi - ncs;
     constexpr int NJ = LC / 32;
-    if (per_unit)
+    if (cb_kind == kCbUnit)
       cb_block_unit<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci, *(CbLds<LC, NS>*)lds);
+    else if (cb_kind == kCbHalves)
+      cb_block_half<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci >> 1, (int)(ci & 1),
+                                *(CbLds<LC, NS>*)lds);
     else
       cb_block_pairs<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci / NJ, (int)(ci % NJ),
                                  *(CbPairLds<LC, NS>*)lds);
@@ -566,13 +700,19 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     const int kn1 = min(k + 1, d.c - 1);      // next chunk (clamped; the last chunk prefetches nothing)
     const int64_t t0 = (int64_t)k * LC;
     __syncthreads();  // B1: chunk k staged; H_{k-1} published; chunk k - 1's buffers free
+    // the wave index, hidden from the compiler at every chunk: values derived
+    // from it (row tiles, fragment offsets, which pairs are below the
+    // diagonal) are then formed per chunk in scalar registers instead of being
+    // hoisted out of the loop and spilled
+    int wk = w;
+    asm volatile("" : "+s"(wk));
     // the first row tile's operands (landing during ChunkState) and the next
     // chunk's share of x (landing by the time it is staged); the second row
     // tile's operands are issued after the first tile, so that the burst at
     // the barrier stays short
     TileOps1 op1;
     TileOps2 op2;
-    load_tile_ops(k, w, op1);
+    load_tile_ops(k, wk, op1);
     SRegs<LC> sreg;
     stage_load(kn1, sreg, k + 1 < d.c);
 
@@ -727,12 +867,12 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     // staged into the other buffer (its readers, chunk k - 1, are past B1)
     const auto next_qbt = [&] { load_qbt(kn1, qbt); };  // the last chunk reloads its own (L2-resident)
     if constexpr (NRR == 2) {
-      scan_tile(w, op1, [] {});
-      load_tile_ops(k, RT - 1 - w, op2);
+      scan_tile(wk, op1, [] {});
+      load_tile_ops(k, RT - 1 - wk, op2);
       if (k + 1 < d.c) stage_store(k + 1, sreg);
-      scan_tile(RT - 1 - w, op2, next_qbt);
+      scan_tile(RT - 1 - wk, op2, next_qbt);
     } else {
-      scan_tile(w, op1, next_qbt);
+      scan_tile(wk, op1, next_qbt);
       if (k + 1 < d.c) stage_store(k + 1, sreg);
     }
 
@@ -806,13 +946,13 @@ hipError_t launch_i8v2(const Dims& d, const void* X, const void* dt, const float
 
   // ChunkCumsum blocks and the B/C + ChunkBMM blocks side by side in one launch
   const int64_t ncs = (int64_t)d.c * d.B * ((d.H + kCsHeads - 1) / kCsHeads);
-  // one block per unit when there are enough units (measured: 64 units of the
-  // 2.7B layer favour it, 8 units of the 1.3B layer favour pairs of row tiles)
-  const int per_unit = bkg >= 32;
-  const int64_t ncb = per_unit ? (int64_t)bkg : (int64_t)bkg * (LC / 32);
+  // block kind by the number of units (measured: 8 units favour pairs of row
+  // tiles, 64 units halves, 256 and 512 units one block per unit)
+  const int cb_kind = bkg < 32 ? kCbPairs : (2 * (int64_t)bkg <= cu_count() ? kCbHalves : kCbUnit);
+  const int64_t ncb = (int64_t)bkg * (cb_kind == kCbUnit ? 1 : cb_kind == kCbHalves ? 2 : LC / 32);
   if (ncs + ncb >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_prep_cb<DT, LC, NS>), dim3((unsigned)(ncs + ncb)), dim3(kPrepT), 0, st, d, dt, A, dAcs, lut,
-                     qd, B, C, sc.inv_B, sc.inv_C, sc.s_B, sc.s_C, qC, qbt, cbf, (int)ncs, per_unit);
+                     qd, B, C, sc.inv_B, sc.inv_C, sc.s_B, sc.s_C, qC, qbt, cbf, (int)ncs, cb_kind);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -18,10 +18,12 @@ CASES = {
     "f32_l256": synth.Workload(14, 1, 512, 2, 64, 128, 1, 256, "fp32", True),
     "bf16_n64_l128": synth.Workload(15, 2, 700, 6, 64, 64, 2, 128, "bf16", True),
     "f16_l128": synth.Workload(16, 1, 384, 3, 64, 128, 1, 128, "fp16", True),
-    # at least 32 (batch, chunk, group) units: the preparation launch's
-    # one-block-per-unit layout, at l = 128 and at N = 64
+    # the preparation launch's block kinds for many (batch, chunk, group)
+    # units: two blocks per unit for 32 .. CUs / 2 units (80 and 48 units, at
+    # l = 128 and at N = 64), one block per unit above that (144 units)
     "bf16_units_l128": synth.Workload(17, 4, 520, 8, 64, 64, 4, 128, "bf16", True),
     "f16_units_n64": synth.Workload(18, 4, 600, 8, 64, 64, 4, 256, "fp16", True),
+    "f16_units_whole": synth.Workload(19, 4, 1100, 4, 64, 128, 4, 128, "fp16", True),
 }
 
 
