@@ -499,6 +499,18 @@ struct SRegs {
   uint32_t qd;  // the dword holding the chunk's Q(Decay) byte
 };
 
+// A row tile's operands as its scan reads them: the m-th off-diagonal CB'
+// fragment (m below MF) is F[m], or F[NF_ - 1 - m] for the second row tile of a
+// wave, whose fragments fill the register array from the top.
+template <int MF_, int NF_, bool REV, int KN>
+struct TileView {
+  static constexpr int MF = MF_;
+  const v4i (&F)[NF_];
+  const v4i& diag;
+  const v4i (&qc)[KN];
+  __device__ __forceinline__ const v4i& off(int m) const { return REV ? F[NF_ - 1 - m] : F[m]; }
+};
+
 template <int DT, int LC, int NS, int PW, bool TAPS>
 __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u16* s_x, int8_t* s_qx,
                                             int8_t* s_h8, float* s_va, float* s_vb, float* s_vw,
@@ -655,29 +667,39 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   // and the diagonal one) and Q(C) rows, issued one phase ahead of their use and
   // always before this wave's Y stores of the phase in between (the vector
   // memory counter retires in issue order, so a wait for an operand then never
-  // waits for a store).
-  // (MF off-diagonal fragments: row tile w < 8 has at most 3, the second row
-  // tile RT - 1 - w at most 7)
-  struct TileOps1 {
-    v4i off[4];
-    v4i diag;
-    v4i qc[KN];
-  };
-  struct TileOps2 {
-    v4i off[RT / 2];
-    v4i diag;
-    v4i qc[KN];
-  };
-  const auto load_tile_ops = [&](int kc, int i, auto& t) {
-    constexpr int MF = sizeof(t.off) / sizeof(t.off[0]);
-    const char* src = cbf_h + kc * cbf_kstride + cb_frag_base(i) * 1024;
-    // every wave issues MF + 1 fragment loads (a fixed count, so the
-    // compiler's in-order wait counts stay exact); pairs past the diagonal
-    // reload the diagonal fragment, which is in the cache
+  // waits for a store). Every wave issues the same number of loads at the same
+  // points, so the compiler's in-order wait counts stay exact.
+  //  - One row tile per wave (l = 128): tile w has w / 2 <= 3 off-diagonal
+  //    pairs; the slots past them reload the diagonal fragment (cached).
+  //  - Two row tiles per wave (l = 256): tiles w and 15 - w have w / 2 and
+  //    7 - w / 2 pairs, 7 together, held in Fo[0 .. 6]: the first tile's
+  //    fragments from the bottom, the second's from the top. Fo[0 .. 3] (the
+  //    first tile's pairs and the second's highest ones) and the first tile's
+  //    diagonal and Q(C) come at the barrier; Fo[4 .. 6] and the second tile's
+  //    diagonal and Q(C) after the first tile.
+  constexpr int NOFF = (NRR == 2) ? RT / 2 - 1 : 4;
+  static_assert(NRR == 1 || RT == 2 * kCompW, "two row tiles per wave pair up as w and RT - 1 - w");
+  const auto frag_src = [&](int kc, int i) { return cbf_h + kc * cbf_kstride + cb_frag_base(i) * 1024; };
+  const auto load_first = [&](int kc, int i1, v4i (&Fo)[NOFF], v4i& diag, v4i (&qc)[KN]) {
+    const int mi1 = i1 >> 1;
+    const char* s1 = frag_src(kc, i1);
+    if constexpr (NRR == 2) {
+      const char* s2 = frag_src(kc, RT - 1 - i1);
 #pragma unroll
-    for (int m = 0; m < MF; ++m) t.off[m] = frag(src + min(m, i / 2) * 1024);
-    t.diag = frag(src + (i / 2) * 1024);
-    load_qc(kc, i, t.qc);
+      for (int j = 0; j < 4; ++j) Fo[j] = frag(j < mi1 ? s1 + j * 1024 : s2 + (NOFF - 1 - j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Fo[j] = frag(s1 + min(j, mi1) * 1024);
+    }
+    diag = frag(s1 + mi1 * 1024);
+    load_qc(kc, i1, qc);
+  };
+  const auto load_second = [&](int kc, int i2, v4i (&Fo)[NOFF], v4i& diag, v4i (&qc)[KN]) {
+    const char* s2 = frag_src(kc, i2);
+#pragma unroll
+    for (int j = NOFF - 1; j >= 4; --j) Fo[j] = frag(s2 + (NOFF - 1 - j) * 1024);
+    diag = frag(s2 + (i2 >> 1) * 1024);
+    load_qc(kc, i2, qc);
   };
 
   // prologue: stage chunk 0 (every wave its share)
@@ -710,9 +732,8 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     // chunk's share of x (landing by the time it is staged); the second row
     // tile's operands are issued after the first tile, so that the burst at
     // the barrier stays short
-    TileOps1 op1;
-    TileOps2 op2;
-    load_tile_ops(k, wk, op1);
+    v4i Fo[NOFF], diag1, diag2, qc1[KN], qc2[KN];
+    load_first(k, wk, Fo, diag1, qc1);
     SRegs<LC> sreg;
     stage_load(kn1, sreg, k + 1 < d.c);
 
@@ -754,7 +775,7 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
 
     // ---- ChunkScan, transposed: Y^T[p, s] for row tile i ----
     const auto scan_tile = [&](const int i, const auto& t, auto after_offdiag) {
-      constexpr int MF = sizeof(t.off) / sizeof(t.off[0]);
+      constexpr int MF = std::remove_reference_t<decltype(t)>::MF;
       const int mi = i >> 1;  // pairs 0 .. mi - 1 are below the diagonal; pair mi holds it
       const int s_row = 16 * i + l16;
       const float a_ref = vA[16 * i];
@@ -785,7 +806,7 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
           const float4 va = *(const float4*)&Vw[32 * m + 8 * lg];
           const float4 vb = *(const float4*)&Vw[32 * m + 8 * lg + 4];
           const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-          const v4i cw = t.off[m];
+          const v4i cw = t.off(m);
           F wf;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -867,12 +888,12 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     // staged into the other buffer (its readers, chunk k - 1, are past B1)
     const auto next_qbt = [&] { load_qbt(kn1, qbt); };  // the last chunk reloads its own (L2-resident)
     if constexpr (NRR == 2) {
-      scan_tile(wk, op1, [] {});
-      load_tile_ops(k, RT - 1 - wk, op2);
+      scan_tile(wk, TileView<4, NOFF, false, KN>{Fo, diag1, qc1}, [] {});
+      load_second(k, RT - 1 - wk, Fo, diag2, qc2);
       if (k + 1 < d.c) stage_store(k + 1, sreg);
-      scan_tile(RT - 1 - wk, op2, next_qbt);
+      scan_tile(RT - 1 - wk, TileView<NOFF, NOFF, true, KN>{Fo, diag2, qc2}, next_qbt);
     } else {
-      scan_tile(wk, op1, next_qbt);
+      scan_tile(wk, TileView<4, NOFF, false, KN>{Fo, diag1, qc1}, next_qbt);
       if (k + 1 < d.c) stage_store(k + 1, sreg);
     }
 
