@@ -20,7 +20,7 @@ namespace ssd {
 // grouping, is a multiple of 2^e of magnitude at most sum |p_s|. When that bound
 // is below 2^(53 + e), every such sum is representable, so each addition is
 // exact and any order of summation gives the sequential result: the wave then
-// adds its lanes' totals with a shuffle scan. The test uses the computed sum of
+// adds its lanes' totals with a cross-lane scan. The test uses the computed sum of
 // |p_s| against 2^(52 + e), a factor of two that covers its own rounding. For
 // heads that fail it (very wide exponent spreads, or inf / NaN), lane 0 runs
 // the sequential chain. Padded positions past L carry dt = 0, which leaves the
@@ -37,6 +37,46 @@ __device__ __forceinline__ int cs_lsb_exp(double p) {
   const int E = (int)((bits >> 52) & 0x7ff);
   const uint64_t m = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
   return E - 1075 + (int)__builtin_ctzll(m);
+}
+
+// Inclusive scans across the 64 lanes of a wave on DPP moves (no LDS round
+// trips): four row shifts within each row of 16 lanes, then the last lane of
+// row 0 broadcast into row 1 (and of row 2 into row 3), then the last lane of
+// row 1 into rows 2 and 3. A lane the move does not reach reads the identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long x = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)x, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(x >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+__device__ __forceinline__ double wave_scan_add(double v) {  // the identity 0.0 (+0)
+  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_min_step(int v) {
+  return min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ int wave_scan_min(int v) {
+  v = dpp_min_step<0x111, 0xf>(v);
+  v = dpp_min_step<0x112, 0xf>(v);
+  v = dpp_min_step<0x114, 0xf>(v);
+  v = dpp_min_step<0x118, 0xf>(v);
+  v = dpp_min_step<0x142, 0xa>(v);
+  v = dpp_min_step<0x143, 0xc>(v);
+  return v;
+}
+__device__ __forceinline__ double lane63_f64(double v) {
+  const unsigned long long x = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(x >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
 // LDS the block body needs (the caller provides it, so that launches holding
@@ -103,21 +143,14 @@ __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
       if (p != 0.0) elo = min(elo, cs_lsb_exp(p));
     }
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    sabs += __shfl_xor(sabs, m);
-    elo = min(elo, __shfl_xor(elo, m));
-  }
+  // wave totals (the last lane of the inclusive scans)
+  sabs = lane63_f64(wave_scan_add(sabs));
+  elo = __builtin_amdgcn_readlane(wave_scan_min(elo), 63);
   // (NaN compares false, so inf / NaN products take the chain)
   const bool exact = elo == INT_MAX || sabs < ldexp(1.0, 52 + elo);
   if (exact) {
-    double incl = tot;  // inclusive scan of the lane totals
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const double o = __shfl_up(incl, m);
-      if (lane >= m) incl += o;
-    }
-    const double excl = incl - tot;  // exact: a partial sum, see above
+    const double incl = wave_scan_add(tot);  // inclusive scan of the lane totals
+    const double excl = incl - tot;          // exact: a partial sum, see above
 #pragma unroll
     for (int u = 0; u < 4; ++u) q[u] += excl;
   } else {
@@ -143,7 +176,7 @@ __device__ __forceinline__ void chunk_cumsum_block(const void* __restrict__ dt,
     for (int u = 0; u < 4; ++u)
       if (u < R) q[u] = sa[j][R * lane + u];
   }
-  const double alast = __shfl(R == 4 ? q[3] : (R == 2 ? q[1] : q[0]), 63);  // a at s = l - 1
+  const double alast = lane63_f64(R == 4 ? q[3] : (R == 2 ? q[1] : q[0]));  // a at s = l - 1
   const int64_t o0 = ((b * d.H + h0 + j) * d.c + k) * (int64_t)l + R * lane;
   float da[4], lu[4];
 #pragma unroll
