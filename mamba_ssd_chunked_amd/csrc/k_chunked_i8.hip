@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kCT) void k_cstate_i8(ChunkArgs a) {
 // state of chunk k - 1 are staged in LDS; the CB' fragments and Q(C) rows come
 // from memory straight into registers.
 // ===========================================================================
-template <int DT, int LC, int NS>
+template <int DT, int LC, int NS, bool YROWS>
 __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
   typedef typename Store<DT>::T T;
   typedef FragF<DT> F;
@@ -378,15 +378,47 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] = F::mma(xd[pt], wf, acc[pt]);
     }
-    if (t0 + s_row < d.L) {
-      char* yt = (char*)(ytile0 + (16 * i) * (int64_t)H * kHP);
-      const uint32_t yo = (uint32_t)((l16 * H * kHP + 4 * lg) * (int)sizeof(T));
+    if constexpr (!YROWS) {
+      if (t0 + s_row < d.L) {
+        char* yt = (char*)(ytile0 + (16 * i) * (int64_t)H * kHP);
+        const uint32_t yo = (uint32_t)((l16 * H * kHP + 4 * lg) * (int)sizeof(T));
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-        *(u2v_t*)(yt + (yo + 16 * pt * (uint32_t)sizeof(T))) =
-            u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])};
+        for (int pt = 0; pt < 4; ++pt)
+          *(u2v_t*)(yt + (yo + 16 * pt * (uint32_t)sizeof(T))) =
+              u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])};
+      }
+      __builtin_amdgcn_wave_barrier();
+      return;
     }
-    __builtin_amdgcn_wave_barrier();
+    // YROWS: Y leaves as whole 128-byte rows. YR rows of the tile at a time go
+    // through this wave's V table (no longer read) and out with one 16-byte
+    // store per lane (lane: row lane / 8, piece lane % 8). Measured on 20480
+    // blocks (the 64K-token layer): 11% faster than 32-byte pieces of 16 rows
+    // per store; on 512 blocks 9% slower (the extra LDS round trips add to a
+    // latency-bound launch), so small launches keep the direct stores.
+    constexpr int YR = (LC * (int)sizeof(float) / 128) < 8 ? LC * (int)sizeof(float) / 128 : 8;
+    static_assert(kHP * sizeof(T) == 128 && 16 % YR == 0, "rows of Y fit the V table");
+    char* const stg = (char*)Vw;
+#pragma unroll
+    for (int hh = 0; hh < 16 / YR; ++hh) {
+      if (l16 / YR == hh) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          *(u2v_t*)(stg + (l16 % YR) * 128 + (16 * pt + 4 * lg) * (int)sizeof(T)) =
+              u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int r = 16 * i + YR * hh + (lane >> 3);
+      if ((lane >> 3) < YR) {
+        const v4i row = *(const v4i*)(stg + (lane >> 3) * 128 + 16 * (lane & 7));
+        if (t0 + r < d.L) *(v4i*)((char*)(ytile0 + (int64_t)r * H * kHP) + 16 * (lane & 7)) = row;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // the table is rewritten next (rows or row tile)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   };
 
   // row tiles of this wave: w, 7 - w (, 8 + w, 15 - w); the next tile's
@@ -447,10 +479,14 @@ hipError_t launch_chunked_i8(const Dims& d, int dtype, const void* X, const void
     if (e != hipSuccess) return e;
   }
   e = hipErrorNotSupported;
-#define SSD_SC(DTV, LCV, NSV)                                                                           \
-  if (dtype == DTV && d.l == LCV && d.N == NSV) {                                                       \
-    hipLaunchKernelGGL((k_cscan_i8<DTV, LCV, NSV>), dim3((unsigned)nb), dim3(kCT), 0, st, ca);         \
-    e = hipGetLastError();                                                                              \
+  const bool yrows = nb >= 8 * (int64_t)cu_count();
+#define SSD_SC(DTV, LCV, NSV)                                                                          \
+  if (dtype == DTV && d.l == LCV && d.N == NSV) {                                                      \
+    if (yrows)                                                                                         \
+      hipLaunchKernelGGL((k_cscan_i8<DTV, LCV, NSV, true>), dim3((unsigned)nb), dim3(kCT), 0, st, ca);  \
+    else                                                                                               \
+      hipLaunchKernelGGL((k_cscan_i8<DTV, LCV, NSV, false>), dim3((unsigned)nb), dim3(kCT), 0, st, ca); \
+    e = hipGetLastError();                                                                             \
   }
   SSD_SC(DT_F16, 256, 128)
   SSD_SC(DT_F16, 256, 64)
