@@ -867,16 +867,39 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
         for (int jp = 0; jp < PW; ++jp) acc[jp] = F::mma(xd[jp], wf, acc[jp]);
       }
       // epilogue: lane holds s = s_row and p = 16 pt + 4 lg + r
-      if (t0 + s_row < d.L) {
-        char* ytile = (char*)(ybase + (t0 + 16 * i) * (int64_t)H * kHP);
-        const uint32_t yo = (uint32_t)((l16 * H * kHP + 4 * lg) * (int)sizeof(T));
+      {
+        // lanes of rows lg and lg ^ 1 (same l16) swap halves so that each lane
+        // holds whole 16-byte pieces (8 consecutive p) and stores half as often
+        uint32_t dv[PW][2];
 #pragma unroll
         for (int jp = 0; jp < PW; ++jp) {
-          const int pt = pt_base + jp;
-          // plain stores: the four 32-byte pieces of a row merge into whole
-          // lines in L2 (streaming stores reach HBM as partial writes)
-          *(u2v_t*)(ytile + (yo + 16 * pt * (uint32_t)sizeof(T))) =
-              u2v_t{pack2<DT>(acc[jp][0], acc[jp][1]), pack2<DT>(acc[jp][2], acc[jp][3])};
+          dv[jp][0] = pack2<DT>(acc[jp][0], acc[jp][1]);
+          dv[jp][1] = pack2<DT>(acc[jp][2], acc[jp][3]);
+        }
+        const bool odd = lg & 1;
+        const uint32_t om = odd ? 0xffffffffu : 0u;  // bitwise selects (no indexed register arrays)
+        constexpr int HP = PW / 2;  // p tiles a lane sends (and keeps)
+        uint32_t rv[HP][2], kv[HP][2];
+#pragma unroll
+        for (int q = 0; q < HP; ++q)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t v = (dv[q][e] & om) | (dv[HP + q][e] & ~om);  // odd rows send p tile q, even ones HP + q
+            kv[q][e] = (dv[HP + q][e] & om) | (dv[q][e] & ~om);          // and keep the other
+            const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            rv[q][e] = (r[0] & om) | (r[1] & ~om);
+          }
+        if (t0 + s_row < d.L) {
+          char* yrow = (char*)(ybase + (t0 + s_row) * (int64_t)H * kHP) + 32 * pt_base + 8 * (lg & 2);
+#pragma unroll
+          for (int q = 0; q < HP; ++q) {
+            const int jp = odd ? HP + q : q;
+            // the lower 8 bytes come from the even row, the upper from the odd one
+            const uint32_t l0 = (rv[q][0] & om) | (kv[q][0] & ~om), l1 = (rv[q][1] & om) | (kv[q][1] & ~om);
+            const uint32_t h0 = (kv[q][0] & om) | (rv[q][0] & ~om), h1 = (kv[q][1] & om) | (rv[q][1] & ~om);
+            const v4i piece = v4i{(int)l0, (int)l1, (int)h0, (int)h1};
+            *(v4i*)(yrow + 32 * jp) = piece;
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();  // this wave's table is rewritten by its next row tile
