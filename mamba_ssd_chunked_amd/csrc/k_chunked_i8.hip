@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kCT) void k_cstate_i8(ChunkArgs a) {
 // state of chunk k - 1 are staged in LDS; the CB' fragments and Q(C) rows come
 // from memory straight into registers.
 // ===========================================================================
-template <int DT, int LC, int NS, bool YROWS>
+template <int DT, int LC, int NS>
 __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
   typedef typename Store<DT>::T T;
   typedef FragF<DT> F;
@@ -390,47 +390,39 @@ __global__ __launch_bounds__(kCT, 3) void k_cscan_i8(ChunkArgs a) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] = F::mma(xd[pt], wf, acc[pt]);
     }
-    if constexpr (!YROWS) {
-      if (t0 + s_row < d.L) {
-        char* yt = (char*)(ytile0 + (16 * i) * (int64_t)H * kHP);
-        const uint32_t yo = (uint32_t)((l16 * H * kHP + 4 * lg) * (int)sizeof(T));
+    // lanes of rows lg and lg ^ 1 (same l16) swap halves so that each lane
+    // holds whole 16-byte pieces (8 consecutive p) and the row leaves in two
+    // stores instead of four. Measured on the 64K-token layer: 549 us with
+    // 8-byte pieces, 478 with the rows gathered through LDS, 468 this way.
+    uint32_t dv[4][2];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          *(u2v_t*)(yt + (yo + 16 * pt * (uint32_t)sizeof(T))) =
-              u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])};
-      }
-      __builtin_amdgcn_wave_barrier();
-      return;
+    for (int pt = 0; pt < 4; ++pt) {
+      dv[pt][0] = pack2<DT>(acc[pt][0], acc[pt][1]);
+      dv[pt][1] = pack2<DT>(acc[pt][2], acc[pt][3]);
     }
-    // YROWS: Y leaves as whole 128-byte rows. YR rows of the tile at a time go
-    // through this wave's V table (no longer read) and out with one 16-byte
-    // store per lane (lane: row lane / 8, piece lane % 8). Measured on 20480
-    // blocks (the 64K-token layer): 11% faster than 32-byte pieces of 16 rows
-    // per store; on 512 blocks 9% slower (the extra LDS round trips add to a
-    // latency-bound launch), so small launches keep the direct stores.
-    constexpr int YR = (LC * (int)sizeof(float) / 128) < 8 ? LC * (int)sizeof(float) / 128 : 8;
-    static_assert(kHP * sizeof(T) == 128 && 16 % YR == 0, "rows of Y fit the V table");
-    char* const stg = (char*)Vw;
+    const uint32_t om = (lg & 1) ? 0xffffffffu : 0u;  // bitwise selects (no indexed register arrays)
+    uint32_t rv[2][2], kv[2][2];
 #pragma unroll
-    for (int hh = 0; hh < 16 / YR; ++hh) {
-      if (l16 / YR == hh) {
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          *(u2v_t*)(stg + (l16 % YR) * 128 + (16 * pt + 4 * lg) * (int)sizeof(T)) =
-              u2v_t{pack2<DT>(acc[pt][0], acc[pt][1]), pack2<DT>(acc[pt][2], acc[pt][3])};
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t v = (dv[q][e] & om) | (dv[2 + q][e] & ~om);  // odd rows send p tile q, even ones 2 + q
+        kv[q][e] = (dv[2 + q][e] & om) | (dv[q][e] & ~om);          // and keep the other
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        rv[q][e] = (r[0] & om) | (r[1] & ~om);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int r = 16 * i + YR * hh + (lane >> 3);
-      if ((lane >> 3) < YR) {
-        const v4i row = *(const v4i*)(stg + (lane >> 3) * 128 + 16 * (lane & 7));
-        if (t0 + r < d.L) *(v4i*)((char*)(ytile0 + (int64_t)r * H * kHP) + 16 * (lane & 7)) = row;
+    if (t0 + s_row < d.L) {
+      char* yrow = (char*)(ytile0 + (16 * i + l16) * (int64_t)H * kHP) + 8 * (lg & 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int jp = (lg & 1) ? 2 + q : q;
+        // the lower 8 bytes come from the even row, the upper from the odd one
+        const uint32_t l0 = (rv[q][0] & om) | (kv[q][0] & ~om), l1 = (rv[q][1] & om) | (kv[q][1] & ~om);
+        const uint32_t h0 = (kv[q][0] & om) | (rv[q][0] & ~om), h1 = (kv[q][1] & om) | (rv[q][1] & ~om);
+        *(v4i*)(yrow + 32 * jp) = v4i{(int)l0, (int)l1, (int)h0, (int)h1};
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();  // the table is rewritten next (rows or row tile)
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    __builtin_amdgcn_wave_barrier();
   };
 
   // row tiles of this wave: w, 7 - w (, 8 + w, 15 - w); the next tile's
@@ -491,14 +483,10 @@ hipError_t launch_chunked_i8(const Dims& d, int dtype, const void* X, const void
     if (e != hipSuccess) return e;
   }
   e = hipErrorNotSupported;
-  const bool yrows = nb >= 8 * (int64_t)cu_count();
-#define SSD_SC(DTV, LCV, NSV)                                                                          \
-  if (dtype == DTV && d.l == LCV && d.N == NSV) {                                                      \
-    if (yrows)                                                                                         \
-      hipLaunchKernelGGL((k_cscan_i8<DTV, LCV, NSV, true>), dim3((unsigned)nb), dim3(kCT), 0, st, ca);  \
-    else                                                                                               \
-      hipLaunchKernelGGL((k_cscan_i8<DTV, LCV, NSV, false>), dim3((unsigned)nb), dim3(kCT), 0, st, ca); \
-    e = hipGetLastError();                                                                             \
+#define SSD_SC(DTV, LCV, NSV)                                                                           \
+  if (dtype == DTV && d.l == LCV && d.N == NSV) {                                                       \
+    hipLaunchKernelGGL((k_cscan_i8<DTV, LCV, NSV>), dim3((unsigned)nb), dim3(kCT), 0, st, ca);         \
+    e = hipGetLastError();                                                                              \
   }
   SSD_SC(DT_F16, 256, 128)
   SSD_SC(DT_F16, 256, 64)
