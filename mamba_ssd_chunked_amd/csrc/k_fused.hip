@@ -350,6 +350,11 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // B rows and C rows have landed
     __syncthreads();  // chunk k staged; s_H holds H_{k-1}
     asm volatile("" : "+s"(wk));
+    // issue priority: the second wave of each SIMD (w + 4) leads ChunkState
+    // and the first row tile, the first wave the second tile, so that neither
+    // falls behind and runs alone at the end of the chunk (as in the INT8
+    // kernel; measured 2% faster here)
+    if (wk >= 4) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
     const float alast2 = vA2[LC - 1];  // a_{k,l-1} log2(e): StatePassing decay
 
 #pragma unroll
@@ -423,6 +428,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int i = (rr == 0) ? wk : 2 * kWaves - 1 - wk;
+      if (rr == 1) { if (wk >= 4) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1); }
       if (i >= RT) continue;
       const int s_row = 16 * i + l16;
       F cr[KNF];
