@@ -181,34 +181,33 @@ __device__ __forceinline__ void cb_block_unit(const Dims& d, const void* __restr
   }
 }
 
-// The first row tile of the second half of a unit: the halves hold as near an
-// equal number of CB' fragments as whole row tiles allow.
-template <int LC>
-__host__ __device__ constexpr int cb_split_tile() {
+// Slices of a unit's row tiles holding about equal numbers of CB' fragments:
+// slice q starts at the first row tile i with S cb_frag_base(i) >= q NF.
+template <int LC, int S>
+__host__ __device__ constexpr int cb_slice_tile(int q) {
   int i = 0;
-  while (2 * cb_frag_base(i) < cb_frags(LC)) ++i;
+  while (S * cb_frag_base(i) < q * cb_frags(LC)) ++i;
   return i;
 }
+// Q(B) rows the CB' fragments of row tiles below i1 reach (0 .. 32 (i1 - 1) / 2 + 31)
+__host__ __device__ constexpr int cb_rows_b(int i1) { return 32 * ((i1 - 1) / 2 + 1); }
 
-// Half sl of a unit: row tiles [i0, i1) (i0 = 0 or the split tile). The block
-// quantises the Q(B) rows its CB' fragments reach (0 .. 32 (i1 - 1) / 2 + 31)
-// and the Q(C) rows of its tiles, writes those Q(C) rows and CB' fragments, and
-// the Q(B)^T fragments of K steps [ks0, ks1): the first half those its Q(B)
-// rows cover whole, the second half the rest.
-template <int DT, int LC, int NS>
-__device__ __forceinline__ void cb_block_half(const Dims& d, const void* __restrict__ B, const void* __restrict__ C,
-                                              const float* __restrict__ inv_B, const float* __restrict__ inv_C,
-                                              const float* __restrict__ s_B, const float* __restrict__ s_C,
-                                              int8_t* __restrict__ qC, int8_t* __restrict__ qbt,
-                                              u16* __restrict__ cbf, int64_t unit, int sl, CbLds<LC, NS>& sm) {
+// Slice sl of S of a unit: row tiles [i0, i1). The block quantises the Q(B)
+// rows its CB' fragments reach and the Q(C) rows of its tiles, writes those
+// Q(C) rows and CB' fragments, and the Q(B)^T fragments of the K steps whose
+// rows it covers and no earlier slice does.
+template <int DT, int LC, int NS, int S>
+__device__ __forceinline__ void cb_block_slice(const Dims& d, const void* __restrict__ B, const void* __restrict__ C,
+                                               const float* __restrict__ inv_B, const float* __restrict__ inv_C,
+                                               const float* __restrict__ s_B, const float* __restrict__ s_C,
+                                               int8_t* __restrict__ qC, int8_t* __restrict__ qbt,
+                                               u16* __restrict__ cbf, int64_t unit, int sl, CbLds<LC, NS>& sm) {
   typedef typename Store<DT>::T T;
   constexpr int KN = NS / 64, NT = NS / 16, KS = LC / 64, NF = cb_frags(LC), RT = LC / 16;
   constexpr int C8 = NS / 8;
   constexpr int NW = kPrepT / kWave;
-  constexpr int IS = cb_split_tile<LC>();
-  constexpr int nB0 = 32 * ((IS - 1) / 2 + 1);  // Q(B) rows of the first half
   constexpr int kMaxIt = (2 * LC * C8 + kPrepT - 1) / kPrepT;
-  static_assert(IS > 0 && IS < RT, "two nonempty halves");
+  static_assert(cb_slice_tile<LC, S>(1) > 0 && cb_slice_tile<LC, S>(S - 1) < RT, "nonempty slices");
   const int64_t g_ = unit % d.G;
   const int64_t bk = unit / d.G;
   const int k = (int)(bk % d.c);
@@ -217,8 +216,8 @@ __device__ __forceinline__ void cb_block_half(const Dims& d, const void* __restr
   const int tid = threadIdx.x;
   const int64_t Lp = (int64_t)d.c * LC;
   const float ib = inv_B[g], ic = inv_C[g];
-  const int i0 = sl ? IS : 0, i1 = sl ? RT : IS;
-  const int nB = sl ? LC : nB0;
+  const int i0 = cb_slice_tile<LC, S>(sl), i1 = cb_slice_tile<LC, S>(sl + 1);
+  const int nB = min(LC, cb_rows_b(i1));
   const int nit = (nB + 16 * (i1 - i0)) * C8;
 
   // 1. quantise: items [0, nB C8) are Q(B) rows 0 .. nB - 1, the rest the Q(C)
@@ -269,8 +268,10 @@ __device__ __forceinline__ void cb_block_half(const Dims& d, const void* __restr
   const int lane = tid & (kWave - 1);
   const int l16 = lane & 15, lg = lane >> 4;
 
-  // 2. Q(B)^T fragments (nt, ks) of K steps [ks0, ks1)
-  const int ks0 = sl ? nB0 / 64 : 0, ks1 = sl ? KS : nB0 / 64;
+  // 2. Q(B)^T fragments (nt, ks) of K steps [ks0, ks1): those whose 64 rows this
+  //    slice covers and the previous slice does not (the last slice: the rest)
+  const int ks0 = sl == 0 ? 0 : min(LC, cb_rows_b(i0)) / 64;
+  const int ks1 = sl == S - 1 ? KS : nB / 64;
   const int nks = ks1 - ks0;
   for (int f = w; f < NT * nks; f += NW) {
     const int nt = f / nks, ks = ks0 + f % nks;
@@ -454,8 +455,9 @@ __global__ __launch_bounds__(kPrepT) void k_prep_cb(Dims d, const void* __restri
     if (cb_kind == kCbUnit)
       cb_block_unit<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci, *(CbLds<LC, NS>*)lds);
     else if (cb_kind == kCbHalves)
-      cb_block_half<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci >> 1, (int)(ci & 1),
-                                *(CbLds<LC, NS>*)lds);
+      cb_block_slice<DT, LC, NS, 2>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci >> 1, (int)(ci & 1),
+                                    *(CbLds<LC, NS>*)lds);
+
     else
       cb_block_pairs<DT, LC, NS>(d, B, C, inv_B, inv_C, s_B, s_C, qC, qbt, cbf, ci / NJ, (int)(ci % NJ),
                                  *(CbPairLds<LC, NS>*)lds);
@@ -1006,7 +1008,9 @@ hipError_t launch_i8v2(const Dims& d, const void* X, const void* dt, const float
   // ChunkCumsum blocks and the B/C + ChunkBMM blocks side by side in one launch
   const int64_t ncs = (int64_t)d.c * d.B * ((d.H + kCsHeads - 1) / kCsHeads);
   // block kind by the number of units (measured: 8 units favour pairs of row
-  // tiles, 64 units halves, 256 and 512 units one block per unit)
+  // tiles, 64 units halves, 256 and 512 units one block per unit; quarters of
+  // 64 units were slower: with the cumsum blocks the launch no longer fits
+  // the CUs at once)
   const int cb_kind = bkg < 32 ? kCbPairs : (2 * (int64_t)bkg <= cu_count() ? kCbHalves : kCbUnit);
   const int64_t ncb = (int64_t)bkg * (cb_kind == kCbUnit ? 1 : cb_kind == kCbHalves ? 2 : LC / 32);
   if (ncs + ncb >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
