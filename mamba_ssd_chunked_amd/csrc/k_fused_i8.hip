@@ -120,15 +120,15 @@ __device__ __forceinline__ void cb_block_unit(const Dims& d, const void* __restr
     const bool ok = t < d.L;
     const float inv = isB ? ib : ic;
     const uint32_t wv[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-    int q[8];
+    // sat(RHAZ(v inv)) through the clamp-then-round-away form of the main
+    // kernel's quantiser (same codes as clamping after rounding; rows past L: 0)
+    float v[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v0 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu)));
-      const float v1 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16)));
-      q[2 * e] = ok ? q_sat(v0 * inv, 127.f) : 0;
-      q[2 * e + 1] = ok ? q_sat(v1 * inv, 127.f) : 0;
+      v[2 * e] = ok ? Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu))) * inv : 0.f;
+      v[2 * e + 1] = ok ? Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16))) * inv : 0.f;
     }
-    const uint2 pq = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+    const uint2 pq = make_uint2(q8x4(v[0], v[1], v[2], v[3]), q8x4(v[4], v[5], v[6], v[7]));
     if (isB) {
       *(uint2*)&sm.qB[bsw<NS>(s, n0)] = pq;
     } else {
@@ -246,15 +246,15 @@ __device__ __forceinline__ void cb_block_slice(const Dims& d, const void* __rest
       const bool ok = t < d.L;
       const float inv = isB ? ib : ic;
       const uint32_t wv[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-      int q[8];
+      // sat(RHAZ(v inv)) through the clamp-then-round-away form of the main
+      // kernel's quantiser (same codes as clamping after rounding; rows past L: 0)
+      float v[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v0 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu)));
-        const float v1 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16)));
-        q[2 * e] = ok ? q_sat(v0 * inv, 127.f) : 0;
-        q[2 * e + 1] = ok ? q_sat(v1 * inv, 127.f) : 0;
+        v[2 * e] = ok ? Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu))) * inv : 0.f;
+        v[2 * e + 1] = ok ? Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16))) * inv : 0.f;
       }
-      const uint2 pq = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      const uint2 pq = make_uint2(q8x4(v[0], v[1], v[2], v[3]), q8x4(v[4], v[5], v[6], v[7]));
       if (isB) {
         *(uint2*)&sm.qB[bsw<NS>(s, n0)] = pq;
       } else {
@@ -362,15 +362,15 @@ __device__ __forceinline__ void cb_block_pairs(const Dims& d, const void* __rest
       const bool ok = t < d.L;
       const float inv = isB ? ib : ic;
       const uint32_t wv[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-      int q[8];
+      // sat(RHAZ(v inv)) through the clamp-then-round-away form of the main
+      // kernel's quantiser (same codes as clamping after rounding; rows past L: 0)
+      float v[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v0 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu)));
-        const float v1 = Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16)));
-        q[2 * e] = ok ? q_sat(v0 * inv, 127.f) : 0;
-        q[2 * e + 1] = ok ? q_sat(v1 * inv, 127.f) : 0;
+        v[2 * e] = ok ? Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] & 0xffffu))) * inv : 0.f;
+        v[2 * e + 1] = ok ? Store<DT>::to_f(__builtin_bit_cast(T, (u16)(wv[e] >> 16))) * inv : 0.f;
       }
-      const uint2 pq = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      const uint2 pq = make_uint2(q8x4(v[0], v[1], v[2], v[3]), q8x4(v[4], v[5], v[6], v[7]));
       if (isB) {
         *(uint2*)&sm.qB[bsw<NS>(s, n0)] = pq;
       } else {
