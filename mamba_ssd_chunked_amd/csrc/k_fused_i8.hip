@@ -56,13 +56,13 @@ constexpr int kCompT = kCompW * kWave;        // 512
 // Preparation launch (1024 threads per block). Blocks [0, ncs) run
 // ChunkCumsum for (chunk, batch, block of kCsHeads heads). The other blocks
 // write Q(C) rows, the Q(B)^T fragments of ChunkState and the CB' fragments of
-// ChunkScan2, in one of two layouts:
+// ChunkScan2, in one of three layouts:
 //  - per unit (batch, chunk, group), when there are enough units to fill the
 //    GPU: the chunk's Q(B) and Q(C) rows are quantised once into LDS and the
 //    16 waves share the fragments;
-//  - per unit half (two blocks per unit, for fewer units): each half takes the
-//    row tiles of about half the CB' fragments and quantises the Q(B) rows
-//    they reach and its own Q(C) rows;
+//  - per unit half (two blocks per unit, for fewer units; cb_block_slice with
+//    S = 2): each half takes the row tiles of about half the CB' fragments and
+//    quantises the Q(B) rows they reach and its own Q(C) rows;
 //  - per unit and pair j of row tiles {2j, 2j + 1}, for few units (more,
 //    smaller blocks): Q(C) of those 32 rows and Q(B) of rows 0 .. 32 j + 31 go
 //    into LDS; the block writes the Q(C) rows, the CB' fragments of the two row
