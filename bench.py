@@ -361,13 +361,17 @@ def schedule_of(w, cus: int) -> str:
     return "chunk" if w.batch * w.nheads < 2 * cus else "head"
 
 
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+
+
 def time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, steps, warmup, copy_gbs,
-                 traffic=None, spread=True) -> dict:
+                 traffic=None, spread=True, cold=False) -> dict:
     """Tokens/s and HBM roofline fraction of ssd_forward on resident inputs:
     `warmup` untimed calls, then `steps` back-to-back calls bracketed by one
     pair of events on the stream the kernels run on (events between the calls
     would add their own packets); optionally the spread of single calls from a
-    second, untimed pass."""
+    second, untimed pass, and (cold) single calls each after a 512 MB write
+    that evicts the inputs from the last-level cache."""
     ws = torch.empty(max(1, L.ssd_workspace_bytes(sh, path)), dtype=torch.uint8, device="cuda")
     sc = scales if path == L.SSD_PATH_INT8 else None
 
@@ -401,6 +405,20 @@ def time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, steps, warmup,
         call_ms.update({"mean": float(per_call_ms.mean()), "median": float(np.median(per_call_ms)),
                         "p10": float(np.percentile(per_call_ms, 10)),
                         "p90": float(np.percentile(per_call_ms, 90))})
+    if cold:
+        scratch = torch.empty(2 * LLC_BYTES // 4, dtype=torch.float32, device="cuda")
+        reps = min(steps, 20)
+        cs = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            scratch.fill_(float(i))
+            cs[i].record()
+            step()
+            ce[i].record()
+        torch.cuda.synchronize()
+        cold_ms = np.array([a.elapsed_time(b) for a, b in zip(cs, ce)])
+        call_ms["cold_median"] = float(np.median(cold_ms))
+        del scratch
     del ws
     bpt = algorithmic_bytes_per_token(w, path == L.SSD_PATH_INT8)
     bytes_per_call = bpt * tokens
@@ -449,8 +467,10 @@ def bench_configs(torch, np, L, synth, steps, warmup, copy_gbs, head=None) -> di
             y = torch.empty_like(dev["x"])
             res = {}
             for name, path in (("int8", L.SSD_PATH_INT8), ("float", L.SSD_PATH_FLOAT)):
+                small = algorithmic_bytes_per_token(w, path == L.SSD_PATH_INT8) * w.batch * w.seqlen < LLC_BYTES
                 res[name] = time_forward(torch, np, L, w, sh, path, dev, A, D, scales, y, steps, warmup,
-                                         copy_gbs, traffic=measured_traffic(w.name, name), spread=False)
+                                         copy_gbs, traffic=measured_traffic(w.name, name), spread=False,
+                                         cold=small)
             del dev, y
             torch.cuda.empty_cache()
         for name, r in res.items():
@@ -458,10 +478,19 @@ def bench_configs(torch, np, L, synth, steps, warmup, copy_gbs, head=None) -> di
                          "roofline_frac": r["roofline"]["frac"],
                          "achieved_gbs": r["roofline"]["achieved"],
                          "traffic": r["roofline"]["traffic"]}
+            if "cold_median" in r["call_ms"]:
+                # back-to-back calls keep this working set in the last-level
+                # cache: the figures above are warm; the cold ones follow a
+                # 512 MB write before each call
+                cm = r["call_ms"]["cold_median"]
+                rec[name]["cache"] = "warm (working set under the 256 MB last-level cache)"
+                rec[name]["cold_call_ms"] = cm
+                rec[name]["cold_roofline_frac"] = r["roofline"]["frac"] * r["call_ms"]["timed_mean"] / cm
         if "int8" in rec and "float" in rec:
             rec["int8_speedup"] = rec["float"]["call_ms"] / rec["int8"]["call_ms"]
         out[w.name] = rec
         print(f"# config {wid}: " + ", ".join(f"{k} {rec[k]['call_ms']:.4f} ms ({rec[k]['roofline_frac']:.3f})"
+                                              + (f" cold {rec[k]['cold_call_ms']:.4f} ms" if "cold_call_ms" in rec[k] else "")
                                               for k in ("int8", "float") if k in rec),
               file=sys.stderr, flush=True)
     return out
@@ -515,9 +544,12 @@ def bench_trend(torch, np, L, synth, steps, warmup, copy_gbs) -> dict:
                               copy_gbs, spread=False)
             del dev, y
             t8, tf = r8["call_ms"]["timed_mean"], rf["call_ms"]["timed_mean"]
+            warm = algorithmic_bytes_per_token(w, False) * b * seqlen < LLC_BYTES
             points.append({"batch": b, "seqlen": seqlen, "int8_schedule": schedule_of(w, cus),
                            "int8_ms": t8, "float_ms": tf, "int8_speedup": tf / t8,
-                           "int8_frac": r8["roofline"]["frac"], "float_frac": rf["roofline"]["frac"]})
+                           "int8_frac": r8["roofline"]["frac"], "float_frac": rf["roofline"]["frac"],
+                           "cache": "warm (back-to-back calls; working set under the 256 MB last-level cache)"
+                           if warm else "working set over the last-level cache"})
             print(f"# trend B={b} L={seqlen}: int8 {t8:.4f} ms, float {tf:.4f} ms, x{tf / t8:.2f}",
                   file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
