@@ -862,24 +862,44 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
       }
       // diagonal pair mi: exp(a_s - a_s') dt_s' 2^-E directly (zero above the
       // diagonal), with D on the diagonal so the skip term D x rides the MFMA
+      // An even tile (i = 2 mi) has its diagonal block in the pair's first
+      // column tile and only zero weights in the second (above the
+      // diagonal), so that half takes no exps and no x reads: its weights
+      // and x slots are written as zeros, which leaves every product, and
+      // so Y, bit for bit as with the full pair.
       {
-        F xd[PW];
-        xfrags(mi, xd);
+        const bool even = (i & 1) == 0;
         const float4 ba = *(const float4*)&vB[32 * mi + 8 * lg];
-        const float4 bb = *(const float4*)&vB[32 * mi + 8 * lg + 4];
-        const float bv[8] = {ba.x, ba.y, ba.z, ba.w, bb.x, bb.y, bb.z, bb.w};
+        const float bva[4] = {ba.x, ba.y, ba.z, ba.w};
         F wf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        const auto diag_w = [&](int e, float bvv) {
           const int sp = 32 * mi + 16 * (e >> 2) + 4 * lg + (e & 3);
-          const float arg = (sp <= s_row) ? a_s - bv[e] : -__builtin_inff();
+          const float arg = (sp <= s_row) ? a_s - bvv : -__builtin_inff();
           const float ev = __builtin_amdgcn_exp2f(arg);
           const uint32_t dw = (uint32_t)t.diag[e >> 1];
           const _Float16 c16 = __builtin_bit_cast(_Float16, (u16)((e & 1) ? (dw >> 16) : (dw & 0xffffu)));
           wf.set(e, __builtin_fmaf((float)c16, ev, (sp == s_row) ? Dh : 0.0f));
+        };
+#pragma unroll
+        for (int e = 0; e < 4; ++e) diag_w(e, bva[e]);
+        if (even) {
+#pragma unroll
+          for (int e = 4; e < 8; ++e) wf.set(e, 0.0f);
+        } else {
+          const float4 bb = *(const float4*)&vB[32 * mi + 8 * lg + 4];
+          const float bvb[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int e = 4; e < 8; ++e) diag_w(e, bvb[e - 4]);
         }
 #pragma unroll
-        for (int jp = 0; jp < PW; ++jp) acc[jp] = F::mma(xd[jp], wf, acc[jp]);
+        for (int jp = 0; jp < PW; ++jp) {
+          const v4s_t lo = ldtr16(xb + xoff[jp] + (32 * mi) * kHP);
+          v4s_t hi = v4s_t{0, 0, 0, 0};
+          if (!even) hi = ldtr16(xb + xoff[jp] + (32 * mi + 16) * kHP);
+          F xd;
+          xd.v = __builtin_bit_cast(decltype(xd.v), v8s_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          acc[jp] = F::mma(xd, wf, acc[jp]);
+        }
       }
       // epilogue: lane holds s = s_row and p = 16 pt + 4 lg + r
       {
