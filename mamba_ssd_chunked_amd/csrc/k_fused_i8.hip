@@ -492,12 +492,13 @@ struct I8Args {
 };
 
 // Staging registers of one wave for one chunk: its share of the chunk is rows
-// s = (l / 8) w + (lane >> 3) + 8 u (u = 0 .. NU - 1), columns 8 (lane & 7) ..
-// + 7, with LUT_state of those rows, and for lanes below l / 8 the dAcs and dt
-// of position (l / 8) w + lane.
-template <int LC>
+// s = (l / 8) w + lane / R + (64 / R) u (u = 0 .. NU - 1) of the block's p
+// range, each lane 8 columns of a row (R = 8 lanes per row for a whole head,
+// 4 for a p half), with LUT_state of those rows, and for lanes below l / 8
+// the dAcs and dt of position (l / 8) w + lane.
+template <int NU_>
 struct SRegs {
-  static constexpr int NU = LC / 64;
+  static constexpr int NU = NU_;
   v4i x[NU];
   float lut[NU];
   float va;
@@ -532,7 +533,10 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   constexpr int XN = LC * kHP, QN = LC * kHP, HN = kHP * NS;
   constexpr int NRR = (LC == 256) ? 2 : 1;  // row tiles per wave
   constexpr int SR = LC / 8;                // staged rows per wave
-  constexpr int NU = SRegs<LC>::NU;
+  constexpr int LPR = 2 * PW;               // staging lanes per row (the block's p range, 16 bytes each)
+  constexpr int RPP = kWave / LPR;          // rows per staging pass
+  constexpr int NU = SR / RPP;              // staging passes per chunk
+  static_assert(NU * RPP == SR, "whole staging passes");
   const Dims& d = a.d;
   const BlockHead bh = block_head<PW>(d, bx, a.nfull, a.unit_map, a.half_il);
   const int pt_base = (PW == 4) ? 0 : 2 * bh.ph;
@@ -562,7 +566,8 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   }
 
   // ---- staging of a chunk (each wave its share) ----
-  const int c8 = lane & 7, sr0 = SR * w + (lane >> 3);
+  // a p half stages only its own columns: its ChunkState and ChunkScan read no others
+  const int c8 = 2 * pt_base + (lane & (LPR - 1)), sr0 = SR * w + lane / LPR;
   const int sv = SR * w + (lane & (SR - 1));  // this lane's position for the per-position values
   const int64_t rowB = (int64_t)H * kHP * sizeof(T);
   const char* xh = (const char*)a.X + (b * d.L * H + h) * (int64_t)kHP * sizeof(T);
@@ -570,14 +575,14 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   // (real == false: the same loads from the chunk's first row, L2-resident
   // and never used, so that every chunk issues the same vector-memory
   // operations and the compiler's in-order wait counts stay exact)
-  const auto stage_load = [&](int kc, SRegs<LC>& r, bool real) {
+  const auto stage_load = [&](int kc, SRegs<NU>& r, bool real) {
     const int64_t t0 = (int64_t)kc * LC;
     const int64_t cs0 = (bh_ * d.c + kc) * (int64_t)LC;
     const int64_t lim = real ? d.L - 1 - t0 : 0;  // last valid row of the chunk
     const int srow = real ? sr0 : 0, svr = real ? sv : 0;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int64_t s = min((int64_t)(srow + (real ? 8 * u : 0)), lim);
+      const int64_t s = min((int64_t)(srow + (real ? RPP * u : 0)), lim);
       r.x[u] = __builtin_nontemporal_load((const v4i*)(xh + (t0 + s) * rowB + x_lane));
       r.lut[u] = a.lut[cs0 + s];
     }
@@ -592,14 +597,14 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
   const float4 ix0 = ld_scale4(&a.sc.inv_X[h * kHP + 8 * c8]);
   const float4 ix1 = ld_scale4(&a.sc.inv_X[h * kHP + 8 * c8 + 4]);
   const float ix[8] = {ix0.x, ix0.y, ix0.z, ix0.w, ix1.x, ix1.y, ix1.z, ix1.w};
-  const auto stage_store = [&](int kc, const SRegs<LC>& r) {
+  const auto stage_store = [&](int kc, const SRegs<NU>& r) {
     const int o = kc & 1;
     u16* xw = s_x + o * XN;
     int8_t* qw = s_qx + o * QN;
     const int64_t t0 = (int64_t)kc * LC;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int s = sr0 + 8 * u;
+      const int s = sr0 + RPP * u;
       *(v4i*)&xw[xsw_off(s, 8 * c8)] = r.x[u];
       // Q(X_scaled) = sat(RHAZ(fl32(fl32(lut * x) * inv_X))) ("Key design 1");
       // rows past L have LUT_state 0, so their codes are 0
@@ -710,7 +715,7 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
 
   // prologue: stage chunk 0 (every wave its share)
   {
-    SRegs<LC> r;
+    SRegs<NU> r;
     stage_load(0, r, true);
     stage_store(0, r);
   }
@@ -749,7 +754,7 @@ __device__ __forceinline__ void fused_i8_v2(const I8Args& a, const int64_t bx, u
     // the barrier stays short
     v4i Fo[NOFF], diag1, diag2, qc1[KN], qc2[KN];
     load_first(k, wk, Fo, diag1, qc1);
-    SRegs<LC> sreg;
+    SRegs<NU> sreg;
     stage_load(kn1, sreg, k + 1 < d.c);
 
     v2s S8a[PTW], S8b[PTW];
