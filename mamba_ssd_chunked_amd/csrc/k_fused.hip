@@ -90,6 +90,20 @@ __device__ __forceinline__ int h_off(int r, int c) {
   return r * W + 8 * ((c >> 3) ^ (r & msk)) + (c & 7);
 }
 
+// The 16-bit (LUT x)^T tile [p][s] (element offsets): h_off's row XOR, and row
+// bit 4 also XORed into bit 2 of the chunk index. The staging writes one column
+// chunk of rows 8 c8 + e (c8 = 0..7) per instruction; with the low row bits
+// alone, rows 16 apart shared a chunk (four-way bank conflicts, the kernel's
+// largest source of them); now they spread over all 16 positions. The
+// ChunkState reads (16 consecutive rows, bit 4 fixed) stay on 16 distinct
+// chunks.
+template <int W>
+__device__ __forceinline__ int xs_off(int r, int c) {
+  constexpr int nch = W / 8;
+  constexpr int msk = (nch < 16 ? nch : 16) - 1;
+  static_assert(nch >= 8, "room for chunk bit 2");
+  return r * W + 8 * ((c >> 3) ^ (r & msk) ^ (((r >> 4) & 1) << 2)) + (c & 7);
+}
 typedef short v4s __attribute__((ext_vector_type(4)));
 // Transposing LDS read (16-bit elements): the 16 lanes of a group each point at
 // 8 bytes; lanes 4r .. 4r + 3 form row r (16 elements) of a 4 x 16 matrix, and
@@ -142,7 +156,7 @@ template <int DT, int LC, int NS>
 struct FLds {
   static constexpr bool SPLIT = DT == DT_BF16;
   u16* xT;    // x^T (xT_pair layout)
-  u16* xs;    // 16-bit (LUT x)^T [p][s] (h_off<LC>); with bf16 the LUT goes on the B side
+  u16* xs;    // 16-bit (LUT x)^T [p][s] (xs_off<LC>); with bf16 the LUT goes on the B side
   u16* B;     // B rows [s][n] (h_off<NS>)
   u16* H;     // 16-bit passed state [p][n] (h_off<NS>)
   u16* H_lo;  // its residual (bf16)
@@ -262,7 +276,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
             const uint32_t hv = (e & 1) ? (dw >> 16) : (dw & 0xffffu);
             v[r] = __builtin_fmaf(lutv[r], Store<DT>::to_f(__builtin_bit_cast(T, (u16)hv)), 0.0f);
           }
-          *(uint2*)&s_xs[h_off<LC>(8 * c8 + e, 4 * q)] = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
+          *(uint2*)&s_xs[xs_off<LC>(8 * c8 + e, 4 * q)] = make_uint2(pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]));
         }
       }
     }
@@ -383,7 +397,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
         const v4s hi = lds_tr16(s_B + h_off<NS>(s0 + 4 + (l16 >> 2), cn));
         a_.v = __builtin_bit_cast(decltype(a_.v), v8s_join(lo, hi));
 #pragma unroll
-        for (int j = 0; j < PTW; ++j) b_[j] = frag16<DT>(&s_xs[h_off<LC>(16 * (pt0 + j) + l16, s0)]);
+        for (int j = 0; j < PTW; ++j) b_[j] = frag16<DT>(&s_xs[xs_off<LC>(16 * (pt0 + j) + l16, s0)]);
       };
       load_ks(0, fa[0], fb[0]);
 #pragma unroll
