@@ -35,14 +35,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // runs s = 32m + 16h + 4g + (0..3) sit at 32m + 8g + 4h + (0..3). A lane's
 // ChunkScan2 operand (group g of tiles 2m and 2m + 1) is then one 16-byte
 // chunk, index 4m + g. Rows are padded by 16 bytes (kXTPad elements), so 16
-// consecutive rows start in 16 different bank groups, and the two low bits of
-// the chunk index are XORed with bits 4-5 of the row, which spreads the
-// staging's writes to rows 8 apart. For the operand reads, whose 16 rows
-// share bits 4-5, the offset is then linear in m (no per-step swizzle).
+// consecutive rows start in 16 different bank groups, and bits 2-3 of the
+// chunk index (the low bits of m) are XORed with bits 4-5 of the row. A
+// staging write covers rows 8 c8 + r of every c8 and every g: with the XOR on
+// g (the low chunk bits) the rows 16 apart met g's own values and the write
+// was four-way bank conflicted; on m they land on distinct chunks (two-way,
+// the least for 512 bytes). The operand reads, whose 16 rows share bits 4-5,
+// stay on 16 distinct bank groups.
 constexpr int kXTPad = 8;
 template <int LC>
 __device__ __forceinline__ int xT_pair(int p, int m, int g) {  // 16-byte chunk start
-  return p * (LC + kXTPad) + 32 * m + 8 * (g ^ ((p >> 4) & 3));  // = chunk (4m + g) ^ ((p >> 4) & 3)
+  return p * (LC + kXTPad) + 32 * (m ^ ((p >> 4) & 3)) + 8 * g;  // = chunk (4m + g) ^ (4 ((p >> 4) & 3))
 }
 template <int LC>
 __device__ __forceinline__ int xT_off(int p, int s) {  // s aligned to 4
