@@ -226,11 +226,29 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     float vl;  // LUT of position tid % LC (bf16 only)
     uint32_t vd;
   };
+  // staging item it -> rows 4q .. 4q + 3, columns 8 c8 .. 8 c8 + 7 of the chunk.
+  // For whole heads the lane bits are dealt out so that every half wave's LDS
+  // writes (x^T and (LUT x)^T) land on 32 distinct 8-byte bank positions: lane
+  // bits 0-1 and 5 are c8's bits 0-1 and 2, bit 2 is q's bit 2 (the 8-byte
+  // half of an x^T chunk), bits 3-4 are q's bits 0-1; before, the half was
+  // lane bit 5 and each half wave wrote one half of 16 chunks (two-way bank
+  // conflicts). The wave index gives q's higher bits.
+  const auto stage_item = [&](int it, int& q, int& c8) {
+    if constexpr (C8N == 8) {
+      const int ln = it & (kWave - 1);
+      c8 = (ln & 3) | (((ln >> 5) & 1) << 2);
+      q = 8 * (it >> 6) + (((ln >> 2) & 1) << 2) + ((ln >> 3) & 3);
+    } else {
+      q = it / C8N;
+      c8 = c8b + it % C8N;
+    }
+  };
   const auto stage_load = [&](int kc, int tid, Pf& pf) {
     const int t0 = kc * LC;
     const int lim = min(LC - 1, (int)d.L - 1 - t0);
     const int it = tid % XI;
-    const int q = it / C8N, c8 = c8b + it % C8N;
+    int q, c8;
+    stage_item(it, q, c8);
     const T* xk = Xb + (int64_t)t0 * rowX + 8 * c8;
 #pragma unroll
     for (int r = 0; r < 4; ++r) pf.x[r] = *(const uint4*)(xk + __umul24(min(4 * q + r, lim), rowX));
@@ -254,7 +272,8 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
     asm volatile("" : "+v"(lutp.x), "+v"(lutp.y), "+v"(lutp.z), "+v"(lutp.w), "+v"(vap), "+v"(vdp));
     if constexpr (SPLIT) asm volatile("" : "+v"(vlp));
     if (tid < XI) {
-      const int q = tid / C8N, c8 = c8b + tid % C8N;
+      int q, c8;
+      stage_item(tid, q, c8);
       const uint32_t* w0 = (const uint32_t*)&xr[0];
       const uint32_t* w1 = (const uint32_t*)&xr[1];
       const uint32_t* w2 = (const uint32_t*)&xr[2];
