@@ -34,22 +34,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // of 32 positions (two 16-position column tiles 2m and 2m + 1): the 4-position
 // runs s = 32m + 16h + 4g + (0..3) sit at 32m + 8g + 4h + (0..3). A lane's
 // ChunkScan2 operand (group g of tiles 2m and 2m + 1) is then one 16-byte
-// chunk, index 4m + g. Rows are padded by 16 bytes (kXTPad elements), so 16
-// consecutive rows start in 16 different bank groups, and bits 2-3 of the
-// chunk index (the low bits of m) are XORed with bits 4-5 of the row. A
-// staging write covers rows 8 c8 + r of every c8 and every g: with the XOR on
-// g (the low chunk bits) the rows 16 apart met g's own values and the write
-// was four-way bank conflicted; on m they land on distinct chunks (two-way,
-// the least for 512 bytes). The operand reads, whose 16 rows share bits 4-5,
-// stay on 16 distinct bank groups.
-constexpr int kXTPad = 8;
+// chunk, index 4m + g. Rows of LC elements; the chunk index is XORed with the
+// row's low four bits and, in bit 2, with row bit 4 (as the (LUT x)^T tile), so
+// the operand reads (16 consecutive rows, one chunk) and each half wave of the
+// staging writes land on distinct bank positions. (Rows padded by 16 bytes
+// instead of XORed, an earlier layout, left the operand reads with bank
+// conflicts: about half of the kernel's remaining ones, measured by a probe.)
 template <int LC>
 __device__ __forceinline__ int xT_pair(int p, int m, int g) {  // 16-byte chunk start
-  return p * (LC + kXTPad) + 32 * (m ^ ((p >> 4) & 3)) + 8 * g;  // = chunk (4m + g) ^ (4 ((p >> 4) & 3))
-}
-template <int LC>
-__device__ __forceinline__ int xT_off(int p, int s) {  // s aligned to 4
-  return xT_pair<LC>(p, s >> 5, (s >> 2) & 3) + 4 * ((s >> 4) & 1);
+  return p * LC + 8 * ((4 * m + g) ^ (p & 15) ^ (((p >> 4) & 1) << 2));
 }
 // byte tiles [rows][W]; c a byte column aligned to 4
 template <int W>
@@ -278,12 +271,12 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
       const uint32_t* w1 = (const uint32_t*)&xr[1];
       const uint32_t* w2 = (const uint32_t*)&xr[2];
       const uint32_t* w3 = (const uint32_t*)&xr[3];
-      u16* const xTb = s_xT + xT_pair<LC>(8 * c8, q >> 3, q & 3) + 4 * ((q >> 2) & 1);  // as in the INT8 kernel
+      const int hx = 4 * ((q >> 2) & 1);  // the 8-byte half of the chunk (h)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *(uint2*)(xTb + (2 * e) * (LC + kXTPad)) =
+        *(uint2*)(s_xT + xT_pair<LC>(8 * c8 + 2 * e, q >> 3, q & 3) + hx) =
             make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u), __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u));
-        *(uint2*)(xTb + (2 * e + 1) * (LC + kXTPad)) =
+        *(uint2*)(s_xT + xT_pair<LC>(8 * c8 + 2 * e + 1, q >> 3, q & 3) + hx) =
             make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u), __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
       }
       // fl32(LUT x) in the 16-bit type for 4 rows of each p (fp16 only)
@@ -635,7 +628,7 @@ __device__ __forceinline__ void fused_f16_body(const FusedFArgs& a, const int64_
 template <int DT, int LC, int NS>
 __global__ __launch_bounds__(kThreads, 1) void k_fused_f16(FusedFArgs a) {
   constexpr bool SPLIT = DT == DT_BF16;
-  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * (LC + kXTPad)];
+  __shared__ __attribute__((aligned(16))) u16 s_xT[kP * LC];
   __shared__ __attribute__((aligned(16))) u16 s_xs[SPLIT ? 8 : kP * LC];
   __shared__ __attribute__((aligned(16))) u16 s_B[LC * NS];
   __shared__ __attribute__((aligned(16))) u16 s_H[kP * NS];
